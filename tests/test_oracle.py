@@ -1,0 +1,370 @@
+"""Pins for the CPU oracle (no GPU needed).
+
+Each test ties the oracle to something other than itself: a library routine
+(torch's bf16 rounding, numpy matmul / argmax), hand-derived worked vectors,
+closed forms, exact rational brute force, or an independent formulation
+(Python big-integer bit streams).  Together they are chosen so that a dropped
+term, a wrong sign or index, or a transposed operand in the oracle fails at
+least one of them (see test_oracle_mutants.py, which plants such mistakes).
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pack_worked.txt")
+
+
+# ------------------------------------------------------------------ bf16
+
+def test_bf16_decode_all_patterns_match_torch():
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.bf16_to_f64(h)
+    ref = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.slow
+def test_f32_to_bf16_rne_exhaustive_matches_torch():
+    """All 2^32 float32 bit patterns, against torch's CPU float->bfloat16 (RNE)."""
+    step = 1 << 26
+    base = np.arange(step, dtype=np.uint32)
+    u = np.empty_like(base)
+    for start in range(0, 1 << 32, step):
+        np.add(base, np.uint32(start), out=u)
+        f = u.view(np.float32)
+        mine = oracle.f32_to_bf16(f)
+        ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        fnan = np.isnan(f)
+        # every mismatch must be a NaN input (payloads are not compared) ...
+        assert not np.any((mine != ref) & ~fnan), hex(start)
+        # ... and NaN stays NaN
+        if fnan.any():
+            mn = mine[fnan]
+            assert np.all(((mn & 0x7F80) == 0x7F80) & ((mn & 0x007F) != 0))
+
+
+def test_f32_to_bf16_ties_to_even_by_hand():
+    # 1 + 2^-8 is exactly halfway between bf16 1.0 (0x3F80) and 1+2^-7 (0x3F81): even -> 0x3F80.
+    # 1 + 3*2^-8 is halfway between 0x3F81 and 0x3F82: even -> 0x3F82.
+    vals = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -20], np.float32)
+    assert list(oracle.f32_to_bf16(vals)) == [0x3F80, 0x3F82, 0xBF80, 0x3F81]
+
+
+# ---------------------------------------------------------- pack / unpack
+
+def _golden_rows():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            rows.append((int(parts[0]), parts[1], [int(w, 16) for w in parts[2:]]))
+    return rows
+
+
+def _codes_from_formula(formula: str, bits: int):
+    k = np.arange(64)
+    table = {"k%4": k % 4, "k%8": k % 8, "k%16": k % 16, "k%32": k % 32, "k%64": k % 64,
+             "k%128": k % 128, "k%256": k % 256, "(7k+3)%16": (7 * k + 3) % 16}
+    c = table[formula].astype(np.uint8)
+    assert c.max() < (1 << bits)
+    return c
+
+
+@pytest.mark.parametrize("row", _golden_rows(), ids=lambda r: "b%d_%s" % (r[0], r[1]))
+def test_pack_worked_vectors(row):
+    bits, formula, expect = row
+    codes = _codes_from_formula(formula, bits)[None, :]
+    words = oracle.pack(codes, bits)
+    assert words.shape == (1, 2 * bits)
+    assert [int(w) for w in words[0, :len(expect)]] == expect
+    assert brute.pack_row(codes[0], bits)[:len(expect)] == expect
+    assert np.array_equal(oracle.unpack(words, bits, 64), codes)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_pack_unpack_roundtrip_random_and_patterns(bits):
+    N, K = 7, 320
+    rnd = synth.random_codes((N, K), bits, 99, "roundtrip/%d" % bits)
+    top = (1 << bits) - 1
+    pats = [np.zeros(K, np.uint8), np.full(K, top, np.uint8),
+            (np.arange(K) % 2 * top).astype(np.uint8)]
+    for i in range(bits):  # walking single bit
+        pats.append(np.full(K, 1 << i, np.uint8))
+    codes = np.vstack([rnd] + [p[None, :] for p in pats])
+    words = oracle.pack(codes, bits)
+    assert np.array_equal(oracle.unpack(words, bits, K), codes)
+    # the big-integer formulation reads the same codes out of the same words
+    for n in range(codes.shape[0]):
+        assert brute.row_codes(words[n], bits, K) == [int(c) for c in codes[n]]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_unpack_of_random_words_matches_bigint_stream(bits):
+    N, K = 5, 192
+    words = synth.random_words((N, K * bits // 32), 98, "unpack/%d" % bits)
+    codes = oracle.unpack(words, bits, K)
+    for n in range(N):
+        assert brute.row_codes(words[n], bits, K) == [int(c) for c in codes[n]]
+    # and pack inverts it exactly (every bit of the stream belongs to a code)
+    assert np.array_equal(oracle.pack(codes, bits), words)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_unpack_closed_form_for_word_aligned_widths(bits):
+    """b in {2,4,8}: code k is field (k mod 32/b) of word k // (32/b)."""
+    N, K = 3, 256
+    words = synth.random_words((N, K * bits // 32), 97, "closed/%d" % bits)
+    per = 32 // bits
+    k = np.arange(K)
+    expect = (words[:, k // per] >> (bits * (k % per)).astype(np.uint32)) & ((1 << bits) - 1)
+    assert np.array_equal(oracle.unpack(words, bits, K), expect.astype(np.uint8))
+
+
+@pytest.mark.parametrize("bits,straddlers", [
+    (3, [10, 21, 42, 53]),
+    (5, [6, 12, 19, 25, 38, 44, 51, 57]),
+    (6, [5, 10, 21, 26, 37, 42, 53, 58]),
+    (7, [4, 9, 13, 18, 22, 27, 36, 41, 45, 50, 54, 59]),
+])
+def test_straddling_codes_take_low_bits_from_lower_word(bits, straddlers):
+    """Codes whose bits cross a 32-bit word boundary (listed by hand) read correctly
+    when only that code is nonzero."""
+    K = 64
+    for k in range(K):
+        starts, ends = (bits * k) >> 5, (bits * k + bits - 1) >> 5
+        assert (starts != ends) == (k in straddlers)
+    for k in straddlers:
+        codes = np.zeros((1, K), np.uint8)
+        codes[0, k] = (1 << bits) - 1
+        words = oracle.pack(codes, bits)
+        lo_word = (bits * k) >> 5
+        nlow = 32 - ((bits * k) & 31)
+        assert int(words[0, lo_word]) == ((1 << nlow) - 1) << (32 - nlow)
+        assert int(words[0, lo_word + 1]) == (1 << (bits - nlow)) - 1
+        assert np.array_equal(oracle.unpack(words, bits, K), codes)
+
+
+# ------------------------------------------------------------------ GEMV
+
+def _bf16(vals):
+    return synth.to_bf16_bits(np.asarray(vals, np.float64))
+
+
+def test_affine_closed_form_all_equal_codes_exact():
+    """b=4, K=64, all codes 5, s=2^-7, bias=-2^-5, x=1: w = 5/128 - 4/128 = 2^-7,
+    y = 64 * 2^-7 = 0.5 exactly."""
+    codes = np.full((1, 64), 5, np.uint8)
+    words = oracle.pack(codes, 4)
+    s = np.array([[0x3C00]], np.uint16)   # 2^-7
+    b = np.array([[0xBD00]], np.uint16)   # -2^-5
+    assert oracle.bf16_to_f64(s)[0, 0] == 2 ** -7 and oracle.bf16_to_f64(b)[0, 0] == -2 ** -5
+    x = np.full((1, 64), 0x3F80, np.uint16)
+    y, A = oracle.gemv_affine(x, words, s, b, 4)
+    assert y[0, 0] == 0.5 and A[0, 0] == 0.5
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_affine_zero_codes_give_bias_times_group_sums(bits):
+    M, N, K = 3, 4, 256
+    x = synth.normal_bf16((M, K), 1.0, 96, "zc/x")
+    b = synth.uniform_bf16((N, K // 64), -0.1, 0.1, 96, "zc/b")
+    s = synth.uniform_bf16((N, K // 64), 0.001, 0.02, 96, "zc/s")
+    words = np.zeros((N, K * bits // 32), np.uint32)
+    y, _ = oracle.gemv_affine(x, words, s, b, bits)
+    X = oracle.bf16_to_f64(x).reshape(M, K // 64, 64).sum(axis=2)      # [M, G]
+    expect = X @ oracle.bf16_to_f64(b).T                                # [M, N]
+    assert np.allclose(y, expect, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_affine_unit_scale_zero_bias_is_integer_dot(bits):
+    """s=1, bias=0 and integer x: y is the integer dot product codes . x (numpy int64)."""
+    M, N, K = 4, 9, 384
+    x_int = synth.rng(95, "int/x").integers(-8, 9, size=(M, K))
+    x = _bf16(x_int)
+    words = synth.random_words((N, K * bits // 32), 95, "int/w%d" % bits)
+    codes = oracle.unpack(words, bits, K).astype(np.int64)
+    s = np.full((N, K // 64), 0x3F80, np.uint16)
+    b = np.zeros((N, K // 64), np.uint16)
+    y, _ = oracle.gemv_affine(x, words, s, b, bits)
+    assert np.array_equal(y, (x_int @ codes.T).astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 5, 8])
+def test_affine_one_hot_reads_single_codes(bits):
+    M, N, K = 64, 3, 128
+    words = synth.random_words((N, K * bits // 32), 94, "onehot/%d" % bits)
+    codes = oracle.unpack(words, bits, K)
+    x = np.zeros((M, K), np.uint16)
+    cols = np.arange(M) * 2 + 1
+    x[np.arange(M), cols] = 0x3F80
+    s = np.full((N, K // 64), 0x3F80, np.uint16)
+    b = np.zeros((N, K // 64), np.uint16)
+    y, _ = oracle.gemv_affine(x, words, s, b, bits)
+    assert np.array_equal(y, codes[:, cols].T.astype(np.float64))
+
+
+def test_dense_matches_numpy_matmul_and_abs_sum():
+    M, N, K = 5, 33, 1536
+    x = synth.normal_bf16((M, K), 1.0, 93, "d/x")
+    W = synth.normal_bf16((N, K), 0.02, 93, "d/W")
+    y, A = oracle.gemv_bf16(x, W)
+    xd, Wd = oracle.bf16_to_f64(x), oracle.bf16_to_f64(W)
+    ref = xd @ Wd.T
+    aref = np.abs(xd) @ np.abs(Wd).T
+    # both sum exact products in double; only the summation order differs
+    assert np.all(np.abs(y - ref) <= 4 * K * 2.0 ** -53 * aref)
+    assert np.all(np.abs(A - aref) <= 4 * K * 2.0 ** -53 * aref)
+
+
+def test_dense_one_hot_returns_weight_exactly():
+    N, K = 6, 64
+    W = synth.normal_bf16((N, K), 0.02, 92, "oh/W")
+    x = np.zeros((K, K), np.uint16)
+    x[np.arange(K), np.arange(K)] = 0x3F80
+    y, _ = oracle.gemv_bf16(x, W)
+    assert np.array_equal(y, oracle.bf16_to_f64(W).T)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_affine_matches_exact_brute_force_on_tiny_exact_inputs(bits):
+    """Small-integer x, s in {1, 2^-n}, integer bias: every product and sum is exact,
+    so the double oracle equals the rational brute force bit for bit."""
+    M, N, K = 3, 5, 128
+    g = synth.rng(91, "tiny/%d" % bits)
+    x = _bf16(g.integers(-4, 5, size=(M, K)))
+    words = synth.random_words((N, K * bits // 32), 91, "tiny/w%d" % bits)
+    s = _bf16(2.0 ** -g.integers(0, 4, size=(N, K // 64)))
+    b = _bf16(g.integers(-3, 4, size=(N, K // 64)))
+    y, _ = oracle.gemv_affine(x, words, s, b, bits)
+    ref = brute.gemv_affine_exact(x.tolist(), words.tolist(), s.tolist(), b.tolist(), bits)
+    for m in range(M):
+        for n in range(N):
+            assert Fraction(y[m, n]) == ref[m][n]
+
+
+@pytest.mark.parametrize("bits", [3, 4, 6])
+def test_affine_random_tiny_within_double_rounding_of_exact(bits):
+    M, N, K = 2, 4, 192
+    x = synth.normal_bf16((M, K), 1.0, 90, "rt/x")
+    aw = synth.affine_weight(90, "rt", bits, N, K)
+    y, A = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
+    ref = brute.gemv_affine_exact(x.tolist(), aw.words.tolist(), aw.scales.tolist(),
+                                  aw.biases.tolist(), bits)
+    for m in range(M):
+        for n in range(N):
+            assert abs(Fraction(y[m, n]) - ref[m][n]) <= Fraction(2 * K * 2.0 ** -53) * Fraction(A[m, n])
+
+
+def test_dense_matches_exact_brute_force():
+    M, N, K = 2, 3, 64
+    x = synth.normal_bf16((M, K), 1.0, 89, "bd/x")
+    W = synth.normal_bf16((N, K), 0.02, 89, "bd/W")
+    y, A = oracle.gemv_bf16(x, W)
+    ref = brute.gemv_dense_exact(x.tolist(), W.tolist())
+    for m in range(M):
+        for n in range(N):
+            assert abs(Fraction(y[m, n]) - ref[m][n]) <= Fraction(2 * K * 2.0 ** -53) * Fraction(A[m, n])
+
+
+@pytest.mark.parametrize("bits", [2, 5, 8])
+def test_cross_width_widened_codes_give_same_result(bits):
+    """Codes of width b, stored widened as 8-bit codes, give the same y (exactly)."""
+    M, N, K = 2, 6, 256
+    x = synth.normal_bf16((M, K), 1.0, 88, "cw/x")
+    aw = synth.affine_weight(88, "cw", bits, N, K)
+    y, _ = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
+    codes = oracle.unpack(aw.words, bits, K)
+    y8, _ = oracle.gemv_affine(x, oracle.pack(codes, 8), aw.scales, aw.biases, 8)
+    assert np.array_equal(y, y8)
+
+
+def test_affine_scale_and_bias_are_per_group_and_per_row():
+    """Changing one group's scale changes exactly the terms of that group of that row."""
+    M, N, K, bits = 1, 3, 192, 4
+    x = synth.normal_bf16((M, K), 1.0, 87, "pg/x")
+    aw = synth.affine_weight(87, "pg", bits, N, K)
+    y0, _ = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
+    s2 = aw.scales.copy()
+    s2[1, 2] = 0  # zero the scale of row 1, group 2 (k in [128, 192))
+    y1, _ = oracle.gemv_affine(x, aw.words, s2, aw.biases, bits)
+    codes = oracle.unpack(aw.words, bits, K).astype(np.float64)
+    xd = oracle.bf16_to_f64(x)[0]
+    s = oracle.bf16_to_f64(aw.scales)[1, 2]
+    delta = s * np.dot(codes[1, 128:192], xd[128:192])
+    assert y1[0, 0] == y0[0, 0] and y1[0, 2] == y0[0, 2]
+    assert abs((y0[0, 1] - y1[0, 1]) - delta) <= 1e-12 * (1 + abs(delta))
+
+
+# --------------------------------------------------------------- SwiGLU
+
+def test_swiglu_matches_numpy_chain():
+    M, N, K = 3, 40, 1536
+    x = synth.normal_bf16((M, K), 1.0, 86, "sw/x")
+    Wg = synth.normal_bf16((N, K), 0.02, 86, "sw/g")
+    Wu = synth.normal_bf16((N, K), 0.02, 86, "sw/u")
+    r = oracle.swiglu_bf16(x, Wg, Wu)
+    xd = oracle.bf16_to_f64(x)
+    g = xd @ oracle.bf16_to_f64(Wg).T
+    u = xd @ oracle.bf16_to_f64(Wu).T
+    ref = g * (1.0 / (1.0 + np.exp(-g))) * u
+    assert np.allclose(r["g"], g, rtol=1e-12, atol=1e-12)
+    assert np.allclose(r["u"], u, rtol=1e-12, atol=1e-12)
+    assert np.allclose(r["out"], ref, rtol=1e-11, atol=1e-13)
+    # swapping the roles of gate and up changes the result (silu is not symmetric)
+    r2 = oracle.swiglu_bf16(x, Wu, Wg)
+    assert not np.allclose(r2["out"], r["out"])
+
+
+def test_swiglu_special_cases():
+    M, N, K = 2, 8, 128
+    x = synth.normal_bf16((M, K), 1.0, 85, "ss/x")
+    W = synth.normal_bf16((N, K), 0.02, 85, "ss/W")
+    Z = np.zeros((N, K), np.uint16)
+    assert np.all(oracle.swiglu_bf16(x, Z, W)["out"] == 0)   # silu(0) = 0
+    assert np.all(oracle.swiglu_bf16(x, W, Z)["out"] == 0)
+    # large negative gate: silu(g) -> 0; large positive: silu(g) -> g
+    ones = np.full((1, K), 0x3F80, np.uint16)
+    big = np.full((1, K), synth.to_bf16_bits(np.array([1.0]))[0], np.uint16)
+    r = oracle.swiglu_bf16(ones, (big ^ 0x8000)[None, :].reshape(1, K), big.reshape(1, K))
+    assert r["g"][0, 0] == -K and abs(r["out"][0, 0]) < 1e-50
+    r = oracle.swiglu_bf16(ones, big.reshape(1, K), big.reshape(1, K))
+    assert abs(r["out"][0, 0] - K * K) <= 1e-9 * K * K
+
+
+# ---------------------------------------------------------------- argmax
+
+def test_argmax_lowest_index_wins_ties_and_matches_numpy():
+    y = np.array([[1.0, 3.0, 3.0, 2.0], [5.0, 5.0, 5.0, 5.0], [-1.0, -2.0, -0.5, -0.5]])
+    assert list(oracle.argmax(y)) == [1, 0, 2]
+    g = synth.rng(84, "am")
+    z = np.round(g.standard_normal((50, 1000)) * 4) / 4  # many ties
+    assert np.array_equal(oracle.argmax(z), np.argmax(z, axis=1))
+
+
+def test_oracle_is_thread_count_independent():
+    M, N, K = 2, 257, 1024
+    x = synth.normal_bf16((M, K), 1.0, 83, "th/x")
+    aw = synth.affine_weight(83, "th", 3, N, K)
+    n0 = oracle.max_threads()
+    try:
+        oracle.set_threads(1)
+        y1, _ = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, 3)
+        oracle.set_threads(max(2, n0))
+        y2, _ = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, 3)
+    finally:
+        oracle.set_threads(n0)
+    assert np.array_equal(y1, y2)
