@@ -1,0 +1,382 @@
+// Small-M projection kernels for gfx950 (CDNA4, wave64).
+//
+// One template covers the dense bf16 GEMV, the affine b-bit GEMVs and the
+// fused up/gate SwiGLU.  Data flow per workgroup:
+//
+//   1. Stage x (all M rows, one K-tile) into LDS.  Dense: as is.  Affine: in
+//      the order and pre-scaling the width's pair plan needs (pair_plans.h),
+//      plus two fp32 constants per (row m, group): X = sum of the group's x
+//      and T = 128 * sum of its pre-scaled x.
+//   2. Each wavefront owns G*R weight rows.  Its 64 lanes form G segments of
+//      2^L lanes; a segment streams one row, each lane taking every 2^L-th
+//      "unit" of it (8 k = 16 bytes dense; one 64-code group = 8b bytes
+//      affine), so every weight byte is read from HBM exactly once.  The next
+//      unit's loads are in flight while the current one is computed.
+//   3. Dense: acc += dot2(W pair, x pair).  Affine: 32 (64 for b = 8) bf16x2
+//      operands 0x43004300 | code fields are built from the packed words with
+//      masks (no lookup tables), d = sum dot2(operand, pre-scaled x pair), then
+//      acc += scale*(d - T) + bias*X, all in fp32 -- the group's algebraically
+//      exact factored form of sum_k x*(scale*q + bias).
+//   4. Segment sums with DPP (fixed tree), then a fused epilogue: fp32 or RNE
+//      bf16 store; SwiGLU applies silu(g)*u in fp32 first.
+//
+// Formats: AstrAI decode_linear_benchmark.md (commit message: BF16 decode
+// GEMV, fused BF16 up/gate SwiGLU); TensorFold PR #849 "qwen3_5 cuda:
+// mixed-width MLX checkpoints, 2 to 8 bits in groups of 64" (affine widths,
+// groups of 64).  Mask-based code placement instead of lookups: FreeToken-Kai
+// docs/turing.md, section 5.
+#pragma once
+#include "aqg_device.h"
+#include "kernels.h"
+#include "pair_plans.h"
+
+namespace aqg {
+namespace detail {
+
+constexpr int kMaxThreads = 512;
+constexpr size_t kLdsBudget = 64 * 1024;
+
+template <int BITS> struct Geo {
+    static constexpr int UK = 64;             // k per unit (one group)
+    static constexpr int NW = 2 * BITS;       // uint32 words per unit
+    static constexpr int NP = PairPlan<BITS>::NP;
+    static constexpr int NCH = NP / 4;        // uint4 x-chunks per (m, unit)
+    static constexpr int LDS_PER_UNIT = 16 * NCH + 8;  // bytes per (m, unit)
+};
+template <> struct Geo<0> {
+    static constexpr int UK = 8;
+    static constexpr int NW = 4;
+    static constexpr int NP = 4;
+    static constexpr int NCH = 1;
+    static constexpr int LDS_PER_UNIT = 16;
+};
+
+__device__ __forceinline__ uint32_t half_of(const uint32_t* xw, int k)
+{
+    return (xw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+}
+
+// Load one unit (NW words) of a row.  Even widths and dense: 16-byte loads;
+// odd widths: 8-byte loads (a group of an odd width is 8b bytes).
+template <int BITS>
+__device__ __forceinline__ void load_unit(const uint32_t* __restrict__ p, uint32_t* w)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int NW = Geo<BITS>::NW;
+    if constexpr (NW % 4 == 0) {
+        const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            u32x4 v = __builtin_nontemporal_load(q + i);
+            w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    } else {
+        const u32x2* q = reinterpret_cast<const u32x2*>(p);
+#pragma unroll
+        for (int i = 0; i < NW / 2; ++i) {
+            u32x2 v = __builtin_nontemporal_load(q + i);
+            w[2 * i + 0] = v.x; w[2 * i + 1] = v.y;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- staging
+
+// Dense: x[m][kt .. kt+kw) -> lds uint4 [MT][kw/8]; rows m >= M are zero.
+template <int MT>
+__device__ void stage_dense(const ProjArgs& a, int kt, int kw, uint4* xs)
+{
+    const int upm = kw / 8;
+    for (int t = threadIdx.x; t < MT * upm; t += blockDim.x) {
+        const int m = t / upm, u = t - m * upm;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (m < a.M)
+            v = *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt + 8 * u);
+        xs[t] = v;
+    }
+}
+
+// Affine: per (m, group g of the tile) write NCH uint4 of pre-scaled bf16
+// pairs in plan order to xp[(m*NCH + c)*ngt + g] and (X, T) to xc[m*ngt + g].
+template <int BITS, int MT>
+__device__ void stage_affine(const ProjArgs& a, int kt, int kw, uint4* xp, float2* xc)
+{
+    using P = PairPlan<BITS>;
+    constexpr int NCH = Geo<BITS>::NCH;
+    const int ngt = kw / 64;
+    for (int t = threadIdx.x; t < MT * ngt; t += blockDim.x) {
+        const int m = t / ngt, g = t - m * ngt;
+        uint32_t xw[32];
+        if (m < a.M) {
+            const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt + 64 * g);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint4 v = src[i];
+                xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) xw[i] = 0;
+        }
+        float X = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 64; ++k) X += bf16_to_f32(half_of(xw, k));
+        float Ts = 0.0f;
+        static_for<0, NCH>([&](auto C) {
+            uint32_t o[4];
+            static_for<0, 4>([&](auto J) {
+                constexpr int I = 4 * decltype(C)::value + decltype(J)::value;
+                const uint32_t lo = bf16_scale_pow2<P::LO_E[I]>(half_of(xw, P::LO_K[I]));
+                const uint32_t hi = bf16_scale_pow2<P::HI_E[I]>(half_of(xw, P::HI_K[I]));
+                o[decltype(J)::value] = lo | (hi << 16);
+                Ts += bf16_to_f32(lo);
+                Ts += bf16_to_f32(hi);
+            });
+            xp[(m * NCH + decltype(C)::value) * ngt + g] = make_uint4(o[0], o[1], o[2], o[3]);
+        });
+        xc[m * ngt + g] = make_float2(X, 128.0f * Ts);
+    }
+}
+
+// ----------------------------------------------------------------- kernel
+
+template <int BITS, int MT, int R, bool SWIGLU>
+__global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
+{
+    extern __shared__ uint4 lds_u4[];
+    constexpr int S = SWIGLU ? 2 : 1;
+    constexpr int UK = Geo<BITS>::UK;
+    constexpr int NW = Geo<BITS>::NW;
+    constexpr int NCH = Geo<BITS>::NCH;
+
+    const int L = a.lpr_log2;
+    const int LPR = 1 << L;
+    const int G = 64 >> L;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int slot = lane >> L;
+    const int li = lane & (LPR - 1);
+    const int nwaves = blockDim.x >> 6;
+
+    const int64_t row0 = ((int64_t)blockIdx.x * nwaves + wave) * (int64_t)(G * R) + slot;
+    int64_t nrow[R];
+    const uint32_t* wrow[S][R];
+    const uint16_t* srow[R];
+    const uint16_t* brow[R];
+    const int64_t row_words = (BITS == 0) ? (int64_t)a.K / 2 : (int64_t)a.K * BITS / 32;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        nrow[r] = row0 + (int64_t)r * G;
+        const int64_t n = nrow[r] < a.N ? nrow[r] : (int64_t)a.N - 1;  // clamp: load, never store
+        wrow[0][r] = reinterpret_cast<const uint32_t*>(a.w0) + n * row_words;
+        if constexpr (SWIGLU) wrow[1][r] = reinterpret_cast<const uint32_t*>(a.w1) + n * row_words;
+        if constexpr (BITS != 0) {
+            srow[r] = a.scales + n * (a.K / 64);
+            brow[r] = a.biases + n * (a.K / 64);
+        }
+    }
+
+    float acc[S][R][MT];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[s][r][m] = 0.0f;
+
+    for (int kt = 0; kt < a.K; kt += a.KT) {
+        const int kw = min(a.KT, a.K - kt);
+        const int ut = kw / UK;            // units in this tile (a multiple of LPR)
+        __syncthreads();                   // previous tile fully consumed
+        uint4* xp = lds_u4;
+        float2* xc = reinterpret_cast<float2*>(lds_u4 + MT * NCH * ut);
+        if constexpr (BITS == 0) stage_dense<MT>(a, kt, kw, xp);
+        else stage_affine<BITS, MT>(a, kt, kw, xp, xc);
+        __syncthreads();
+
+        const int ubase = kt / UK;         // unit index of the tile start within a row
+        uint32_t wc[S][R][NW], wn[S][R][NW];
+        float sc[R], bi[R], scn[R], bin[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) { sc[r] = bi[r] = scn[r] = bin[r] = 0.0f; }
+        auto fetch = [&](int u, uint32_t (&w)[S][R][NW], float (&s_)[R], float (&b_)[R]) {
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    load_unit<BITS>(wrow[s][r] + (int64_t)(ubase + u) * NW, w[s][r]);
+            if constexpr (BITS != 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    s_[r] = bf16_to_f32(srow[r][ubase + u]);
+                    b_[r] = bf16_to_f32(brow[r][ubase + u]);
+                }
+            }
+        };
+
+        int u = li;
+        if (u < ut) fetch(u, wc, sc, bi);
+        for (; u < ut; u += LPR) {
+            if (u + LPR < ut) fetch(u + LPR, wn, scn, bin);
+            if constexpr (BITS == 0) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const uint4 xv = xp[m * ut + u];
+#pragma unroll
+                    for (int s = 0; s < S; ++s)
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float t = acc[s][r][m];
+                            t = dot2(wc[s][r][0], xv.x, t);
+                            t = dot2(wc[s][r][1], xv.y, t);
+                            t = dot2(wc[s][r][2], xv.z, t);
+                            t = dot2(wc[s][r][3], xv.w, t);
+                            acc[s][r][m] = t;
+                        }
+                }
+            } else {
+                using P = PairPlan<BITS>;
+                float d[S][R][MT];
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) d[s][r][m] = 0.0f;
+                static_for<0, NCH>([&](auto C) {
+                    constexpr int c = decltype(C)::value;
+                    uint32_t p[S][R][4];
+#pragma unroll
+                    for (int s = 0; s < S; ++s)
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            p[s][r][0] = P::template pair<4 * c + 0>(wc[s][r]);
+                            p[s][r][1] = P::template pair<4 * c + 1>(wc[s][r]);
+                            p[s][r][2] = P::template pair<4 * c + 2>(wc[s][r]);
+                            p[s][r][3] = P::template pair<4 * c + 3>(wc[s][r]);
+                        }
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        const uint4 xv = xp[(m * NCH + c) * ut + u];
+#pragma unroll
+                        for (int s = 0; s < S; ++s)
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                float t = d[s][r][m];
+                                t = dot2(p[s][r][0], xv.x, t);
+                                t = dot2(p[s][r][1], xv.y, t);
+                                t = dot2(p[s][r][2], xv.z, t);
+                                t = dot2(p[s][r][3], xv.w, t);
+                                d[s][r][m] = t;
+                            }
+                    }
+                });
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const float2 xcv = xc[m * ut + u];
+#pragma unroll
+                    for (int s = 0; s < S; ++s)
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            acc[s][r][m] = fmaf(sc[r], d[s][r][m] - xcv.y, fmaf(bi[r], xcv.x, acc[s][r][m]));
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int i = 0; i < NW; ++i) wc[s][r][i] = wn[s][r][i];
+#pragma unroll
+            for (int r = 0; r < R; ++r) { sc[r] = scn[r]; bi[r] = bin[r]; }
+        }
+    }
+
+    // Segment reduction and epilogue.
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[s][r][m] = segment_sum(acc[s][r][m], L);
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const bool row_ok = nrow[r] < a.N;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float v = acc[0][r][m];
+            if constexpr (SWIGLU) {
+                const float g = v;
+                v = (g / (1.0f + __expf(-g))) * acc[1][r][m];
+            }
+            const int idx = r * MT + m;
+            if (row_ok && m < a.M && (idx & (LPR - 1)) == li) {
+                const size_t o = (size_t)m * a.N + nrow[r];
+                if (a.out_f32) reinterpret_cast<float*>(a.y)[o] = v;
+                else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16_rne(v);
+            }
+        }
+    }
+}
+
+// One thread per 64-code group: unpack through the same pair plan the GEMV
+// uses, and write the codes as bytes.
+template <int BITS>
+__global__ void __launch_bounds__(256) unpack_kernel(const uint32_t* __restrict__ Wq,
+                                                     uint8_t* __restrict__ codes, int64_t ngroups)
+{
+    using P = PairPlan<BITS>;
+    constexpr int NW = 2 * BITS;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= ngroups) return;
+    uint32_t w[NW];
+    load_unit<BITS>(Wq + t * NW, w);
+    uint32_t c[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = 0;
+    constexpr uint32_t FM = (1u << P::SW) - 1u;
+    static_for<0, P::NP>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const uint32_t p = P::template pair<i>(w);
+        const uint32_t lo = (p >> P::LO_P[i]) & FM;
+        const uint32_t hi = (p >> (16 + P::HI_P[i])) & FM;
+        constexpr int klo = P::LO_K[i], khi = P::HI_K[i];
+        constexpr int glo = P::LO_E[i] + P::LO_P[i], ghi = P::HI_E[i] + P::HI_P[i];  // significance
+        c[klo >> 2] |= (lo << glo) << (8 * (klo & 3));
+        c[khi >> 2] |= (hi << ghi) << (8 * (khi & 3));
+    });
+    uint4* dst = reinterpret_cast<uint4*>(codes + t * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
+}
+
+template <int BITS, int MT, int R, bool SW>
+hipError_t launch_one(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+{
+    hipLaunchKernelGGL((proj_kernel<BITS, MT, R, SW>), dim3(c.blocks), dim3(64 * c.nwaves), c.lds, s, a);
+    return hipGetLastError();
+}
+
+template <int BITS, bool SW>
+hipError_t launch_bits_impl(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+{
+#define AQG_CASE_MT(MTV)                                                    \
+    case MTV:                                                               \
+        return c.R == 2 ? launch_one<BITS, MTV, 2, SW>(a, c, s)             \
+                        : launch_one<BITS, MTV, 1, SW>(a, c, s);
+    switch (c.MT) {
+        AQG_CASE_MT(1)
+        AQG_CASE_MT(2)
+        AQG_CASE_MT(4)
+        AQG_CASE_MT(8)
+        AQG_CASE_MT(16)
+        AQG_CASE_MT(32)
+        default: return hipErrorInvalidValue;
+    }
+#undef AQG_CASE_MT
+}
+
+}  // namespace detail
+}  // namespace aqg

@@ -1,0 +1,374 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element.
+
+Bars (all through the C ABI, via the Python binding):
+  * unpacked codes: bit-exact with the oracle's unpack;
+  * fp32 outputs: |y - y_ref| <= 2e-3 * sum|w||x| + 1e-6 per element;
+  * bf16 outputs: exactly RNE of the same call's fp32 outputs;
+  * LM heads: row argmax equal to the oracle's (ambiguous only within tolerance);
+  * exact cases (one-hot rows, small integers, closed forms): bit-exact;
+  * rows are independent: y(M)[m] == y(1, x[m]) bit for bit within the path;
+  * no write outside the output (canary guards), deterministic repeats.
+Inputs follow the seeded synthetic recipe in synth.py.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import affine_quantized_gemv_amd as aqg
+import oracle
+import synth
+from gpu_helpers import (Guarded, assert_within, bf16_dev, check_argmax, metrics, run_guarded,
+                         u32_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    aqg.load()
+    yield
+
+
+# ------------------------------------------------------------ cached inputs
+
+@functools.lru_cache(maxsize=None)
+def dense_case(cfg, name, N, K):
+    x = synth.activations(cfg, K)
+    W = synth.dense_weight(cfg, name, N, K)
+    return x, W, bf16_dev(x), bf16_dev(W)
+
+
+@functools.lru_cache(maxsize=None)
+def dense_ref(cfg, name, N, K):
+    x, W, _, _ = dense_case(cfg, name, N, K)
+    return oracle.gemv_bf16(x, W)   # at M = 32; smaller M are prefixes
+
+
+@functools.lru_cache(maxsize=None)
+def affine_case(cfg, name, bits, N, K):
+    x = synth.activations(cfg, K)
+    aw = synth.affine_weight(cfg, name, bits, N, K)
+    return x, aw, bf16_dev(x), u32_dev(aw.words), bf16_dev(aw.scales), bf16_dev(aw.biases)
+
+
+@functools.lru_cache(maxsize=None)
+def affine_ref(cfg, name, bits, N, K, M):
+    x, aw = affine_case(cfg, name, bits, N, K)[:2]
+    return oracle.gemv_affine(x[:M], aw.words, aw.scales, aw.biases, bits)
+
+
+def gemv_dense_gpu(xd, Wd, M):
+    return lambda out: aqg.gemv_bf16(xd[:M], Wd, out=out)
+
+
+def gemv_affine_gpu(xd, wq, sd, bd, bits, M):
+    return lambda out: aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out=out)
+
+
+# ------------------------------------------------------------------ codes
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("shape", synth.MIXED_SHAPES, ids=lambda s: s[0])
+def test_unpack_codes_bit_exact_mixed_width(bits, shape):
+    name, N, K = shape
+    _, aw, _, wq, _, _ = affine_case(synth.CFG_MIXED_WIDTH, name, bits, N, K)
+    got = aqg.unpack_codes(wq, bits, K).cpu().numpy()
+    assert np.array_equal(got, oracle.unpack(aw.words, bits, K))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_unpack_codes_bit_exact_small_and_patterns(bits):
+    K = 192
+    codes = [synth.random_codes((37, K), bits, 50, "up/%d" % bits)]
+    top = (1 << bits) - 1
+    codes.append(np.full((1, K), top, np.uint8))
+    codes.append(np.zeros((1, K), np.uint8))
+    codes.append((np.arange(K) % (top + 1)).astype(np.uint8)[None, :])
+    codes = np.vstack(codes)
+    words = oracle.pack(codes, bits)
+    got = aqg.unpack_codes(u32_dev(words), bits, K).cpu().numpy()
+    assert np.array_equal(got, codes)
+
+
+def test_unpack_codes_lm_head_4bit():
+    name, N, K = synth.AFFINE4_SHAPES[3]
+    _, aw, _, wq, _, _ = affine_case(synth.CFG_AFFINE4_08B, name, 4, N, K)
+    assert np.array_equal(aqg.unpack_codes(wq, 4, K).cpu().numpy(), oracle.unpack(aw.words, 4, K))
+
+
+# ------------------------------------------------------------------ dense
+
+def test_dense_config1_m1():
+    N = K = 1536
+    x, W, xd, Wd = dense_case(synth.CFG_DENSE_1536, "W", N, K)
+    y = run_guarded(gemv_dense_gpu(xd, Wd, 1), 1, N)
+    ref, A = oracle.gemv_bf16(x[:1], W)
+    assert_within(y, ref, oracle.tolerance(A), "dense 1536x1536 M=1")
+    print(metrics(y, ref, A))
+
+
+@pytest.mark.parametrize("M", synth.DENSE_DECODE_M)
+@pytest.mark.parametrize("shape", synth.DENSE_DECODE_SHAPES[:7], ids=lambda s: s[0])
+def test_dense_decode_projections(shape, M):
+    name, N, K = shape
+    x, W, xd, Wd = dense_case(synth.CFG_DENSE_DECODE, name, N, K)
+    ref, A = dense_ref(synth.CFG_DENSE_DECODE, name, N, K)
+    y = run_guarded(gemv_dense_gpu(xd, Wd, M), M, N)
+    assert_within(y, ref[:M], oracle.tolerance(A[:M]), "%s M=%d" % (name, M))
+
+
+@functools.lru_cache(maxsize=None)
+def dense_lm_head():
+    name, N, K = synth.DENSE_DECODE_SHAPES[7]
+    x = synth.activations(synth.CFG_DENSE_DECODE, K)
+    W = synth.dense_weight(synth.CFG_DENSE_DECODE, name, N, K)
+    ref, A = oracle.gemv_bf16(x, W)
+    # plant a unique argmax with margin for row 0: W[n*] = 2 W[n0] (exact in bf16)
+    n0 = int(oracle.argmax(ref[:1])[0])
+    n_star = (n0 + N // 2) % N
+    if ref[0, n0] > 0:
+        W = W.copy()
+        W[n_star] = W[n0] + 0x80  # +1 in the exponent field doubles a bf16 (no zeros/denormals here)
+        assert np.all((W[n0] & 0x7F80) != 0)
+        ref2, A2 = oracle.gemv_bf16(x, W[n_star:n_star + 1])
+        ref[:, n_star], A[:, n_star] = ref2[:, 0], A2[:, 0]
+    return x, W, bf16_dev(x), bf16_dev(W), ref, A, n_star
+
+
+@pytest.mark.parametrize("M", synth.DENSE_DECODE_M)
+def test_dense_lm_head_values_and_argmax(M):
+    x, W, xd, Wd, ref, A, n_star = dense_lm_head()
+    N = W.shape[0]
+    y = run_guarded(gemv_dense_gpu(xd, Wd, M), M, N)
+    assert_within(y, ref[:M], oracle.tolerance(A[:M]), "lm_head M=%d" % M)
+    amb = check_argmax(y, ref[:M], A[:M])
+    print("lm_head M=%d: %d argmax rows within tolerance of a tie" % (M, amb))
+    assert oracle.argmax(y)[0] == n_star
+
+
+def test_dense_one_hot_exact():
+    N, K = 513, 1536
+    W = synth.dense_weight(70, "onehot", N, K)
+    cols = (np.arange(32) * 47 + 5) % K
+    x = np.zeros((32, K), np.uint16)
+    x[np.arange(32), cols] = 0x3F80
+    y = run_guarded(gemv_dense_gpu(bf16_dev(x), bf16_dev(W), 32), 32, N)
+    assert np.array_equal(y, oracle.bf16_to_f64(W[:, cols]).T)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (3, 5, 64), (5, 77, 136), (17, 1000, 520), (31, 129, 2048),
+                                   (2, 257, 8192), (32, 64, 4096)])
+def test_dense_ragged_shapes(M, N, K):
+    x = synth.normal_bf16((M, K), 1.0, 71, "rg/x/%d" % K)
+    W = synth.normal_bf16((N, K), 0.02, 71, "rg/W/%d/%d" % (N, K))
+    y = run_guarded(gemv_dense_gpu(bf16_dev(x), bf16_dev(W), M), M, N)
+    ref, A = oracle.gemv_bf16(x, W)
+    assert_within(y, ref, oracle.tolerance(A), "dense %dx%dx%d" % (M, N, K))
+
+
+def test_dense_small_integers_exact():
+    M, N, K = 3, 5, 128
+    g = synth.rng(72, "ex")
+    x = synth.to_bf16_bits(g.integers(-4, 5, size=(M, K)).astype(np.float64))
+    W = synth.to_bf16_bits(g.integers(-8, 9, size=(N, K)).astype(np.float64) / 8)
+    y = run_guarded(gemv_dense_gpu(bf16_dev(x), bf16_dev(W), M), M, N)
+    ref, _ = oracle.gemv_bf16(x, W)
+    assert np.array_equal(y, ref)
+
+
+def test_dense_rows_independent_of_m():
+    name, N, K = synth.DENSE_DECODE_SHAPES[4]
+    x, W, xd, Wd = dense_case(synth.CFG_DENSE_DECODE, name, N, K)
+    ones = [aqg.gemv_bf16(xd[m:m + 1], Wd, out_dtype=torch.float32) for m in range(32)]
+    y1 = torch.cat(ones).cpu().numpy()
+    for M in (2, 3, 4, 8, 13, 16, 32):
+        yM = aqg.gemv_bf16(xd[:M], Wd, out_dtype=torch.float32).cpu().numpy()
+        assert np.array_equal(yM, y1[:M]), "M=%d" % M
+
+
+def test_dense_deterministic():
+    name, N, K = synth.DENSE_DECODE_SHAPES[6]
+    _, _, xd, Wd = dense_case(synth.CFG_DENSE_DECODE, name, N, K)
+    a = aqg.gemv_bf16(xd[:8], Wd, out_dtype=torch.float32).cpu().numpy()
+    b = aqg.gemv_bf16(xd[:8], Wd, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ----------------------------------------------------------------- SwiGLU
+
+@functools.lru_cache(maxsize=None)
+def swiglu_case():
+    N, K = synth.SWIGLU_SHAPE
+    x = synth.activations(synth.CFG_SWIGLU, K)
+    Wg = synth.dense_weight(synth.CFG_SWIGLU, "gate", N, K)
+    Wu = synth.dense_weight(synth.CFG_SWIGLU, "up", N, K)
+    r = oracle.swiglu_bf16(x, Wg, Wu)
+    return x, Wg, Wu, bf16_dev(x), bf16_dev(Wg), bf16_dev(Wu), r
+
+
+@pytest.mark.parametrize("M", synth.SWIGLU_M)
+def test_swiglu_against_unfused_oracle_chain(M):
+    x, Wg, Wu, xd, Wgd, Wud, r = swiglu_case()
+    N = Wg.shape[0]
+    y = run_guarded(lambda out: aqg.swiglu_bf16(xd[:M], Wgd, Wud, out=out), M, N)
+    tol = oracle.swiglu_tolerance(r["g"][:M], r["u"][:M], r["Ag"][:M], r["Au"][:M], r["out"][:M])
+    assert_within(y, r["out"][:M], tol, "swiglu M=%d" % M)
+
+
+def test_swiglu_zero_weights_give_exact_zero():
+    N, K = 300, 1536
+    x = bf16_dev(synth.activations(synth.CFG_SWIGLU, K)[:4])
+    W = bf16_dev(synth.dense_weight(73, "sz", N, K))
+    Z = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda:0")
+    for a, b in ((Z, W), (W, Z)):
+        y = aqg.swiglu_bf16(x, a, b, out_dtype=torch.float32).cpu().numpy()
+        assert np.all(y == 0)
+
+
+def test_swiglu_large_negative_gate_is_near_zero():
+    K = 64
+    x = np.full((1, K), 0x3F80, np.uint16)          # ones
+    Wg = np.full((2, K), 0xC100, np.uint16)         # -8  -> g = -512
+    Wu = np.full((2, K), 0x3F80, np.uint16)         # 1   -> u = 64
+    y = aqg.swiglu_bf16(bf16_dev(x), bf16_dev(Wg), bf16_dev(Wu), out_dtype=torch.float32).cpu().numpy()
+    assert np.all(np.abs(y) < 1e-30)
+
+
+# ----------------------------------------------------------------- affine
+
+@pytest.mark.parametrize("M", synth.AFFINE4_M)
+@pytest.mark.parametrize("shape", synth.AFFINE4_SHAPES[:3], ids=lambda s: s[0])
+def test_affine4_decoder_shapes(shape, M):
+    name, N, K = shape
+    x, aw, xd, wq, sd, bd = affine_case(synth.CFG_AFFINE4_08B, name, 4, N, K)
+    ref, A = affine_ref(synth.CFG_AFFINE4_08B, name, 4, N, K, 16)
+    y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, 4, M), M, N)
+    assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q4 %s M=%d" % (name, M))
+
+
+@pytest.mark.parametrize("M", synth.AFFINE4_M)
+def test_affine4_lm_head_values_and_argmax(M):
+    name, N, K = synth.AFFINE4_SHAPES[3]
+    x, aw, xd, wq, sd, bd = affine_case(synth.CFG_AFFINE4_08B, name, 4, N, K)
+    ref, A = affine_ref(synth.CFG_AFFINE4_08B, name, 4, N, K, 16)
+    y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, 4, M), M, N)
+    assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q4 lm_head M=%d" % M)
+    amb = check_argmax(y, ref[:M], A[:M])
+    print("q4 lm_head M=%d: %d argmax rows within tolerance of a tie" % (M, amb))
+
+
+def test_affine4_lm_head_planted_argmax():
+    """Same codes with doubled scale and bias in row n*: y[n*] = 2 y[n0] exactly in
+    the oracle, a unique argmax with margin when y[n0] > 0."""
+    name, N, K = synth.AFFINE4_SHAPES[3]
+    x, aw, xd, wq, sd, bd = affine_case(synth.CFG_AFFINE4_08B, name, 4, N, K)
+    ref, A = affine_ref(synth.CFG_AFFINE4_08B, name, 4, N, K, 16)
+    n0 = int(oracle.argmax(ref[:1])[0])
+    assert ref[0, n0] > 0
+    n_star = (n0 + 7919) % N
+    words, s, b = aw.words.copy(), aw.scales.copy(), aw.biases.copy()
+    words[n_star], s[n_star], b[n_star] = words[n0], s[n0] + 0x80, b[n0] + 0x80
+    y = aqg.gemv_affine(xd[:1], u32_dev(words), bf16_dev(s), bf16_dev(b), 4,
+                        out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    assert int(oracle.argmax(y)[0]) == n_star
+
+
+@pytest.mark.parametrize("M", synth.MIXED_M)
+@pytest.mark.parametrize("bits", synth.MIXED_BITS)
+@pytest.mark.parametrize("shape", synth.MIXED_SHAPES, ids=lambda s: s[0])
+def test_affine_mixed_width(shape, bits, M):
+    name, N, K = shape
+    x, aw, xd, wq, sd, bd = affine_case(synth.CFG_MIXED_WIDTH, name, bits, N, K)
+    ref, A = affine_ref(synth.CFG_MIXED_WIDTH, name, bits, N, K, 16)
+    y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, M), M, N)
+    assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q%d %s M=%d" % (bits, name, M))
+
+
+@pytest.mark.parametrize("M", [1, 5, 32])
+def test_affine_q7(M):
+    N, K = 700, 1024
+    x, aw, xd, wq, sd, bd = affine_case(74, "q7", 7, N, K)
+    ref, A = affine_ref(74, "q7", 7, N, K, 32)
+    y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, 7, M), M, N)
+    assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q7 M=%d" % M)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_affine_one_hot_reads_codes_exactly(bits):
+    """s = 1, bias = 0, x rows one-hot: y[m, n] = q[n, col_m] exactly -- pins the
+    in-GEMV unpack and the activation layout for 32 columns per call."""
+    N, K = 300, 1024
+    words = synth.random_words((N, K * bits // 32), 75, "oh/%d" % bits)
+    codes = oracle.unpack(words, bits, K)
+    cols = (np.arange(32) * 31 + bits) % K
+    x = np.zeros((32, K), np.uint16)
+    x[np.arange(32), cols] = 0x3F80
+    ones = np.full((N, K // 64), 0x3F80, np.uint16)
+    zeros = np.zeros((N, K // 64), np.uint16)
+    for M in (1, 32):
+        y = run_guarded(gemv_affine_gpu(bf16_dev(x), u32_dev(words), bf16_dev(ones), bf16_dev(zeros), bits, M),
+                        M, N)
+        assert np.array_equal(y, codes[:, cols[:M]].T.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_affine_small_integers_exact(bits):
+    M, N, K = 3, 5, 192
+    g = synth.rng(76, "ex/%d" % bits)
+    x = synth.to_bf16_bits(g.integers(-4, 5, size=(M, K)).astype(np.float64))
+    words = synth.random_words((N, K * bits // 32), 76, "exw/%d" % bits)
+    s = synth.to_bf16_bits(2.0 ** -g.integers(0, 4, size=(N, K // 64)))
+    b = synth.to_bf16_bits(g.integers(-3, 4, size=(N, K // 64)).astype(np.float64))
+    y = run_guarded(gemv_affine_gpu(bf16_dev(x), u32_dev(words), bf16_dev(s), bf16_dev(b), bits, M), M, N)
+    ref, _ = oracle.gemv_affine(x, words, s, b, bits)
+    assert np.array_equal(y, ref)
+
+
+def test_affine_closed_form_half():
+    codes = np.full((1, 64), 5, np.uint8)
+    words = oracle.pack(codes, 4)
+    s = np.array([[0x3C00]], np.uint16)
+    b = np.array([[0xBD00]], np.uint16)
+    x = np.full((1, 64), 0x3F80, np.uint16)
+    y = aqg.gemv_affine(bf16_dev(x), u32_dev(words), bf16_dev(s), bf16_dev(b), 4,
+                        out_dtype=torch.float32).cpu().numpy()
+    assert y[0, 0] == 0.5
+
+
+@pytest.mark.parametrize("bits", [2, 3, 5, 6])
+def test_affine_cross_width_widened_to_8bit(bits):
+    """The same codes stored at width b and widened to 8 bits give the same y (within
+    tolerance: the two widths sum their code pairs in different orders)."""
+    M, N, K = 4, 1000, 4096
+    x, aw, xd, wq, sd, bd = affine_case(synth.CFG_MIXED_WIDTH, "sq_4096", bits, N, K)
+    w8 = oracle.pack(oracle.unpack(aw.words, bits, K), 8)
+    yb = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    y8 = aqg.gemv_affine(xd[:M], u32_dev(w8), sd, bd, 8, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    _, A = oracle.gemv_affine(x[:M], aw.words, aw.scales, aw.biases, bits)
+    assert_within(yb, y8, 2 * oracle.tolerance(A), "q%d vs widened q8" % bits)
+
+
+@pytest.mark.parametrize("M,N,K,bits", [(1, 1, 64, 4), (3, 7, 64, 3), (5, 77, 128, 5), (17, 1000, 576, 2),
+                                        (31, 129, 3584, 6), (2, 3000, 8192, 4), (32, 100, 4096, 8)])
+def test_affine_ragged_shapes(M, N, K, bits):
+    x = synth.normal_bf16((M, K), 1.0, 77, "ar/x/%d" % K)
+    aw = synth.affine_weight(77, "ar", bits, N, K)
+    y = run_guarded(gemv_affine_gpu(bf16_dev(x), u32_dev(aw.words), bf16_dev(aw.scales), bf16_dev(aw.biases),
+                                    bits, M), M, N)
+    ref, A = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
+    assert_within(y, ref, oracle.tolerance(A), "q%d %dx%dx%d" % (bits, M, N, K))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_affine_rows_independent_of_m(bits):
+    name, N, K = synth.MIXED_SHAPES[0]
+    x, aw, xd, wq, sd, bd = affine_case(synth.CFG_MIXED_WIDTH, name, bits, N, K)
+    y1 = torch.cat([aqg.gemv_affine(xd[m:m + 1], wq, sd, bd, bits, out_dtype=torch.float32)
+                    for m in range(32)]).cpu().numpy()
+    for M in (2, 4, 7, 8, 16, 32):
+        yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
+        assert np.array_equal(yM, y1[:M]), "M=%d" % M
