@@ -102,7 +102,7 @@ int run_projection(int bits, bool swiglu, const void* x, const void* w0, const v
     st = check_device();
     if (st != AQG_OK) return st;
 
-    const aqg::LaunchCfg cfg = aqg::choose_valu(bits, swiglu, M, N, K);
+    const aqg::LaunchCfg cfg = aqg::choose_config(bits, swiglu, M, N, K);
     aqg::ProjArgs a{};
     a.x = static_cast<const uint16_t*>(x);
     a.w0 = w0;
@@ -115,8 +115,10 @@ int run_projection(int bits, bool swiglu, const void* x, const void* w0, const v
     a.K = K;
     a.KT = cfg.KT;
     a.lpr_log2 = cfg.lpr_log2;
+    a.ksplit_log2 = cfg.ksplit_log2;
+    a.tpw = cfg.tpw;
     a.out_f32 = out_dtype == AQG_OUT_F32;
-    return finish(aqg::launch_valu(bits, swiglu, a, cfg, static_cast<hipStream_t>(stream)));
+    return finish(aqg::launch_proj(bits, swiglu, a, cfg, static_cast<hipStream_t>(stream)));
 }
 
 int run_affine(int bits, const void* x, const uint32_t* Wq, const void* scales, const void* biases,

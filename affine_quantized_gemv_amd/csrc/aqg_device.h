@@ -9,8 +9,17 @@ namespace aqg {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// (a & m) | c -- one v_and_or_b32.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | c; }
+// (a & m) | c -- one v_and_or_b32.  Written as asm because, with m and c
+// compile-time constants, the compiler would otherwise emit v_and_b32 +
+// v_or_b32 with literal operands (a 3-operand VALU op cannot take literals
+// here); m goes to a scalar register and c to a vector register, both loop
+// invariant.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+    return r;
+}
 
 // 32 consecutive bits of a group's LSB-first code stream (NW words), starting
 // at stream bit ST; bits outside the stream read as zero.  ST is a compile-time
@@ -81,6 +90,20 @@ __device__ __forceinline__ float segment_sum(float v, int L)
     if (L >= 4) v += dpp_f32<0x140>(v);  // row_mirror
     return v;
 }
+
+// Keep the code on each side of this point on its own side: a compiler
+// memory barrier (no load moves across it) plus a machine-scheduler barrier.
+// Used between the chunks of an unrolled unit so that each chunk's operands
+// and LDS reads stay short-lived.
+__device__ __forceinline__ void code_fence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Make v's current value an input and output of an empty asm statement: every
+// instruction that produces v is placed before this point and every use after.
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int I> struct Int { static constexpr int value = I; };

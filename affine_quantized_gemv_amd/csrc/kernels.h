@@ -1,5 +1,6 @@
 // Host-side interface between the C ABI (abi.hip) and the kernels
-// (kernels.hip).  Not installed; not part of the public ABI.
+// (kernels.hip, proj_b*.hip, mfma_*.hip).  Not installed; not part of the
+// public ABI.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -17,29 +18,46 @@ struct ProjArgs {
     void* y;                 // bf16 or f32 [M][N]
     int M, N, K;
     int KT;                  // K elements staged in LDS per tile
-    int lpr_log2;            // log2 of lanes that share one weight row
+    int lpr_log2;            // VALU path: log2 of lanes that share one weight row
+    int ksplit_log2;         // MFMA path: log2 of wavefronts splitting K per row group
     int out_f32;             // 1: store fp32, 0: store bf16 (RNE)
+    int64_t tpw;             // stream path: row tiles per super-tile
+    int64_t tmax;            // stream path: most row tiles any wavefront finishes
 };
+
+enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2 };
 
 // Launch geometry chosen for a call.
 struct LaunchCfg {
+    int path;       // PATH_VALU or PATH_MFMA
     int MT;         // padded M (1, 2, 4, 8, 16, 32)
-    int R;          // rows per lane (1 or 2)
-    int lpr_log2;   // lanes per weight row = 2^lpr_log2 (<= 16)
+    int R;          // VALU: rows per lane; MFMA: 16-row tiles per row group (1 or 2)
+    int lpr_log2;   // VALU: lanes per weight row = 2^lpr_log2 (<= 64)
+    int ksplit_log2;  // MFMA: wavefronts splitting K per row group = 2^ksplit_log2
     int KT;         // K-tile in elements
+    int xreg;       // stream: x held in registers (affine, one group per lane)
+    int64_t tpw;    // stream: row tiles per wavefront
     int nwaves;     // waves per workgroup
     int blocks;     // workgroups
     size_t lds;     // dynamic LDS bytes
 };
 
-// Per-width launchers, each instantiated in its own translation unit
+// Per-width VALU launchers, each instantiated in its own translation unit
 // (proj_b*.hip) so the kernels compile in parallel.
 template <int BITS, bool SWIGLU>
 hipError_t launch_bits(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
+// Per-width persistent streaming launchers (also in proj_b*.hip).
+template <int BITS, bool SWIGLU>
+hipError_t launch_stream(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+// Dense / SwiGLU matrix-core launcher (mfma_dense.hip).
+template <bool SWIGLU>
+hipError_t launch_mfma(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
 // bits: 0 = dense bf16, 2..8 = affine width.
-LaunchCfg choose_valu(int bits, bool swiglu, int M, int N, int K);
-hipError_t launch_valu(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K);
+hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_unpack(int bits, const uint32_t* Wq, uint8_t* codes, int N, int K, hipStream_t s);
 
 }  // namespace aqg

@@ -1,33 +1,42 @@
-// Launch-geometry choice and dispatch to the per-width kernel instantiations
-// (proj_b*.hip), plus the code-unpack kernel.
-#include "proj_kernel.h"
+// Launch-geometry choice and dispatch: VALU kernels (proj_b*.hip) for M <= 8
+// and for affine weights, matrix-core kernels (mfma_dense.hip) for dense and
+// SwiGLU calls with M = 9..32; plus the code-unpack kernel.
+#include "stream_kernel.h"
 
 namespace aqg {
-namespace detail {
+namespace {
 
 int ctz_u(unsigned v) { int n = 0; while (v && !(v & 1u)) { v >>= 1; ++n; } return n; }
 
-}  // namespace detail
-using detail::ctz_u;
-using detail::kLdsBudget;
-using detail::kMaxThreads;
+constexpr size_t kLdsBudget = detail::kLdsBudget;
+constexpr int kValuThreads = detail::kMaxThreads;
 
 LaunchCfg choose_valu(int bits, bool swiglu, int M, int N, int K)
 {
     LaunchCfg c{};
+    c.path = PATH_VALU;
     c.MT = 1;
     while (c.MT < M) c.MT <<= 1;
     const int UK = bits ? 64 : 8;
     int per_unit = 16;  // LDS bytes per (m, unit)
     if (bits) per_unit = (bits == 8 ? 16 * 16 : 16 * 8) + 8;
     const int U = K / UK;                                   // units per row
-    // Lanes per row: the largest power of two (<= 16) dividing U that still
-    // lets a K-tile of 2^L units fit at the largest M.  It depends on (bits, K)
-    // only, so every M sums each output in the same order.
-    int L = ctz_u((unsigned)U);
-    if (L > 4) L = 4;
+    // Lanes per row, 2^L.  Upper bound: a power of two dividing U (each lane
+    // gets the same number of units), at most 64, and small enough that a
+    // K-tile of 2^L units fits in LDS at the largest M.  Lower bound: 2^L
+    // consecutive units span >= 128 contiguous bytes of a row.  Between the
+    // two, the smallest L that still gives ~2048 wavefronts.  The choice
+    // depends on (bits, N, K) only, so every M sums each output in the same
+    // order.
+    const int unit_bytes = bits ? 8 * bits : 16;
+    int Lcap = ctz_u((unsigned)U);
+    if (Lcap > 6) Lcap = 6;
     const int64_t fit_max = (int64_t)kLdsBudget / ((int64_t)32 * per_unit);
-    while (L > 0 && fit_max < (1 << L)) --L;
+    while (Lcap > 0 && fit_max < (1 << Lcap)) --Lcap;
+    int L = 0;
+    while ((unit_bytes << L) < 128) ++L;
+    if (L > Lcap) L = Lcap;
+    while (L < Lcap && (((int64_t)N << L) >> 6) < 2048) ++L;
     const int64_t fit = (int64_t)kLdsBudget / ((int64_t)c.MT * per_unit);  // units per tile
     const int LPR = 1 << L;
     int64_t kt_units = (fit / LPR) * LPR;
@@ -38,18 +47,120 @@ LaunchCfg choose_valu(int bits, bool swiglu, int M, int N, int K)
     c.lds = (size_t)c.MT * kt_units * per_unit;
     const int G = 64 >> L;
     const int64_t tiles1 = ((int64_t)N + G - 1) / G;        // wave tiles at R = 1
-    c.R = (!swiglu && c.MT <= 16 && tiles1 >= 4096) ? 2 : 1;
+    c.R = (!swiglu && tiles1 >= 8192) ? 2 : 1;
     const int64_t wave_tiles = ((int64_t)N + G * c.R - 1) / (G * c.R);
-    int64_t nw = wave_tiles / 512;
-    if (nw < 1) nw = 1;
-    if (nw > kMaxThreads / 64) nw = kMaxThreads / 64;
+    int64_t nw = kValuThreads / 64;
+    if (nw > wave_tiles) nw = wave_tiles;
     c.nwaves = (int)nw;
     c.blocks = (int)((wave_tiles + nw - 1) / nw);
     return c;
 }
 
-hipError_t launch_valu(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+// Matrix-core geometry: workgroups of 8 wavefronts = NR row groups x NK
+// k-splits.  NK grows (up to 8) until there are ~2048 wavefronts; large N
+// uses NK = 1 and two 16-row tiles per row group.  Depends on (N, K) only.
+LaunchCfg choose_mfma(bool swiglu, int M, int N, int K)
 {
+    LaunchCfg c{};
+    c.path = PATH_MFMA;
+    c.MT = M <= 16 ? 16 : 32;
+    const int64_t tiles16 = ((int64_t)N + 15) / 16;
+    int nk = 1;
+    while (nk < 8 && tiles16 * nk < 2048) nk <<= 1;
+    const int nr = 8 / nk;
+    c.R = (nk == 1 && tiles16 >= 4096) ? 2 : 1;
+    c.ksplit_log2 = ctz_u((unsigned)nk);
+    c.nwaves = 8;
+    c.blocks = (int)((tiles16 + (int64_t)nr * c.R - 1) / ((int64_t)nr * c.R));
+    int kt = (int)(kLdsBudget / ((size_t)c.MT * 2)) / 32 * 32;
+    if (kt > K) kt = K;
+    c.KT = kt;
+    size_t lds = (size_t)c.MT * kt * 2;
+    const size_t red = nk > 1 ? (size_t)c.nwaves * (swiglu ? 2 : 1) * c.R * (c.MT / 16) * 4 * 64 * 4 : 0;
+    c.lds = lds > red ? lds : red;
+    return c;
+}
+
+int ceil_log2(int v) { int l = 0; while ((1 << l) < v) ++l; return l; }
+
+// Persistent streaming geometry (M <= 8, large N).  Lanes per row: dense up
+// to 64 (one row per tile, 1 KB per load); affine: the smallest power of two
+// >= the groups per row (<= 64), so each lane owns at most one group per row
+// and, for M <= 2, keeps that group's x in registers.  Returns false when the
+// shape is better served by the tiled kernel (too few row tiles to stream, or
+// x does not fit in LDS).
+bool choose_stream(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
+{
+    c = LaunchCfg{};
+    c.path = PATH_STREAM;
+    c.MT = 1;
+    while (c.MT < M) c.MT <<= 1;
+    if (c.MT > 8) return false;
+    const int UK = bits ? 64 : 8;
+    const int U = K / UK;
+    int L;
+    if (bits == 0) {
+        // one row per tile: a load instruction reads 1 KB of one row
+        L = ctz_u((unsigned)U);
+        if (L > 6) L = 6;
+    } else {
+        L = ceil_log2(U);
+        if (L > 6) L = 6;
+    }
+    c.lpr_log2 = L;
+    const int G = 64 >> L;
+    const int64_t T = ((int64_t)N + G - 1) / G;
+    if (T < 2048) return false;
+    c.xreg = (bits != 0 && !swiglu && U <= 64 && (c.MT == 1 || (c.MT == 2 && bits != 8))) ? 1 : 0;
+    const size_t per_unit = bits ? (bits == 8 ? 16 * 16 : 16 * 8) + 8 : 16;
+    c.lds = c.xreg ? 0 : (size_t)c.MT * U * per_unit;
+    // output staging, bounded with the fewest wavefronts the launch can get
+    // (one 4-wave workgroup per CU)
+    const int64_t row_bytes = bits ? (int64_t)K * bits / 8 : (int64_t)K * 2;
+    int64_t ct = 4096 / (G * row_bytes);
+    if (ct < 1) ct = 1;
+    const int64_t st = (T + ct - 1) / ct;
+    const int64_t tmax = ((st + 1023) / 1024) * ct;
+    const int vpl = (c.MT + (1 << L) - 1) >> L;
+    if (c.lds + (size_t)4 * tmax * 64 * vpl * 4 > detail::kStreamLdsMax) return false;
+    c.KT = K;
+    c.nwaves = 4;
+    c.R = 1;
+    // tiles per wavefront and the grid are set at launch from the kernel's
+    // occupancy (every resident wavefront gets an equal range of tiles)
+    return true;
+}
+
+}  // namespace
+
+LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
+{
+    if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
+    LaunchCfg c;
+    if (choose_stream(bits, swiglu, M, N, K, c)) return c;
+    return choose_valu(bits, swiglu, M, N, K);
+}
+
+hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+{
+    if (c.path == PATH_MFMA) {
+        if (bits != 0) return hipErrorInvalidValue;
+        return swiglu ? launch_mfma<true>(a, c, s) : launch_mfma<false>(a, c, s);
+    }
+    if (c.path == PATH_STREAM) {
+        if (swiglu) return bits == 0 ? launch_stream<0, true>(a, c, s) : hipErrorInvalidValue;
+        switch (bits) {
+            case 0: return launch_stream<0, false>(a, c, s);
+            case 2: return launch_stream<2, false>(a, c, s);
+            case 3: return launch_stream<3, false>(a, c, s);
+            case 4: return launch_stream<4, false>(a, c, s);
+            case 5: return launch_stream<5, false>(a, c, s);
+            case 6: return launch_stream<6, false>(a, c, s);
+            case 7: return launch_stream<7, false>(a, c, s);
+            case 8: return launch_stream<8, false>(a, c, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (swiglu) {
         if (bits != 0) return hipErrorInvalidValue;
         return launch_bits<0, true>(a, c, s);

@@ -1,4 +1,4 @@
-// Small-M projection kernels for gfx950 (CDNA4, wave64).
+// Small-M projection kernels for gfx950 (CDNA4, wave64): VALU path.
 //
 // One template covers the dense bf16 GEMV, the affine b-bit GEMVs and the
 // fused up/gate SwiGLU.  Data flow per workgroup:
@@ -6,19 +6,21 @@
 //   1. Stage x (all M rows, one K-tile) into LDS.  Dense: as is.  Affine: in
 //      the order and pre-scaling the width's pair plan needs (pair_plans.h),
 //      plus two fp32 constants per (row m, group): X = sum of the group's x
-//      and T = 128 * sum of its pre-scaled x.
+//      and T = 128 * sum of its pre-scaled x.  The x loads are issued first,
+//      then the first weight loads, so HBM latency overlaps the staging.
 //   2. Each wavefront owns G*R weight rows.  Its 64 lanes form G segments of
 //      2^L lanes; a segment streams one row, each lane taking every 2^L-th
 //      "unit" of it (8 k = 16 bytes dense; one 64-code group = 8b bytes
-//      affine), so every weight byte is read from HBM exactly once.  The next
-//      unit's loads are in flight while the current one is computed.
+//      affine), so every weight byte is read from HBM exactly once.  A ring
+//      of D units per lane keeps D loads in flight while one is computed.
 //   3. Dense: acc += dot2(W pair, x pair).  Affine: 32 (64 for b = 8) bf16x2
 //      operands 0x43004300 | code fields are built from the packed words with
 //      masks (no lookup tables), d = sum dot2(operand, pre-scaled x pair), then
 //      acc += scale*(d - T) + bias*X, all in fp32 -- the group's algebraically
 //      exact factored form of sum_k x*(scale*q + bias).
-//   4. Segment sums with DPP (fixed tree), then a fused epilogue: fp32 or RNE
-//      bf16 store; SwiGLU applies silu(g)*u in fp32 first.
+//   4. Segment sums (DPP within 16 lanes, lane shuffles across 16 and 32; one
+//      fixed tree), then a fused epilogue: fp32 or RNE bf16 store; SwiGLU
+//      applies silu(g)*u in fp32 first.
 //
 // Formats: AstrAI decode_linear_benchmark.md (commit message: BF16 decode
 // GEMV, fused BF16 up/gate SwiGLU); TensorFold PR #849 "qwen3_5 cuda:
@@ -33,7 +35,7 @@
 namespace aqg {
 namespace detail {
 
-constexpr int kMaxThreads = 512;
+constexpr int kMaxThreads = 256;
 constexpr size_t kLdsBudget = 64 * 1024;
 
 template <int BITS> struct Geo {
@@ -42,6 +44,7 @@ template <int BITS> struct Geo {
     static constexpr int NP = PairPlan<BITS>::NP;
     static constexpr int NCH = NP / 4;        // uint4 x-chunks per (m, unit)
     static constexpr int LDS_PER_UNIT = 16 * NCH + 8;  // bytes per (m, unit)
+    static constexpr int D = 2;               // units in flight per lane
 };
 template <> struct Geo<0> {
     static constexpr int UK = 8;
@@ -49,6 +52,7 @@ template <> struct Geo<0> {
     static constexpr int NP = 4;
     static constexpr int NCH = 1;
     static constexpr int LDS_PER_UNIT = 16;
+    static constexpr int D = 4;
 };
 
 __device__ __forceinline__ uint32_t half_of(const uint32_t* xw, int k)
@@ -57,7 +61,8 @@ __device__ __forceinline__ uint32_t half_of(const uint32_t* xw, int k)
 }
 
 // Load one unit (NW words) of a row.  Even widths and dense: 16-byte loads;
-// odd widths: 8-byte loads (a group of an odd width is 8b bytes).
+// odd widths: 8-byte loads (a group of an odd width is 8b bytes).  Weights are
+// read once, so the loads are non-temporal.
 template <int BITS>
 __device__ __forceinline__ void load_unit(const uint32_t* __restrict__ p, uint32_t* w)
 {
@@ -83,59 +88,194 @@ __device__ __forceinline__ void load_unit(const uint32_t* __restrict__ p, uint32
 
 // ---------------------------------------------------------------- staging
 
-// Dense: x[m][kt .. kt+kw) -> lds uint4 [MT][kw/8]; rows m >= M are zero.
-template <int MT>
-__device__ void stage_dense(const ProjArgs& a, int kt, int kw, uint4* xs)
-{
-    const int upm = kw / 8;
-    for (int t = threadIdx.x; t < MT * upm; t += blockDim.x) {
-        const int m = t / upm, u = t - m * upm;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (m < a.M)
-            v = *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt + 8 * u);
-        xs[t] = v;
-    }
-}
-
-// Affine: per (m, group g of the tile) write NCH uint4 of pre-scaled bf16
-// pairs in plan order to xp[(m*NCH + c)*ngt + g] and (X, T) to xc[m*ngt + g].
-template <int BITS, int MT>
-__device__ void stage_affine(const ProjArgs& a, int kt, int kw, uint4* xp, float2* xc)
+// Pre-scaled pair operands and group constants of one 64-k group of x, in the
+// width's plan order: xq[i] = (x[LO_K] * 2^LO_E) | (x[HI_K] * 2^HI_E) << 16,
+// X = sum of the group's x (each code once: its significance-0 subcode),
+// T = 128 * sum of the pre-scaled halves.  Sums run in pair order, low half
+// first; every caller uses this one routine, so the constants are identical
+// wherever x is kept.
+template <int BITS>
+__device__ __forceinline__ void group_x_operands(const uint32_t (&xw)[32], uint32_t (&xq)[PairPlan<BITS>::NP],
+                                                 float& X, float& T)
 {
     using P = PairPlan<BITS>;
-    constexpr int NCH = Geo<BITS>::NCH;
-    const int ngt = kw / 64;
-    for (int t = threadIdx.x; t < MT * ngt; t += blockDim.x) {
+    float xs = 0.0f, ts = 0.0f;
+    static_for<0, P::NP>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const uint32_t hl = half_of(xw, P::LO_K[i]);
+        const uint32_t hh = half_of(xw, P::HI_K[i]);
+        if constexpr (P::LO_E[i] + P::LO_P[i] == 0) xs += bf16_to_f32(hl);
+        if constexpr (P::HI_E[i] + P::HI_P[i] == 0) xs += bf16_to_f32(hh);
+        const uint32_t lo = bf16_scale_pow2<P::LO_E[i]>(hl);
+        const uint32_t hi = bf16_scale_pow2<P::HI_E[i]>(hh);
+        xq[i] = lo | (hi << 16);
+        ts += bf16_to_f32(lo);
+        ts += bf16_to_f32(hi);
+    });
+    X = xs;
+    T = 128.0f * ts;
+}
+
+// A staging task is split into load (global -> registers) and store (compute
+// and write LDS) so the caller can issue weight loads in between.
+
+template <int BITS, int MT> struct Stager;
+
+// Dense: task t = (m, u) copies 8 bf16: x[m][kt + 8u ..] -> xs[m*upm + u].
+template <int MT> struct Stager<0, MT> {
+    struct Regs { uint4 v; };
+    const ProjArgs& a;
+    int kt, upm;
+    uint4* xs;
+    __device__ int ntasks() const { return MT * upm; }
+    __device__ Regs load(int t) const
+    {
+        const int m = t / upm, u = t - m * upm;
+        Regs r;
+        r.v = make_uint4(0, 0, 0, 0);
+        if (m < a.M) r.v = *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt + 8 * u);
+        return r;
+    }
+    __device__ void store(int t, const Regs& r) const { xs[t] = r.v; }
+};
+
+// Affine: task t = (m, group g of the tile) writes NCH uint4 of pre-scaled bf16
+// pairs in plan order to xp[(m*NCH + c)*ngt + g] and (X, T) to xc[m*ngt + g].
+template <int BITS, int MT> struct Stager {
+    struct Regs { uint32_t xw[32]; };
+    const ProjArgs& a;
+    int kt, ngt;
+    uint4* xp;
+    float2* xc;
+    __device__ int ntasks() const { return MT * ngt; }
+    __device__ Regs load(int t) const
+    {
         const int m = t / ngt, g = t - m * ngt;
-        uint32_t xw[32];
+        Regs r;
         if (m < a.M) {
             const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt + 64 * g);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 uint4 v = src[i];
-                xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+                r.xw[4 * i] = v.x; r.xw[4 * i + 1] = v.y; r.xw[4 * i + 2] = v.z; r.xw[4 * i + 3] = v.w;
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) xw[i] = 0;
+            for (int i = 0; i < 32; ++i) r.xw[i] = 0;
         }
-        float X = 0.0f;
+        return r;
+    }
+    __device__ void store(int t, const Regs& r) const
+    {
+        constexpr int NCH = Geo<BITS>::NCH;
+        const int m = t / ngt, g = t - m * ngt;
+        uint32_t xq[PairPlan<BITS>::NP];
+        float X, T;
+        group_x_operands<BITS>(r.xw, xq, X, T);
 #pragma unroll
-        for (int k = 0; k < 64; ++k) X += bf16_to_f32(half_of(xw, k));
-        float Ts = 0.0f;
+        for (int c = 0; c < NCH; ++c)
+            xp[(m * NCH + c) * ngt + g] = make_uint4(xq[4 * c], xq[4 * c + 1], xq[4 * c + 2], xq[4 * c + 3]);
+        xc[m * ngt + g] = make_float2(X, T);
+    }
+};
+
+// Sum over aligned segments of 2^L lanes (L <= 6); every lane of a segment
+// ends with the same bits.  Within 16 lanes: segment_sum's DPP tree; across
+// 16 and 32: lane swaps adding two equal-shaped partial sums.
+__device__ __forceinline__ float segment_sum64(float v, int L)
+{
+    v = segment_sum(v, L < 4 ? L : 4);
+    if (L >= 5) v += __shfl_xor(v, 16);
+    if (L >= 6) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// ------------------------------------------------------- per-unit arithmetic
+
+// One unit of R rows (S weight streams) against x from LDS:
+//   dense:  acc[s][r][m] += sum of 8 products (4 dot2)
+//   affine: d = sum over the group's pairs of dot2(operand, x' pair);
+//           acc += scale*(d - T) + bias*X.
+// xp/xc: the tile's staged x (ut units per m row); u: unit within the tile.
+template <int BITS, int MT, int S, int R>
+__device__ __forceinline__ void unit_mac(const uint32_t (&w)[S][R][Geo<BITS>::NW], const float (&sc)[R],
+                                         const float (&bi)[R], const uint4* xp, const float2* xc, int ut,
+                                         int u, float (&acc)[S][R][MT])
+{
+    if constexpr (BITS == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint4 xv = xp[m * ut + u];
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float v = acc[s][r][m];
+                    v = dot2(w[s][r][0], xv.x, v);
+                    v = dot2(w[s][r][1], xv.y, v);
+                    v = dot2(w[s][r][2], xv.z, v);
+                    v = dot2(w[s][r][3], xv.w, v);
+                    acc[s][r][m] = v;
+                }
+        }
+    } else {
+        using P = PairPlan<BITS>;
+        constexpr int NCH = Geo<BITS>::NCH;
+        // two accumulators per output (even and odd pairs of each chunk), so
+        // consecutive dot2 do not wait on each other; d = d0 + d1
+        float dd[S][R][MT], de[S][R][MT];
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) dd[s][r][m] = de[s][r][m] = 0.0f;
         static_for<0, NCH>([&](auto C) {
-            uint32_t o[4];
-            static_for<0, 4>([&](auto J) {
-                constexpr int I = 4 * decltype(C)::value + decltype(J)::value;
-                const uint32_t lo = bf16_scale_pow2<P::LO_E[I]>(half_of(xw, P::LO_K[I]));
-                const uint32_t hi = bf16_scale_pow2<P::HI_E[I]>(half_of(xw, P::HI_K[I]));
-                o[decltype(J)::value] = lo | (hi << 16);
-                Ts += bf16_to_f32(lo);
-                Ts += bf16_to_f32(hi);
-            });
-            xp[(m * NCH + decltype(C)::value) * ngt + g] = make_uint4(o[0], o[1], o[2], o[3]);
+            constexpr int c = decltype(C)::value;
+            uint32_t p[S][R][4];
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    p[s][r][0] = P::template pair<4 * c + 0>(w[s][r]);
+                    p[s][r][1] = P::template pair<4 * c + 1>(w[s][r]);
+                    p[s][r][2] = P::template pair<4 * c + 2>(w[s][r]);
+                    p[s][r][3] = P::template pair<4 * c + 3>(w[s][r]);
+                }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const uint4 xv = xp[(m * NCH + c) * ut + u];
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        float v0 = dd[s][r][m], v1 = de[s][r][m];
+                        v0 = dot2(p[s][r][0], xv.x, v0);
+                        v1 = dot2(p[s][r][1], xv.y, v1);
+                        v0 = dot2(p[s][r][2], xv.z, v0);
+                        v1 = dot2(p[s][r][3], xv.w, v1);
+                        dd[s][r][m] = v0;
+                        de[s][r][m] = v1;
+                    }
+            }
+            // keep each chunk's operands and x reads local to it
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) { pin(dd[s][r][m]); pin(de[s][r][m]); }
+            code_fence();
         });
-        xc[m * ngt + g] = make_float2(X, 128.0f * Ts);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const float2 xcv = xc[m * ut + u];
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    acc[s][r][m] = fmaf(sc[r], (dd[s][r][m] + de[s][r][m]) - xcv.y, fmaf(bi[r], xcv.x, acc[s][r][m]));
+        }
     }
 }
 
@@ -149,6 +289,7 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
     constexpr int UK = Geo<BITS>::UK;
     constexpr int NW = Geo<BITS>::NW;
     constexpr int NCH = Geo<BITS>::NCH;
+    constexpr int D = Geo<BITS>::D;
 
     const int L = a.lpr_log2;
     const int LPR = 1 << L;
@@ -185,111 +326,76 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[s][r][m] = 0.0f;
 
+    // Ring of D units of weights (and their scale/bias) per lane.
+    uint32_t wb[D][S][R][NW];
+    float sb[D][R], bb[D][R];
+
     for (int kt = 0; kt < a.K; kt += a.KT) {
         const int kw = min(a.KT, a.K - kt);
         const int ut = kw / UK;            // units in this tile (a multiple of LPR)
-        __syncthreads();                   // previous tile fully consumed
+        const int upl = ut >> L;           // units per lane in this tile
+        const int ubase = kt / UK;         // unit index of the tile start within a row
         uint4* xp = lds_u4;
         float2* xc = reinterpret_cast<float2*>(lds_u4 + MT * NCH * ut);
-        if constexpr (BITS == 0) stage_dense<MT>(a, kt, kw, xp);
-        else stage_affine<BITS, MT>(a, kt, kw, xp, xc);
-        __syncthreads();
 
-        const int ubase = kt / UK;         // unit index of the tile start within a row
-        uint32_t wc[S][R][NW], wn[S][R][NW];
-        float sc[R], bi[R], scn[R], bin[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) { sc[r] = bi[r] = scn[r] = bin[r] = 0.0f; }
-        auto fetch = [&](int u, uint32_t (&w)[S][R][NW], float (&s_)[R], float (&b_)[R]) {
+        auto fetch = [&](int d, int u) {
 #pragma unroll
             for (int s = 0; s < S; ++s)
 #pragma unroll
                 for (int r = 0; r < R; ++r)
-                    load_unit<BITS>(wrow[s][r] + (int64_t)(ubase + u) * NW, w[s][r]);
+                    load_unit<BITS>(wrow[s][r] + (int64_t)(ubase + u) * NW, wb[d][s][r]);
             if constexpr (BITS != 0) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    s_[r] = bf16_to_f32(srow[r][ubase + u]);
-                    b_[r] = bf16_to_f32(brow[r][ubase + u]);
+                    sb[d][r] = bf16_to_f32(srow[r][ubase + u]);
+                    bb[d][r] = bf16_to_f32(brow[r][ubase + u]);
                 }
             }
         };
 
-        int u = li;
-        if (u < ut) fetch(u, wc, sc, bi);
-        for (; u < ut; u += LPR) {
-            if (u + LPR < ut) fetch(u + LPR, wn, scn, bin);
-            if constexpr (BITS == 0) {
+        // x loads for this thread's first staging task, then the first D
+        // units of weights, then the staging arithmetic and LDS writes.
+        using St = Stager<BITS, MT>;
+        St st = [&] {
+            if constexpr (BITS == 0) return St{a, kt, kw / 8, xp};
+            else return St{a, kt, kw / 64, xp, xc};
+        }();
+        // Dense tasks are 16-byte copies: XB of them are loaded at once.
+        constexpr int XB = (BITS == 0) ? 8 : 1;
+        const int ntask = st.ntasks();
+        const int nthr = blockDim.x;
+        typename St::Regs xr[XB];
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const uint4 xv = xp[m * ut + u];
+        for (int i = 0; i < XB; ++i)
+            if ((int)threadIdx.x + i * nthr < ntask) xr[i] = st.load(threadIdx.x + i * nthr);
+        static_for<0, D>([&](auto Dd) {
+            constexpr int d = decltype(Dd)::value;
+            if (d < upl) fetch(d, li + d * LPR);
+        });
+        if (kt > 0) __syncthreads();       // previous tile's x fully consumed
+        for (int t0 = threadIdx.x; t0 < ntask; t0 += XB * nthr) {
+            if (t0 != (int)threadIdx.x) {
 #pragma unroll
-                    for (int s = 0; s < S; ++s)
-#pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            float t = acc[s][r][m];
-                            t = dot2(wc[s][r][0], xv.x, t);
-                            t = dot2(wc[s][r][1], xv.y, t);
-                            t = dot2(wc[s][r][2], xv.z, t);
-                            t = dot2(wc[s][r][3], xv.w, t);
-                            acc[s][r][m] = t;
-                        }
-                }
-            } else {
-                using P = PairPlan<BITS>;
-                float d[S][R][MT];
-#pragma unroll
-                for (int s = 0; s < S; ++s)
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-#pragma unroll
-                        for (int m = 0; m < MT; ++m) d[s][r][m] = 0.0f;
-                static_for<0, NCH>([&](auto C) {
-                    constexpr int c = decltype(C)::value;
-                    uint32_t p[S][R][4];
-#pragma unroll
-                    for (int s = 0; s < S; ++s)
-#pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            p[s][r][0] = P::template pair<4 * c + 0>(wc[s][r]);
-                            p[s][r][1] = P::template pair<4 * c + 1>(wc[s][r]);
-                            p[s][r][2] = P::template pair<4 * c + 2>(wc[s][r]);
-                            p[s][r][3] = P::template pair<4 * c + 3>(wc[s][r]);
-                        }
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        const uint4 xv = xp[(m * NCH + c) * ut + u];
-#pragma unroll
-                        for (int s = 0; s < S; ++s)
-#pragma unroll
-                            for (int r = 0; r < R; ++r) {
-                                float t = d[s][r][m];
-                                t = dot2(p[s][r][0], xv.x, t);
-                                t = dot2(p[s][r][1], xv.y, t);
-                                t = dot2(p[s][r][2], xv.z, t);
-                                t = dot2(p[s][r][3], xv.w, t);
-                                d[s][r][m] = t;
-                            }
-                    }
-                });
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const float2 xcv = xc[m * ut + u];
-#pragma unroll
-                    for (int s = 0; s < S; ++s)
-#pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            acc[s][r][m] = fmaf(sc[r], d[s][r][m] - xcv.y, fmaf(bi[r], xcv.x, acc[s][r][m]));
-                }
+                for (int i = 0; i < XB; ++i)
+                    if (t0 + i * nthr < ntask) xr[i] = st.load(t0 + i * nthr);
             }
 #pragma unroll
-            for (int s = 0; s < S; ++s)
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int i = 0; i < NW; ++i) wc[s][r][i] = wn[s][r][i];
-#pragma unroll
-            for (int r = 0; r < R; ++r) { sc[r] = scn[r]; bi[r] = bin[r]; }
+            for (int i = 0; i < XB; ++i)
+                if (t0 + i * nthr < ntask) st.store(t0 + i * nthr, xr[i]);
+        }
+        __syncthreads();
+
+        for (int base = 0; base < upl; base += D) {
+            static_for<0, D>([&](auto Dd) {
+                constexpr int d = decltype(Dd)::value;
+                const int j = base + d;
+                if (j < upl) {
+                    const int u = li + j * LPR;
+                    unit_mac<BITS, MT, S, R>(wb[d], sb[d], bb[d], xp, xc, ut, u, acc);
+                    if (j + D < upl) fetch(d, u + D * LPR);
+                }
+                code_fence();
+            });
         }
     }
 
@@ -299,7 +405,7 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[s][r][m] = segment_sum(acc[s][r][m], L);
+            for (int m = 0; m < MT; ++m) acc[s][r][m] = segment_sum64(acc[s][r][m], L);
 
 #pragma unroll
     for (int r = 0; r < R; ++r) {

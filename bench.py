@@ -169,19 +169,28 @@ def other_calls():
 
 # ------------------------------------------------------------------ timing
 
-def time_call(call, n):
-    """Average device time (us) of n back-to-back calls, HIP events on the launch stream."""
+def time_call(call, n, reps=3):
+    """Average device time (us) per call.  At least n calls, and at least one
+    call per weight copy (>= 1 GiB of distinct weights), are captured into a HIP
+    graph; the graph is replayed `reps` times between HIP events on the launch
+    stream, so host launch overhead is excluded and no weight is cache-hot."""
     import torch
+    n = max(n, call.w.R)
+    call()
+    call()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            call()
+    g.replay()
     s = torch.cuda.current_stream()
-    call()
-    call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
-    for _ in range(n):
-        call()
+    for _ in range(reps):
+        g.replay()
     e1.record(s)
     e1.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / n
+    return e0.elapsed_time(e1) * 1e3 / (n * reps)
 
 
 def kernel_sources_hash():
