@@ -18,24 +18,25 @@ struct ProjArgs {
     void* y;                 // bf16 or f32 [M][N]
     int M, N, K;
     int KT;                  // K elements staged in LDS per tile
-    int lpr_log2;            // VALU path: log2 of lanes that share one weight row
+    int lpr_log2;            // VALU/stream paths: log2 of lanes that share one weight row
     int ksplit_log2;         // MFMA path: log2 of wavefronts splitting K per row group
     int out_f32;             // 1: store fp32, 0: store bf16 (RNE)
     int64_t tpw;             // stream path: row tiles per super-tile
     int64_t tmax;            // stream path: most row tiles any wavefront finishes
 };
 
-enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2 };
+enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3 };
 
 // Launch geometry chosen for a call.
 struct LaunchCfg {
-    int path;       // PATH_VALU or PATH_MFMA
+    int path;       // PATH_*
     int MT;         // padded M (1, 2, 4, 8, 16, 32)
     int R;          // VALU: rows per lane; MFMA: 16-row tiles per row group (1 or 2)
     int lpr_log2;   // VALU: lanes per weight row = 2^lpr_log2 (<= 64)
     int ksplit_log2;  // MFMA: wavefronts splitting K per row group = 2^ksplit_log2
     int KT;         // K-tile in elements
-    int xreg;       // stream: x held in registers (affine, one group per lane)
+    int xreg;       // stream/piece: x operands held in registers
+    int pieces_per_lane;  // piece: 16-byte pieces per lane per row (1, 2, 3, 4, 8)
     int64_t tpw;    // stream: row tiles per wavefront
     int nwaves;     // waves per workgroup
     int blocks;     // workgroups
@@ -50,6 +51,11 @@ hipError_t launch_bits(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 // Per-width persistent streaming launchers (also in proj_b*.hip).
 template <int BITS, bool SWIGLU>
 hipError_t launch_stream(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+// Per-width persistent 16-byte-piece streaming launchers (piece_b*.hip):
+// dense, SwiGLU and affine b = 2, 4, 8.
+template <int BITS, bool SWIGLU>
+hipError_t launch_piece(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // Dense / SwiGLU matrix-core launcher (mfma_dense.hip).
 template <bool SWIGLU>

@@ -1,6 +1,9 @@
-// Launch-geometry choice and dispatch: VALU kernels (proj_b*.hip) for M <= 8
-// and for affine weights, matrix-core kernels (mfma_dense.hip) for dense and
-// SwiGLU calls with M = 9..32; plus the code-unpack kernel.
+// Launch-geometry choice and dispatch: for M <= 8 the 16-byte-piece streaming
+// kernels (piece_b*.hip: dense, SwiGLU, affine b = 2, 4, 8), else the group
+// streaming or tiled VALU kernels (proj_b*.hip); matrix-core kernels
+// (mfma_dense.hip) for dense and SwiGLU calls with M = 9..32, tiled VALU
+// kernels for affine M = 9..32; plus the code-unpack kernel.
+#include "piece_kernel.h"
 #include "stream_kernel.h"
 
 namespace aqg {
@@ -131,12 +134,62 @@ bool choose_stream(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
     return true;
 }
 
+int floor_log2(int v) { int l = 0; while ((2 << l) <= v) ++l; return l; }
+
+// 16-byte-piece streaming geometry (M <= 8; dense, SwiGLU, b = 2, 4, 8).
+// Lanes per row 2^L: the largest power of two <= the row's pieces, at most
+// 64 (one instruction reads 2^L * 16 contiguous bytes of each row); pieces
+// per lane J = ceil(pieces / 2^L), rounded up to 8 when it is 5..7.  x stays
+// in registers when its operands need at most 128 registers per lane.  The
+// path is feasible or not for all M <= 8 of a shape alike (checked at M = 8),
+// so every M <= 8 computes each output the same way.
+bool choose_piece(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
+{
+    c = LaunchCfg{};
+    if (!(bits == 0 || bits == 2 || bits == 4 || bits == 8)) return false;
+    if (swiglu && bits != 0) return false;
+    c.path = PATH_PIECE;
+    c.MT = 1;
+    while (c.MT < M) c.MT <<= 1;
+    if (c.MT > 8) return false;
+    const int KPP = bits ? 128 / bits : 8;
+    if (K % KPP != 0) return false;
+    const int PR = K / KPP;
+    int L = floor_log2(PR);
+    if (L > 6) L = 6;
+    int J = (PR + (1 << L) - 1) >> L;
+    if (J > 4 && J <= 8) J = 8;
+    if (J > 8) return false;
+    const int NPP = bits == 0 ? 4 : (bits == 2 ? 32 : 16);
+    auto xreg_at = [&](int mt) { return NPP * J * mt <= detail::kPieceXregBudget; };
+    // LDS at M = 8: staged x (unless in registers) plus the output staging
+    // with the fewest wavefronts a launch can get (one 4-wave workgroup per CU)
+    const int G = 64 >> L;
+    const int64_t T = ((int64_t)N + G - 1) / G;
+    const int64_t row_bytes = bits ? (int64_t)K * bits / 8 : (int64_t)K * 2;
+    int64_t ct = 4096 / (G * row_bytes);
+    if (ct < 1) ct = 1;
+    const int64_t st = (T + ct - 1) / ct;
+    const int64_t tmax = ((st + 1023) / 1024) * ct;
+    const size_t x8 = xreg_at(8) ? 0 : (size_t)8 * PR * (4 * NPP + (bits ? 8 : 0));
+    if (x8 + (size_t)4 * tmax * G * 8 * 4 > detail::kPieceLdsMax) return false;
+    c.lpr_log2 = L;
+    c.pieces_per_lane = J;
+    c.xreg = xreg_at(c.MT) ? 1 : 0;
+    c.lds = c.xreg ? 0 : (size_t)c.MT * PR * (4 * NPP + (bits ? 8 : 0));
+    c.KT = K;
+    c.nwaves = 4;
+    c.R = 1;
+    return true;
+}
+
 }  // namespace
 
 LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 {
     if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
     LaunchCfg c;
+    if (choose_piece(bits, swiglu, M, N, K, c)) return c;
     if (choose_stream(bits, swiglu, M, N, K, c)) return c;
     return choose_valu(bits, swiglu, M, N, K);
 }
@@ -146,6 +199,16 @@ hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg
     if (c.path == PATH_MFMA) {
         if (bits != 0) return hipErrorInvalidValue;
         return swiglu ? launch_mfma<true>(a, c, s) : launch_mfma<false>(a, c, s);
+    }
+    if (c.path == PATH_PIECE) {
+        if (swiglu) return bits == 0 ? launch_piece<0, true>(a, c, s) : hipErrorInvalidValue;
+        switch (bits) {
+            case 0: return launch_piece<0, false>(a, c, s);
+            case 2: return launch_piece<2, false>(a, c, s);
+            case 4: return launch_piece<4, false>(a, c, s);
+            case 8: return launch_piece<8, false>(a, c, s);
+            default: return hipErrorInvalidValue;
+        }
     }
     if (c.path == PATH_STREAM) {
         if (swiglu) return bits == 0 ? launch_stream<0, true>(a, c, s) : hipErrorInvalidValue;

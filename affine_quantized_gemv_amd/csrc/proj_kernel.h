@@ -88,17 +88,17 @@ __device__ __forceinline__ void load_unit(const uint32_t* __restrict__ p, uint32
 
 // ---------------------------------------------------------------- staging
 
-// Pre-scaled pair operands and group constants of one 64-k group of x, in the
-// width's plan order: xq[i] = (x[LO_K] * 2^LO_E) | (x[HI_K] * 2^HI_E) << 16,
-// X = sum of the group's x (each code once: its significance-0 subcode),
+// Pre-scaled pair operands and constants of the x values that one plan covers
+// (a 64-k group for PairPlan, a 16-byte piece's 128/b k for PiecePlan), in the
+// plan's order: xq[i] = (x[LO_K] * 2^LO_E) | (x[HI_K] * 2^HI_E) << 16,
+// X = sum of the covered x (each code once: its significance-0 subcode),
 // T = 128 * sum of the pre-scaled halves.  Sums run in pair order, low half
 // first; every caller uses this one routine, so the constants are identical
 // wherever x is kept.
-template <int BITS>
-__device__ __forceinline__ void group_x_operands(const uint32_t (&xw)[32], uint32_t (&xq)[PairPlan<BITS>::NP],
-                                                 float& X, float& T)
+template <class P, int NXW>
+__device__ __forceinline__ void plan_x_operands(const uint32_t (&xw)[NXW], uint32_t (&xq)[P::NP],
+                                                float& X, float& T)
 {
-    using P = PairPlan<BITS>;
     float xs = 0.0f, ts = 0.0f;
     static_for<0, P::NP>([&](auto I) {
         constexpr int i = decltype(I)::value;
@@ -114,6 +114,13 @@ __device__ __forceinline__ void group_x_operands(const uint32_t (&xw)[32], uint3
     });
     X = xs;
     T = 128.0f * ts;
+}
+
+template <int BITS>
+__device__ __forceinline__ void group_x_operands(const uint32_t (&xw)[32], uint32_t (&xq)[PairPlan<BITS>::NP],
+                                                 float& X, float& T)
+{
+    plan_x_operands<PairPlan<BITS>, 32>(xw, xq, X, T);
 }
 
 // A staging task is split into load (global -> registers) and store (compute

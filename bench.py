@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     p.add_argument("--copy-probe", type=float, default=0.0,
                    help="only run a device copy of this many MiB (counter calibration) and exit")
+    p.add_argument("--summarize-profile", metavar="DB", default=None,
+                   help="print a markdown summary of a rocprofv3 database (rocpd) taken with "
+                        "--kernel-trace --marker-trace --kernel-rename of this script, then exit")
     return p.parse_args()
 
 
@@ -185,12 +188,55 @@ def time_call(call, n, reps=3):
     g.replay()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    MARKERS.push(label_of(call))
     e0.record(s)
     for _ in range(reps):
         g.replay()
     e1.record(s)
     e1.synchronize()
+    MARKERS.pop()
     return e0.elapsed_time(e1) * 1e3 / (n * reps)
+
+
+class Markers:
+    """roctx ranges around each timed region, so that a profile taken with
+    `rocprofv3 --kernel-trace --marker-trace --kernel-rename --stats` lists every
+    call's dispatches under that call's label.  A no-op when the roctx library of
+    the ROCm profiler SDK is not present."""
+
+    def __init__(self):
+        import ctypes
+        self.lib = None
+        for name in ("librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so"):
+            for d in ("", "/opt/rocm/lib/"):
+                try:
+                    self.lib = ctypes.CDLL(d + name)
+                    break
+                except OSError:
+                    continue
+            if self.lib is not None:
+                break
+        if self.lib is not None:
+            self.lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+            self.lib.roctxRangePushA.restype = ctypes.c_int
+            self.lib.roctxRangePop.restype = ctypes.c_int
+
+    def push(self, label):
+        if self.lib is not None:
+            self.lib.roctxRangePushA(label.encode())
+
+    def pop(self):
+        if self.lib is not None:
+            self.lib.roctxRangePop()
+
+
+MARKERS = None
+
+
+def label_of(call):
+    b = "q%d " % call.bits if call.bits else ""
+    return "%s%s %s M=%d %dx%d" % (b, call.kind, call.name, call.M, call.N, call.K)
 
 
 def kernel_sources_hash():
@@ -254,10 +300,59 @@ def cpu_baseline(steps_bytes):
             "ms_per_step": round(el * 1e3 / nsteps, 1)}
 
 
+def label_bytes(label):
+    """Algorithmic bytes of the call a region label names (see label_of)."""
+    parts = label.split()
+    bits = 0
+    if parts[0].startswith("q") and parts[0][1:].isdigit():
+        bits = int(parts[0][1:])
+        parts = parts[1:]
+    kind = parts[0]
+    M = int(parts[2].split("=")[1])
+    N, K = (int(v) for v in parts[3].split("x"))
+    if kind == "dense":
+        return 2 * N * K + 2 * M * K + 2 * M * N
+    if kind == "swiglu":
+        return 4 * N * K + 2 * M * K + 2 * M * N
+    return N * K * bits // 8 + 4 * N * (K // 64) + 2 * M * K + 2 * M * N
+
+
+def summarize_profile(db):
+    """Per-call kernel durations from a rocprofv3 database of a run of this
+    script: dispatches inside each call's timing region are grouped under the
+    call's label (by --kernel-rename), with the kernel symbol they ran."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = list(c.execute(
+        "select region, name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+        "from kernels group by region, name order by sum(duration) desc"))
+    out = ["| region (call) | kernel | dispatches | avg us | min us | max us | GB/s at avg | % of 8 TB/s |",
+           "|---|---|---|---|---|---|---|---|"]
+    for region, name, n, avg, mn, mx, _ in rows:
+        if not region or region.startswith("timed steps"):
+            continue
+        b = label_bytes(region)
+        gbps = b / avg
+        out.append("| %s | `%s` | %d | %.2f | %.2f | %.2f | %.0f | %.1f |" % (
+            region, name, n, avg / 1e3, mn / 1e3, mx / 1e3, gbps, 100 * gbps / HBM_PEAK_GBPS))
+    out.append("")
+    out.append("Whole timed steps (graph replay and eager), by kernel symbol:")
+    out.append("")
+    out.append("| region | kernel | dispatches | avg us | total ms |")
+    out.append("|---|---|---|---|---|")
+    for region, name, n, avg, mn, mx, tot in rows:
+        if region and region.startswith("timed steps"):
+            out.append("| %s | `%s` | %d | %.2f | %.3f |" % (region, name, n, avg / 1e3, tot / 1e6))
+    print("\n".join(out))
+    return 0
+
+
 # -------------------------------------------------------------------- main
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        return summarize_profile(args.summarize_profile)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the projections run on a single MI355X and this "
               "build has no multi-GPU path (requested --gpus %d)." % args.gpus, file=sys.stderr)
@@ -266,6 +361,8 @@ def main():
     import affine_quantized_gemv_amd as aqg
     aqg.load()
     torch.cuda.set_device(0)
+    global MARKERS
+    MARKERS = Markers()
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return 0
@@ -304,11 +401,13 @@ def main():
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    MARKERS.push("timed steps (graph replay)")
     e0.record(s)
     for i in range(args.steps):
         graphs[i % NG].replay()
     e1.record(s)
     torch.cuda.synchronize()
+    MARKERS.pop()
     wall = time.perf_counter() - t0
     ms_graph = e0.elapsed_time(e1) / args.steps
 
@@ -316,11 +415,13 @@ def main():
     for _ in range(max(1, args.warmup // 2)):
         step()
     torch.cuda.synchronize()
+    MARKERS.push("timed steps (eager)")
     e0.record(s)
     for _ in range(args.steps):
         step()
     e1.record(s)
     torch.cuda.synchronize()
+    MARKERS.pop()
     ms_eager = e0.elapsed_time(e1) / args.steps
 
     # dominant kernel: the call with the largest device time per step

@@ -160,6 +160,23 @@ def test_dense_one_hot_exact():
     assert np.array_equal(y, oracle.bf16_to_f64(W[:, cols]).T)
 
 
+@pytest.mark.parametrize("K", [1536, 4096, 1000])
+def test_dense_one_hot_every_piece_position_m8(K):
+    """M = 8 (streaming path) one-hot rows over all 8 positions of a 16-byte
+    piece, spread over the row (K = 1000: the row's last lane slot is ragged):
+    y = W[n, k] exactly."""
+    N = 333
+    W = synth.dense_weight(70, "onehot8/%d" % K, N, K)
+    npiece = K // 8
+    cols = np.array([((r * 37 + 11) % npiece) * 8 + r for r in range(8)] + [K - 1 - r for r in range(8)])
+    for c0 in range(0, len(cols), 8):
+        c = cols[c0:c0 + 8]
+        x = np.zeros((8, K), np.uint16)
+        x[np.arange(8), c] = 0x3F80
+        y = run_guarded(gemv_dense_gpu(bf16_dev(x), bf16_dev(W), 8), 8, N)
+        assert np.array_equal(y, oracle.bf16_to_f64(W[:, c]).T), "cols %s" % c
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 8), (3, 5, 64), (5, 77, 136), (17, 1000, 520), (31, 129, 2048),
                                    (2, 257, 8192), (32, 64, 4096)])
 def test_dense_ragged_shapes(M, N, K):
@@ -337,6 +354,29 @@ def test_affine_one_hot_reads_codes_exactly(bits):
         assert np.array_equal(y, codes[:, cols[:M]].T.astype(np.float64))
 
 
+@pytest.mark.parametrize("K", [1024, 3584])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_affine_one_hot_every_group_position_m8(bits, K):
+    """M = 8 (streaming path) one-hot rows over all 64 positions of a group,
+    each in a different group of the row (K = 3584 at b = 4: the row's last
+    lane slot is ragged): y[m, n] = q[n, col_m] exactly.  Pins the in-GEMV
+    unpack of the streaming kernels for every code position."""
+    N = 211
+    words = synth.random_words((N, K * bits // 32), 78, "oh8/%d/%d" % (bits, K))
+    codes = oracle.unpack(words, bits, K)
+    G = K // 64
+    cols = np.array([((r * 5 + 3) % G) * 64 + r for r in range(64)])
+    ones = np.full((N, G), 0x3F80, np.uint16)
+    zeros = np.zeros((N, G), np.uint16)
+    wq, sd, bd = u32_dev(words), bf16_dev(ones), bf16_dev(zeros)
+    for c0 in range(0, 64, 8):
+        c = cols[c0:c0 + 8]
+        x = np.zeros((8, K), np.uint16)
+        x[np.arange(8), c] = 0x3F80
+        y = run_guarded(gemv_affine_gpu(bf16_dev(x), wq, sd, bd, bits, 8), 8, N)
+        assert np.array_equal(y, codes[:, c].T.astype(np.float64)), "cols %s" % c
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_affine_small_integers_exact(bits):
     M, N, K = 3, 5, 192
@@ -387,10 +427,10 @@ def test_affine_ragged_shapes(M, N, K, bits):
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_affine_rows_independent_of_m(bits):
-    name, N, K = synth.MIXED_SHAPES[0]
-    x, aw, xd, wq, sd, bd = affine_case(synth.CFG_MIXED_WIDTH, name, bits, N, K)
     """M <= 8 (streaming path, x in registers or LDS) matches one-row calls bit
     for bit; M = 9..32 (tiled path) matches the 32-row call bit for bit."""
+    name, N, K = synth.MIXED_SHAPES[0]
+    x, aw, xd, wq, sd, bd = affine_case(synth.CFG_MIXED_WIDTH, name, bits, N, K)
     y1 = torch.cat([aqg.gemv_affine(xd[m:m + 1], wq, sd, bd, bits, out_dtype=torch.float32)
                     for m in range(8)]).cpu().numpy()
     for M in (2, 3, 4, 7, 8):
