@@ -134,15 +134,16 @@ bool choose_stream(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
     return true;
 }
 
-int floor_log2(int v) { int l = 0; while ((2 << l) <= v) ++l; return l; }
-
 // 16-byte-piece streaming geometry (M <= 8; dense, SwiGLU, b = 2, 4, 8).
-// Lanes per row 2^L: the largest power of two <= the row's pieces, at most
-// 64 (one instruction reads 2^L * 16 contiguous bytes of each row); pieces
-// per lane J = ceil(pieces / 2^L), rounded up to 8 when it is 5..7.  x stays
-// in registers when its operands need at most 128 registers per lane.  The
-// path is feasible or not for all M <= 8 of a shape alike (checked at M = 8),
-// so every M <= 8 computes each output the same way.
+// Rows of >= 64 pieces: 64 lanes per row (one instruction reads 1 KB of a
+// row), J = ceil(pieces / 64) pieces per lane, rounded up to 8 when 5..7.
+// Shorter rows: 16 lanes per row and J = 2..4 (measured faster than 32 lanes
+// with J = 1 on the 4-bit LM head), or, for rows of <= 16 pieces, the
+// smallest 2^L >= pieces with J = 1.  Lane slots past the row's end compute
+// with zero x.  x stays in registers when its operands need at most 128
+// (dense) or 64 (affine) registers per lane.  The path is feasible or not for
+// all M <= 8 of a shape alike (checked at M = 8), so every M <= 8 computes
+// each output the same way.
 bool choose_piece(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
 {
     c = LaunchCfg{};
@@ -155,28 +156,40 @@ bool choose_piece(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
     const int KPP = bits ? 128 / bits : 8;
     if (K % KPP != 0) return false;
     const int PR = K / KPP;
-    int L = floor_log2(PR);
-    if (L > 6) L = 6;
-    int J = (PR + (1 << L) - 1) >> L;
-    if (J > 4 && J <= 8) J = 8;
-    if (J > 8) return false;
+    int L, J;
+    if (PR >= 64) {
+        L = 6;
+        J = (PR + 63) / 64;
+        if (J > 4 && J <= 8) J = 8;
+        if (J > 8) return false;
+    } else if (PR > 16) {
+        L = 4;
+        J = (PR + 15) / 16;
+    } else {
+        L = PR > 8 ? 4 : (PR > 4 ? 3 : 2);
+        J = 1;
+    }
+    // a tile's scales and biases come in with one bf16 per lane each
+    if (bits != 0 && (int64_t)(64 >> L) * (K / 64) > 64) return false;
     const int NPP = bits == 0 ? 4 : (bits == 2 ? 32 : 16);
-    auto xreg_at = [&](int mt) { return NPP * J * mt <= detail::kPieceXregBudget; };
+    const int budget = bits == 0 ? detail::piece_xreg_budget<0>() : detail::piece_xreg_budget<4>();
+    auto xreg_at = [&](int mt) { return NPP * J * mt <= budget; };
     // LDS at M = 8: staged x (unless in registers) plus the output staging
     // with the fewest wavefronts a launch can get (one 4-wave workgroup per CU)
     const int G = 64 >> L;
+    const int PRP = J << L;
     const int64_t T = ((int64_t)N + G - 1) / G;
-    const int64_t row_bytes = bits ? (int64_t)K * bits / 8 : (int64_t)K * 2;
-    int64_t ct = 4096 / (G * row_bytes);
+    const int64_t row_bytes = (int64_t)PR * 16;
+    int64_t ct = 8192 / (G * row_bytes);
     if (ct < 1) ct = 1;
     const int64_t st = (T + ct - 1) / ct;
     const int64_t tmax = ((st + 1023) / 1024) * ct;
-    const size_t x8 = xreg_at(8) ? 0 : (size_t)8 * PR * (4 * NPP + (bits ? 8 : 0));
+    const size_t x8 = xreg_at(8) ? 0 : (size_t)8 * PRP * (4 * NPP + (bits ? 8 : 0));
     if (x8 + (size_t)4 * tmax * G * 8 * 4 > detail::kPieceLdsMax) return false;
     c.lpr_log2 = L;
     c.pieces_per_lane = J;
     c.xreg = xreg_at(c.MT) ? 1 : 0;
-    c.lds = c.xreg ? 0 : (size_t)c.MT * PR * (4 * NPP + (bits ? 8 : 0));
+    c.lds = c.xreg ? 0 : (size_t)c.MT * PRP * (4 * NPP + (bits ? 8 : 0));
     c.KT = K;
     c.nwaves = 4;
     c.R = 1;

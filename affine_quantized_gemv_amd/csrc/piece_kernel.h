@@ -19,12 +19,25 @@
 // Each lane's pieces sit at fixed k offsets of every row, so their x operands
 // (all M rows) are computed once and kept in registers when they fit, else
 // staged in LDS in the same form by the same routine; both give bit-identical
-// results.  The rest follows the streaming kernel: super-tiles of consecutive
-// row tiles dealt round-robin to all resident wavefronts, a ring of loads
-// that stays in flight across row boundaries with unconditional (clamped)
-// loads in the steady state, outputs staged in LDS and written at the end.
-// J = pieces per lane per row is a compile-time constant, so every ring slot
-// knows its piece (and its x registers) statically.
+// results.  A lane slot past the row's last piece (rows whose piece count is
+// not a multiple of 2^L) gets zero x operands, which makes its contribution
+// exactly zero without any masking.
+//
+// Weights, scales and biases are read with buffer loads: the row tile is
+// wave-uniform, so its base address and byte range live in a scalar buffer
+// descriptor, and each lane's offset into the tile is a loop-invariant 32-bit
+// register.  Rows past N fall outside the descriptor's range and read as zero
+// without touching memory.  A tile's scales (and biases) are G*K/64 <= 64
+// adjacent bf16: lane g loads the tile's group g (one 128-byte instruction
+// per tile, range-checked to the exact byte), and each piece takes its
+// group's value from that lane with ds_bpermute -- two narrow loads per piece
+// measured 15% slower.  The rest follows the streaming kernel:
+// super-tiles of consecutive row tiles dealt round-robin to the resident
+// wavefronts, a ring of loads that stays in flight across row boundaries
+// (steady-state loads are unconditional, nothing is stored to global memory
+// in the loop, so each wait is for one slot's loads), outputs staged in LDS
+// and written at the end.  L and J (pieces per lane per row) are compile-time
+// constants, so the loop body has no branches besides the loop itself.
 #pragma once
 #include <atomic>
 
@@ -35,7 +48,14 @@ namespace detail {
 
 constexpr int kPieceThreads = 256;
 constexpr size_t kPieceLdsMax = 160 * 1024;
-constexpr int kPieceXregBudget = 128;   // x-operand registers per lane
+// x-operand registers per lane above which x is staged in LDS instead
+// (affine: with the unpack's registers, more measured slower than LDS)
+template <int BITS> constexpr int piece_xreg_budget() { return BITS == 0 ? 128 : 64; }
+// Resident wavefronts per CU: more were measured no faster (dense: 8 with
+// ~3 KB in flight each; affine, with more arithmetic per byte: 24).
+template <int BITS> constexpr int piece_max_waves_per_cu() { return BITS == 0 ? 8 : 24; }
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kLoadNT = 2;                // non-temporal: weights are read once
 
 template <int BITS> struct PieceGeo {
     using Plan = PiecePlan<BITS>;
@@ -50,16 +70,19 @@ template <> struct PieceGeo<0> {
 };
 
 template <int BITS, int MT, int J>
-constexpr bool piece_xreg_ok() { return PieceGeo<BITS>::NPP * J * MT <= kPieceXregBudget; }
+constexpr bool piece_xreg_ok() { return PieceGeo<BITS>::NPP * J * MT <= piece_xreg_budget<BITS>(); }
 
-// Row tiles in flight per wavefront: about 4 pieces per lane, at least 2 rows
-// when a row has fewer than 4 pieces per lane.
-template <int J> struct PieceDepth {
-    static constexpr int RD = J >= 4 ? 1 : (J >= 2 ? 2 : 4);
+// Row tiles in flight per wavefront (measured on the LM-head shapes): 2 when
+// a lane has one piece per row, and for affine codes with two; dense with
+// 2..3 pieces: 1 for M <= 4, 2 for M = 8 (fewer wavefronts fit, each needs
+// more in flight); 1 from 4 pieces.
+template <int BITS, int J, int MT> struct PieceDepth {
+    static constexpr int RD = J == 1 ? 2 : (J >= 4 ? 1 : ((MT >= 8 || (BITS != 0 && J == 2)) ? 2 : 1));
 };
 
 // x operands of one piece for one row m: dense, the 8 bf16 as they are;
-// affine, the piece plan's pre-scaled pairs plus X and T.
+// affine, the piece plan's pre-scaled pairs plus X and T.  have = false gives
+// all zeros.
 template <int BITS>
 __device__ __forceinline__ void piece_x(const uint16_t* __restrict__ xrow, bool have,
                                         uint32_t (&xq)[PieceGeo<BITS>::NPP], float& X, float& T)
@@ -81,7 +104,14 @@ __device__ __forceinline__ void piece_x(const uint16_t* __restrict__ xrow, bool 
     }
 }
 
-template <int BITS, int MT, bool SWIGLU, bool XREG, int J, int RD = PieceDepth<J>::RD>
+// Buffer descriptor over `bytes` bytes from p (clamped to the 32-bit range).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int64_t bytes)
+{
+    const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kBufferFlags);
+}
+
+template <int BITS, int MT, bool SWIGLU, bool XREG, int L, int J, int RD = PieceDepth<BITS, J, MT>::RD>
 __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 {
     extern __shared__ uint4 lds_p4[];
@@ -91,102 +121,126 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
     constexpr int NPP = PG::NPP;
     constexpr int NCHP = NPP / 4;                 // uint4 chunks of x operands per (m, piece)
     constexpr int D = RD * J;                     // ring slots (pieces in flight per lane)
+    constexpr int P = 1 << L;                     // lanes per row
+    constexpr int G = 64 >> L;                    // rows per tile
+    constexpr int PRP = J * P;                    // piece slots per row (>= pieces per row)
+    constexpr int PER_TILE = G * MT;              // staged outputs per tile
     static_assert(!SWIGLU || BITS == 0, "the fused SwiGLU takes dense weights");
+    static_assert(L >= 2 && L <= 6, "segment of 4..64 lanes");
 
-    const int L = a.lpr_log2;
-    const int P = 1 << L;
-    const int G = 64 >> L;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slot = lane >> L;
     const int li = lane & (P - 1);
     const int PR = a.K / KPP;                                 // pieces per row
-    const bool ragged = J * P != PR;                          // last piece slot partly empty
+    const int64_t row_bytes = (int64_t)PR * 16;
+    const int gpr = a.K / 64;
     const int64_t T = ((int64_t)a.N + G - 1) / G;             // row tiles
     const int64_t CT = a.tpw;                                 // tiles per super-tile
     const int64_t ST = (T + CT - 1) / CT;
-    const int64_t W = (int64_t)gridDim.x * (blockDim.x >> 6);
-    const int64_t wg = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+    const int64_t W = (int64_t)gridDim.x * (kPieceThreads / 64);
+    const int64_t wg = (int64_t)blockIdx.x * (kPieceThreads / 64) + wave;
     int64_t my_tiles = 0;
     if (wg < ST) {
         const int64_t nst = (ST - 1 - wg) / W + 1;
         my_tiles = nst * CT;
         if ((ST - 1 - wg) % W == 0) my_tiles -= ST * CT - T;  // this wave owns the last, partial one
     }
-    const int64_t row_words = (int64_t)PR * 4;
-    const int gpr = a.K / 64;
 
-    // ---- x operands: registers or LDS (whole K, all MT rows)
-    uint4* xp = lds_p4;                                                   // [m][chunk][piece]
-    float2* xc = reinterpret_cast<float2*>(lds_p4 + (size_t)MT * NCHP * PR);  // [m][piece] (X, T)
+    // ---- x operands: registers or LDS (PRP piece slots per row, zero past PR).
+    // Filled after the first weight loads are issued (see the prologue), so
+    // their latencies overlap.
+    uint4* xp = lds_p4;                                                   // [m][chunk][piece slot]
+    float2* xc = reinterpret_cast<float2*>(lds_p4 + (size_t)MT * NCHP * PRP);  // [m][piece slot] (X, T)
     uint32_t xq[XREG ? J : 1][XREG ? MT : 1][NPP];
     float xX[XREG ? J : 1][XREG ? MT : 1], xT[XREG ? J : 1][XREG ? MT : 1];
-    if constexpr (XREG) {
+    auto load_x = [&]() __attribute__((always_inline)) {
+        if constexpr (XREG) {
 #pragma unroll
-        for (int j = 0; j < J; ++j)
+            for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int p = li + P * j;
+                for (int m = 0; m < MT; ++m) {
+                    const int p = li + P * j;
+                    const bool have = m < a.M && p < PR;
+                    piece_x<BITS>(a.x + (size_t)m * a.K + (size_t)(have ? p : 0) * KPP, have,
+                                  xq[j][m], xX[j][m], xT[j][m]);
+                }
+        } else {
+            // every wavefront of the workgroup stages, then all synchronize
+            for (int t = threadIdx.x; t < MT * PRP; t += kPieceThreads) {
+                const int m = t / PRP, p = t - m * PRP;
                 const bool have = m < a.M && p < PR;
-                piece_x<BITS>(a.x + (size_t)m * a.K + (size_t)(have ? p : 0) * KPP, have,
-                              xq[j][m], xX[j][m], xT[j][m]);
-            }
-    } else {
-        const int ntask = MT * PR;
-        for (int t = threadIdx.x; t < ntask; t += blockDim.x) {
-            const int m = t / PR, p = t - m * PR;
-            uint32_t q[NPP];
-            float X, Tc;
-            piece_x<BITS>(a.x + (size_t)m * a.K + (size_t)p * KPP, m < a.M, q, X, Tc);
+                uint32_t q[NPP];
+                float X, Tc;
+                piece_x<BITS>(a.x + (size_t)m * a.K + (size_t)(have ? p : 0) * KPP, have, q, X, Tc);
 #pragma unroll
-            for (int c = 0; c < NCHP; ++c)
-                xp[((size_t)m * NCHP + c) * PR + p] = make_uint4(q[4 * c], q[4 * c + 1], q[4 * c + 2], q[4 * c + 3]);
-            if constexpr (BITS != 0) xc[(size_t)m * PR + p] = make_float2(X, Tc);
+                for (int c = 0; c < NCHP; ++c)
+                    xp[(m * NCHP + c) * PRP + p] = make_uint4(q[4 * c], q[4 * c + 1], q[4 * c + 2], q[4 * c + 3]);
+                if constexpr (BITS != 0) xc[m * PRP + p] = make_float2(X, Tc);
+            }
+            __syncthreads();
         }
-        __syncthreads();
-    }
-    if (my_tiles == 0) return;
+    };
 
     // ---- output staging: G*MT fp32 per finished tile, wavefront-private
-    const int per_tile = G * MT;
     float* obuf = reinterpret_cast<float*>(
                       XREG ? lds_p4
-                           : lds_p4 + (size_t)MT * NCHP * PR + (BITS != 0 ? ((size_t)MT * PR + 1) / 2 : 0))
-                  + (size_t)wave * a.tmax * per_tile;
+                           : lds_p4 + (size_t)MT * NCHP * PRP + (BITS != 0 ? ((size_t)MT * PRP + 1) / 2 : 0))
+                  + (size_t)wave * a.tmax * PER_TILE;
 
-    // ---- ring of D = RD*J slots; slot d holds piece j = d % J of a row tile.
-    // Loads in the steady state are unconditional (rows and pieces clamped to
-    // valid addresses; clamped values are never used) and nothing is stored
-    // to global memory inside the loop, so every wait is for one slot's loads.
+    // ---- lane offsets within a tile (loop-invariant)
+    // gsrc[j]: byte address (for ds_bpermute) of the lane holding piece j's
+    // group (lane g holds the tile's group g); a lane slot past the row's end
+    // points at some group of the tile, its x operands are zero
+    uint32_t woff[J];
+    [[maybe_unused]] int gsrc[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int p = li + P * j;
+        woff[j] = (uint32_t)(slot * row_bytes + (int64_t)p * 16);
+        gsrc[j] = ((slot * gpr + p / PG::PPG) & 63) * 4;
+    }
+
+    // ---- ring of D = RD*J slots; slot d holds piece j = d % J of a row tile
     uint32_t wb[D][S][4];
-    [[maybe_unused]] float sb[D], bb[D];
-    int64_t f_tile = wg * CT;
-    int f_c = 0;
-    auto next_tile = [&](int64_t t) __attribute__((always_inline)) {
-        ++t;
-        if (++f_c == CT) { f_c = 0; t += (W - 1) * CT; }
-        return t;
+    [[maybe_unused]] uint32_t sw[RD], bw[RD];   // per ring row: the scale / bias of group `lane`
+    int64_t f_tile = wg * CT;   // tile being fetched (wave-uniform)
+    int f_c = 0;                // its index within the super-tile
+    __amdgpu_buffer_rsrc_t rw[S], rs, rb;
+    auto set_tile = [&]() __attribute__((always_inline)) {
+        const int64_t n0 = f_tile * G;
+        const int64_t rows = a.N - n0;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            rw[s] = tile_rsrc(static_cast<const char*>(s == 0 ? a.w0 : a.w1) + n0 * row_bytes, rows * row_bytes);
+        if constexpr (BITS != 0) {
+            rs = tile_rsrc(a.scales + n0 * gpr, rows * gpr * 2);
+            rb = tile_rsrc(a.biases + n0 * gpr, rows * gpr * 2);
+        }
     };
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     auto fetch = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
         constexpr int j = d % J;
-        int p = li + P * j;
-        if (p >= PR) p = PR - 1;
-        int64_t n = f_tile * G + slot;
-        if (n >= a.N) n = a.N - 1;
+        if constexpr (j == 0) {
+            set_tile();
+            // issued before the row's first piece, so waiting for that piece
+            // covers them; consume(d) of the row's first piece has already
+            // taken the previous values out (fetch(d) follows consume(d))
+            if constexpr (BITS != 0) {
+                sw[d / J] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)lane * 2, 0, kLoadNT);
+                bw[d / J] = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)lane * 2, 0, kLoadNT);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            const uint32_t* base = reinterpret_cast<const uint32_t*>(s == 0 ? a.w0 : a.w1);
-            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + n * row_words + (int64_t)p * 4));
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw[s], woff[j], 0, kLoadNT);
             wb[d][s][0] = v.x; wb[d][s][1] = v.y; wb[d][s][2] = v.z; wb[d][s][3] = v.w;
         }
-        if constexpr (BITS != 0) {
-            const int g = p / PG::PPG;
-            sb[d] = bf16_to_f32(a.scales[n * gpr + g]);
-            bb[d] = bf16_to_f32(a.biases[n * gpr + g]);
+        if constexpr (j == J - 1) {
+            ++f_tile;
+            if (++f_c == CT) { f_c = 0; f_tile += (W - 1) * CT; }
         }
-        if constexpr (j == J - 1) f_tile = next_tile(f_tile);
     };
 
     float acc[S][MT];
@@ -195,29 +249,15 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[s][m] = 0.0f;
     int ti = 0;                 // tiles finished by this wavefront
+    [[maybe_unused]] float rsc[J], rbi[J];   // scale and bias of each piece of the row in use
 
     auto consume = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
         constexpr int j = d % J;
+        const int p = li + P * j;
         // x in LDS is loop-invariant; the fence keeps its reads here instead
         // of letting them be hoisted out of the loop into registers
         if constexpr (!XREG) code_fence();
-        const int p0 = li + P * j;
-        const bool live = p0 < PR;
-        const int p = live ? p0 : PR - 1;
-        // An empty piece slot (the row's last, ragged slot) contributes
-        // exactly 0: zeroed weights (dense) or zeroed scale and bias (affine).
-        if (ragged) {
-            if constexpr (BITS == 0) {
-#pragma unroll
-                for (int s = 0; s < S; ++s)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) wb[d][s][i] = live ? wb[d][s][i] : 0u;
-            } else {
-                sb[d] = live ? sb[d] : 0.0f;
-                bb[d] = live ? bb[d] : 0.0f;
-            }
-        }
         if constexpr (BITS == 0) {
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
@@ -226,7 +266,7 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) xv[i] = xq[j][m][i];
                 } else {
-                    const uint4 v = xp[(size_t)m * PR + p];
+                    const uint4 v = xp[m * PRP + p];
                     xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
                 }
 #pragma unroll
@@ -253,7 +293,7 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                         x0 = xq[j][m][4 * c]; x1 = xq[j][m][4 * c + 1];
                         x2 = xq[j][m][4 * c + 2]; x3 = xq[j][m][4 * c + 3];
                     } else {
-                        const uint4 v = xp[((size_t)m * NCHP + c) * PR + p];
+                        const uint4 v = xp[(m * NCHP + c) * PRP + p];
                         x0 = v.x; x1 = v.y; x2 = v.z; x3 = v.w;
                     }
                     float v0 = dd[m], v1 = de[m];
@@ -268,6 +308,16 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                 for (int m = 0; m < MT; ++m) { pin(dd[m]); pin(de[m]); }
                 code_fence();
             });
+            if constexpr (j == 0) {
+                // the row's first piece takes every piece's scale and bias
+#pragma unroll
+                for (int jj = 0; jj < J; ++jj) {
+                    rsc[jj] = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(gsrc[jj], (int)sw[d / J]) << 16);
+                    rbi[jj] = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(gsrc[jj], (int)bw[d / J]) << 16);
+                }
+            }
+            const float sc = rsc[j];
+            const float bi = rbi[j];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 float X, Tc;
@@ -275,32 +325,48 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                     X = xX[j][m];
                     Tc = xT[j][m];
                 } else {
-                    const float2 v = xc[(size_t)m * PR + p];
+                    const float2 v = xc[m * PRP + p];
                     X = v.x;
                     Tc = v.y;
                 }
-                acc[0][m] = fmaf(sb[d], (dd[m] + de[m]) - Tc, fmaf(bb[d], X, acc[0][m]));
+                acc[0][m] = fmaf(sc, (dd[m] + de[m]) - Tc, fmaf(bi, X, acc[0][m]));
             }
         }
         if constexpr (j == J - 1) {
-            // end of a row tile: segment sums, epilogue, stage, reset
+            // end of a row tile: segment sums, epilogue, stage, reset.  Lane li
+            // of a segment stages outputs m = li mod MT (+ P, + 2P, ... when
+            // MT > P); lanes holding the same m write the same value.
+            float out[MT];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                float v = segment_sum64(acc[0][m], L);
+                float v = segment_sum64_ct<L>(acc[0][m]);
                 if constexpr (SWIGLU) {
-                    const float u = segment_sum64(acc[1][m], L);
+                    const float u = segment_sum64_ct<L>(acc[1][m]);
                     v = (v / (1.0f + __expf(-v))) * u;
                 }
+                out[m] = v;
 #pragma unroll
                 for (int s = 0; s < S; ++s) acc[s][m] = 0.0f;
-                if (li == (m & (P - 1))) obuf[(size_t)ti * per_tile + slot * MT + m] = v;
+            }
+            constexpr int NV = MT > P ? MT / P : 1;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int m0 = (li & (MT - 1) & (P - 1)) + v * P;
+                float val = out[0];
+#pragma unroll
+                for (int m = 1; m < MT; ++m) val = (m == m0) ? out[m] : val;
+                obuf[ti * PER_TILE + slot * MT + m0] = val;
             }
             ++ti;
         }
     };
 
-    // prologue: RD rows, unconditionally
+    // prologue: RD rows, unconditionally (tiles past the wavefront's share --
+    // all of them for a wavefront with no tiles -- read as zero or as valid
+    // rows; they are never consumed), then x
     static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
+    load_x();
+    if (my_tiles == 0) return;
     int64_t bt = 0;
     for (; bt + 2 * RD <= my_tiles; bt += RD) {          // steady state
         static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
@@ -320,14 +386,12 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 
     // write out the staged outputs: value v of the wavefront's list is tile
     // v / (G*MT), row slot (v / MT) % G, output row m = v % MT
-    const int lg_pt = __builtin_ctz(per_tile);
-    const int lg_mt = __builtin_ctz(MT);
-    for (int v = lane; v < ti * per_tile; v += 64) {
-        const int t2 = v >> lg_pt;
-        const int r = v & (per_tile - 1);
-        const int m = r & (MT - 1);
+    for (int v = lane; v < ti * PER_TILE; v += 64) {
+        const int t2 = v / PER_TILE;
+        const int r = v % PER_TILE;
+        const int m = r % MT;
         const int64_t tile = (wg + (int64_t)(t2 / CT) * W) * CT + t2 % CT;
-        const int64_t n = tile * G + (r >> lg_mt);
+        const int64_t n = tile * G + r / MT;
         if (m < a.M && n < a.N) {
             const float val = obuf[v];
             const size_t o = (size_t)m * a.N + n;
@@ -337,23 +401,24 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
     }
 }
 
-// LDS bytes of one workgroup of `nwaves` wavefronts: staged x (none when x is
-// in registers) plus the output staging for `tmax` tiles per wavefront.
+// LDS bytes of one workgroup: staged x (none when x is in registers) plus the
+// output staging for `tmax` tiles per wavefront.
 template <int BITS>
-size_t piece_lds_bytes(int MT, bool xreg, int L, int nwaves, int K, int64_t tmax)
+size_t piece_lds_bytes(int MT, bool xreg, int L, int J, int K, int64_t tmax)
 {
+    (void)K;
     const int G = 64 >> L;
-    const size_t out = (size_t)nwaves * tmax * G * MT * 4;
+    const size_t out = (size_t)(kPieceThreads / 64) * tmax * G * MT * 4;
     if (xreg) return out;
-    const int PR = K / PieceGeo<BITS>::KPP;
-    const size_t x16 = (size_t)MT * (PieceGeo<BITS>::NPP / 4) * PR + (BITS != 0 ? ((size_t)MT * PR + 1) / 2 : 0);
+    const size_t PRP = (size_t)J << L;
+    const size_t x16 = (size_t)MT * (PieceGeo<BITS>::NPP / 4) * PRP + (BITS != 0 ? ((size_t)MT * PRP + 1) / 2 : 0);
     return x16 * 16 + out;
 }
 
-template <int BITS, int MT, bool SW, bool XREG, int J>
-hipError_t launch_piece_one(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+template <int BITS, int MT, bool SW, bool XREG, int L, int J>
+hipError_t launch_piece_one(const ProjArgs& a, hipStream_t s)
 {
-    const void* fn = reinterpret_cast<const void*>(&piece_kernel<BITS, MT, SW, XREG, J>);
+    const void* fn = reinterpret_cast<const void*>(&piece_kernel<BITS, MT, SW, XREG, L, J>);
     {
         static std::atomic<int> raised{0};
         if (!raised.load(std::memory_order_acquire)) {
@@ -366,72 +431,81 @@ hipError_t launch_piece_one(const ProjArgs& a, const LaunchCfg& c, hipStream_t s
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const int L = c.lpr_log2;
-    const int64_t G = 64 >> L;
+    constexpr int64_t G = 64 >> L;
+    constexpr int NW = kPieceThreads / 64;
     const int64_t T = ((int64_t)a.N + G - 1) / G;
     const int64_t row_bytes = BITS == 0 ? (int64_t)a.K * 2 : (int64_t)a.K * BITS / 8;
-    int64_t ct = 4096 / (G * row_bytes);                      // ~4 KB super-tiles
+    // super-tiles of ~8 KB of consecutive rows
+    int64_t ct = 8192 / (G * row_bytes);
     if (ct < 1) ct = 1;
     const int64_t st = (T + ct - 1) / ct;
-    // Grid: every wavefront slot the device holds at once at this LDS size
-    // (the output staging depends on the grid: settle in a few rounds).
+    // Grid: the wavefront slots the device holds at once at this LDS size, at
+    // most piece_max_waves_per_cu per CU (the output staging depends on the
+    // grid: settle in a few rounds).
     int64_t waves = st, tmax = 0;
     size_t lds = 0;
     for (int round = 0; round < 3; ++round) {
         tmax = ((st + waves - 1) / waves) * ct;
-        lds = piece_lds_bytes<BITS>(MT, XREG, L, c.nwaves, a.K, tmax);
+        lds = piece_lds_bytes<BITS>(MT, XREG, L, J, a.K, tmax);
         if (lds > kPieceLdsMax) return hipErrorInvalidValue;
         int bpc = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, 64 * c.nwaves, lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, kPieceThreads, lds);
         if (e != hipSuccess) return e;
         if (bpc < 1) bpc = 1;
-        int64_t w = (int64_t)bpc * cus * c.nwaves;
+        if (bpc * NW > piece_max_waves_per_cu<BITS>()) bpc = piece_max_waves_per_cu<BITS>() / NW;
+        int64_t w = (int64_t)bpc * cus * NW;
         if (w > st) w = st;
         if (w == waves && round > 0) break;
         waves = w;
     }
-    tmax = ((st + waves - 1) / waves) * ct;
-    lds = piece_lds_bytes<BITS>(MT, XREG, L, c.nwaves, a.K, tmax);
+    const int blocks = (int)((waves + NW - 1) / NW);
+    // the kernel deals super-tiles over all blocks*NW wavefronts
+    tmax = ((st + (int64_t)blocks * NW - 1) / ((int64_t)blocks * NW)) * ct;
+    lds = piece_lds_bytes<BITS>(MT, XREG, L, J, a.K, tmax);
     if (lds > kPieceLdsMax) return hipErrorInvalidValue;
     ProjArgs a2 = a;
     a2.tpw = ct;
     a2.tmax = tmax;
-    const int blocks = (int)((waves + c.nwaves - 1) / c.nwaves);
-    hipLaunchKernelGGL((piece_kernel<BITS, MT, SW, XREG, J>), dim3(blocks), dim3(64 * c.nwaves), lds, s, a2);
+    hipLaunchKernelGGL((piece_kernel<BITS, MT, SW, XREG, L, J>), dim3(blocks), dim3(kPieceThreads), lds, s, a2);
     return hipGetLastError();
 }
 
-template <int BITS, int MT, bool SW, int J>
+template <int BITS, int MT, bool SW, int L, int J>
 hipError_t launch_piece_mt(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
-    if (c.xreg) {
-        if constexpr (piece_xreg_ok<BITS, MT, J>()) return launch_piece_one<BITS, MT, SW, true, J>(a, c, s);
-        else return hipErrorInvalidValue;
-    }
-    return launch_piece_one<BITS, MT, SW, false, J>(a, c, s);
+    constexpr bool XR = piece_xreg_ok<BITS, MT, J>();
+    if ((c.xreg != 0) != XR) return hipErrorInvalidValue;
+    return launch_piece_one<BITS, MT, SW, XR, L, J>(a, s);
 }
 
-template <int BITS, bool SW, int J>
-hipError_t launch_piece_j(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+template <int BITS, bool SW, int L, int J>
+hipError_t launch_piece_lj(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
     switch (c.MT) {
-        case 1: return launch_piece_mt<BITS, 1, SW, J>(a, c, s);
-        case 2: return launch_piece_mt<BITS, 2, SW, J>(a, c, s);
-        case 4: return launch_piece_mt<BITS, 4, SW, J>(a, c, s);
-        case 8: return launch_piece_mt<BITS, 8, SW, J>(a, c, s);
+        case 1: return launch_piece_mt<BITS, 1, SW, L, J>(a, c, s);
+        case 2: return launch_piece_mt<BITS, 2, SW, L, J>(a, c, s);
+        case 4: return launch_piece_mt<BITS, 4, SW, L, J>(a, c, s);
+        case 8: return launch_piece_mt<BITS, 8, SW, L, J>(a, c, s);
         default: return hipErrorInvalidValue;
     }
 }
 
+// The (2^L lanes per row, J pieces per lane) pairs the geometry choice uses.
 template <int BITS, bool SW>
 hipError_t launch_piece_impl(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
-    switch (c.pieces_per_lane) {
-        case 1: return launch_piece_j<BITS, SW, 1>(a, c, s);
-        case 2: return launch_piece_j<BITS, SW, 2>(a, c, s);
-        case 3: return launch_piece_j<BITS, SW, 3>(a, c, s);
-        case 4: return launch_piece_j<BITS, SW, 4>(a, c, s);
-        case 8: return launch_piece_j<BITS, SW, 8>(a, c, s);
+    switch (c.lpr_log2 * 16 + c.pieces_per_lane) {
+        case 6 * 16 + 1: return launch_piece_lj<BITS, SW, 6, 1>(a, c, s);
+        case 6 * 16 + 2: return launch_piece_lj<BITS, SW, 6, 2>(a, c, s);
+        case 6 * 16 + 3: return launch_piece_lj<BITS, SW, 6, 3>(a, c, s);
+        case 6 * 16 + 4: return launch_piece_lj<BITS, SW, 6, 4>(a, c, s);
+        case 6 * 16 + 8: return launch_piece_lj<BITS, SW, 6, 8>(a, c, s);
+        case 4 * 16 + 1: return launch_piece_lj<BITS, SW, 4, 1>(a, c, s);
+        case 4 * 16 + 2: return launch_piece_lj<BITS, SW, 4, 2>(a, c, s);
+        case 4 * 16 + 3: return launch_piece_lj<BITS, SW, 4, 3>(a, c, s);
+        case 4 * 16 + 4: return launch_piece_lj<BITS, SW, 4, 4>(a, c, s);
+        case 3 * 16 + 1: return launch_piece_lj<BITS, SW, 3, 1>(a, c, s);
+        case 2 * 16 + 1: return launch_piece_lj<BITS, SW, 2, 1>(a, c, s);
         default: return hipErrorInvalidValue;
     }
 }

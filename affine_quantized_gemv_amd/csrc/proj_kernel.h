@@ -197,6 +197,19 @@ __device__ __forceinline__ float segment_sum64(float v, int L)
     return v;
 }
 
+// The same tree with the segment width fixed at compile time (no branches).
+template <int L>
+__device__ __forceinline__ float segment_sum64_ct(float v)
+{
+    if constexpr (L >= 1) v += dpp_f32<0xB1>(v);
+    if constexpr (L >= 2) v += dpp_f32<0x4E>(v);
+    if constexpr (L >= 3) v += dpp_f32<0x141>(v);
+    if constexpr (L >= 4) v += dpp_f32<0x140>(v);
+    if constexpr (L >= 5) v += __shfl_xor(v, 16);
+    if constexpr (L >= 6) v += __shfl_xor(v, 32);
+    return v;
+}
+
 // ------------------------------------------------------- per-unit arithmetic
 
 // One unit of R rows (S weight streams) against x from LDS:
