@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(kMfmaMaxThreads) mfma_dense_kernel(ProjArgs a)
         const int ks = kw >> 5;                        // k-steps in this tile
         const int nsteps = (ks - wk + NK - 1) >> nk_log2;  // this wavefront's k-steps
 
-        auto fetch = [&](int d, int j) {
+        auto fetch = [&](int d, int j) __attribute__((always_inline)) {
             const int koff = kt + 32 * j;
 #pragma unroll
             for (int s = 0; s < S; ++s)
@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(kMfmaMaxThreads) mfma_dense_kernel(ProjArgs a)
         const int ntask = MT * c8n;
         const int nthr = blockDim.x;
         u32x4_t xr[XB];
-        auto xload = [&](int t0) {
+        auto xload = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < XB; ++i) {
                 const int t = t0 + i * nthr;
@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(kMfmaMaxThreads) mfma_dense_kernel(ProjArgs a)
                 }
             }
         };
-        auto xstore = [&](int t0) {
+        auto xstore = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < XB; ++i) {
                 const int t = t0 + i * nthr;
@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(kMfmaMaxThreads) mfma_dense_kernel(ProjArgs a)
             }
         };
         xload(threadIdx.x);
-        static_for<0, D>([&](auto Dd) {
+        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
             constexpr int d = decltype(Dd)::value;
             if (d < nsteps) fetch(d, wk + d * NK);
         });
@@ -136,7 +136,7 @@ __global__ void __launch_bounds__(kMfmaMaxThreads) mfma_dense_kernel(ProjArgs a)
         __syncthreads();
 
         for (int base = 0; base < nsteps; base += D) {
-            static_for<0, D>([&](auto Dd) {
+            static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
                 constexpr int d = decltype(Dd)::value;
                 const int i = base + d;
                 if (i < nsteps) {

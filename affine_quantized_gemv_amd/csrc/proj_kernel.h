@@ -100,7 +100,7 @@ __device__ __forceinline__ void plan_x_operands(const uint32_t (&xw)[NXW], uint3
                                                 float& X, float& T)
 {
     float xs = 0.0f, ts = 0.0f;
-    static_for<0, P::NP>([&](auto I) {
+    static_for<0, P::NP>([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         const uint32_t hl = half_of(xw, P::LO_K[i]);
         const uint32_t hh = half_of(xw, P::HI_K[i]);
@@ -250,7 +250,7 @@ __device__ __forceinline__ void unit_mac(const uint32_t (&w)[S][R][Geo<BITS>::NW
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int m = 0; m < MT; ++m) dd[s][r][m] = de[s][r][m] = 0.0f;
-        static_for<0, NCH>([&](auto C) {
+        static_for<0, NCH>([&](auto C) __attribute__((always_inline)) {
             constexpr int c = decltype(C)::value;
             uint32_t p[S][R][4];
 #pragma unroll
@@ -358,7 +358,7 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
         uint4* xp = lds_u4;
         float2* xc = reinterpret_cast<float2*>(lds_u4 + MT * NCH * ut);
 
-        auto fetch = [&](int d, int u) {
+        auto fetch = [&](int d, int u) __attribute__((always_inline)) {
 #pragma unroll
             for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -388,7 +388,7 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
 #pragma unroll
         for (int i = 0; i < XB; ++i)
             if ((int)threadIdx.x + i * nthr < ntask) xr[i] = st.load(threadIdx.x + i * nthr);
-        static_for<0, D>([&](auto Dd) {
+        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
             constexpr int d = decltype(Dd)::value;
             if (d < upl) fetch(d, li + d * LPR);
         });
@@ -406,7 +406,7 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
         __syncthreads();
 
         for (int base = 0; base < upl; base += D) {
-            static_for<0, D>([&](auto Dd) {
+            static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
                 constexpr int d = decltype(Dd)::value;
                 const int j = base + d;
                 if (j < upl) {
@@ -463,7 +463,7 @@ __global__ void __launch_bounds__(256) unpack_kernel(const uint32_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 16; ++i) c[i] = 0;
     constexpr uint32_t FM = (1u << P::SW) - 1u;
-    static_for<0, P::NP>([&](auto I) {
+    static_for<0, P::NP>([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         const uint32_t p = P::template pair<i>(w);
         const uint32_t lo = (p >> P::LO_P[i]) & FM;

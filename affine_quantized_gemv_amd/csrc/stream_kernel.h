@@ -125,12 +125,12 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
     int f_j = 0;
     // next tile of this wavefront: the next one in the super-tile, else the
     // first of the super-tile W further on (counters, no 64-bit division)
-    auto next_tile = [&](int64_t t) {
+    auto next_tile = [&](int64_t t) __attribute__((always_inline)) {
         ++t;
         if (++f_c == CT) { f_c = 0; t += (W - 1) * CT; }
         return t;
     };
-    auto fetch = [&](int d) {
+    auto fetch = [&](int d) __attribute__((always_inline)) {
         int u = li + f_j * LPR;
         if (u >= U) u = U - 1;
         int64_t n = f_tile * G + slot;
@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
     const int64_t nitems = my_tiles * upl;
     // prologue: D items, unconditionally (past the end they are clamped,
     // harmless re-reads that are never consumed)
-    static_for<0, D>([&](auto Dd) { fetch(decltype(Dd)::value); });
+    static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(decltype(Dd)::value); });
 
     float acc[S][1][MT];
 #pragma unroll
@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
     int c_j = 0;
     int ti = 0;                 // tiles finished by this wavefront
 
-    auto consume = [&](auto Dd) {
+    auto consume = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
         {
             {
@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
                         for (int s = 0; s < S; ++s)
 #pragma unroll
                             for (int m = 0; m < MT; ++m) dd[s][m] = de[s][m] = 0.0f;
-                        static_for<0, NCH>([&](auto C) {
+                        static_for<0, NCH>([&](auto C) __attribute__((always_inline)) {
                             constexpr int c = decltype(C)::value;
 #pragma unroll
                             for (int s = 0; s < S; ++s) {
@@ -254,13 +254,13 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
 
     int64_t base = 0;
     for (; base + 2 * D <= nitems; base += D) {         // steady state: no branches around memory ops
-        static_for<0, D>([&](auto Dd) {
+        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
             consume(Dd);
             fetch(decltype(Dd)::value);
         });
     }
     for (; base < nitems; base += D) {                  // drain
-        static_for<0, D>([&](auto Dd) {
+        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
             constexpr int d = decltype(Dd)::value;
             if (base + d < nitems) {
                 consume(Dd);
