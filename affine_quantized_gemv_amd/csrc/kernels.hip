@@ -3,6 +3,7 @@
 // streaming or tiled VALU kernels (proj_b*.hip); matrix-core kernels
 // (mfma_dense.hip) for dense and SwiGLU calls with M = 9..32, tiled VALU
 // kernels for affine M = 9..32; plus the code-unpack kernel.
+#include "mfma_stream.h"
 #include "piece_kernel.h"
 #include "stream_kernel.h"
 
@@ -82,6 +83,27 @@ LaunchCfg choose_mfma(bool swiglu, int M, int N, int K)
     const size_t red = nk > 1 ? (size_t)c.nwaves * (swiglu ? 2 : 1) * c.R * (c.MT / 16) * 4 * 64 * 4 : 0;
     c.lds = lds > red ? lds : red;
     return c;
+}
+
+// Persistent matrix-core geometry for large N (M = 9..32, dense / SwiGLU):
+// at least 2048 row tiles of 16 rows, and x^T for the whole K plus the output
+// staging fit in LDS at M = 32 with one 4-wavefront workgroup per CU.  The
+// choice depends on (N, K) only, so every M = 9..32 of a shape takes it.
+bool choose_mfma_stream(bool swiglu, int M, int N, int K, LaunchCfg& c)
+{
+    c = LaunchCfg{};
+    if (K % 32 != 0) return false;
+    const int64_t T = ((int64_t)N + 15) / 16;
+    if (T < 2048) return false;
+    const int64_t tmax = (T + 1023) / 1024;
+    if (detail::mfma_stream_lds_bytes(32, K, tmax) > detail::kMfmaStreamLdsMax) return false;
+    c.path = PATH_MFMA_STREAM;
+    c.MT = M <= 16 ? 16 : 32;
+    c.KT = K;
+    c.nwaves = detail::kMfmaStreamThreads / 64;
+    c.R = 1;
+    (void)swiglu;
+    return true;
 }
 
 int ceil_log2(int v) { int l = 0; while ((1 << l) < v) ++l; return l; }
@@ -200,8 +222,9 @@ bool choose_piece(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
 
 LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 {
-    if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
     LaunchCfg c;
+    if (bits == 0 && M > 8 && choose_mfma_stream(swiglu, M, N, K, c)) return c;
+    if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
     if (choose_piece(bits, swiglu, M, N, K, c)) return c;
     if (choose_stream(bits, swiglu, M, N, K, c)) return c;
     return choose_valu(bits, swiglu, M, N, K);
@@ -209,6 +232,10 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 
 hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
+    if (c.path == PATH_MFMA_STREAM) {
+        if (bits != 0) return hipErrorInvalidValue;
+        return swiglu ? launch_mfma_stream<true>(a, c, s) : launch_mfma_stream<false>(a, c, s);
+    }
     if (c.path == PATH_MFMA) {
         if (bits != 0) return hipErrorInvalidValue;
         return swiglu ? launch_mfma<true>(a, c, s) : launch_mfma<false>(a, c, s);

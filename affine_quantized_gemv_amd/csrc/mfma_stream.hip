@@ -1,0 +1,16 @@
+// Instantiation of the persistent matrix-core streaming kernels (dense bf16
+// GEMV and fused SwiGLU, M padded to 16 or 32).
+#include "mfma_stream.h"
+
+namespace aqg {
+template <>
+hipError_t launch_mfma_stream<false>(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+{
+    return detail::launch_mfma_stream_impl<false>(a, c, s);
+}
+template <>
+hipError_t launch_mfma_stream<true>(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+{
+    return detail::launch_mfma_stream_impl<true>(a, c, s);
+}
+}  // namespace aqg

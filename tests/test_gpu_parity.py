@@ -258,6 +258,36 @@ def test_swiglu_against_unfused_oracle_chain(M):
     assert_within(y, r["out"][:M], tol, "swiglu M=%d" % M)
 
 
+@pytest.mark.parametrize("M", [9, 16, 32])
+def test_dense_large_n_ragged_matrix_core_stream(M):
+    """N = 40001 (>= 2048 row tiles of 16, last one ragged): the persistent
+    matrix-core path, within tolerance, and M = 9..31 bit for bit equal to the
+    first rows of the M = 32 call."""
+    N, K = 40001, 512
+    x = synth.normal_bf16((32, K), 1.0, 79, "ln/x")
+    W = synth.normal_bf16((N, K), 0.02, 79, "ln/W")
+    xd, Wd = bf16_dev(x), bf16_dev(W)
+    y = run_guarded(gemv_dense_gpu(xd, Wd, M), M, N)
+    ref, A = oracle.gemv_bf16(x[:M], W)
+    assert_within(y, ref, oracle.tolerance(A), "dense %dx%dx%d" % (M, N, K))
+    y32 = aqg.gemv_bf16(xd[:32], Wd, out_dtype=torch.float32).cpu().numpy()
+    yM = aqg.gemv_bf16(xd[:M], Wd, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(yM, y32[:M])
+
+
+@pytest.mark.parametrize("M", [12, 32])
+def test_swiglu_large_n_matrix_core_stream(M):
+    N, K = 33001, 256
+    x = synth.normal_bf16((32, K), 1.0, 80, "sl/x")
+    Wg = synth.normal_bf16((N, K), 0.02, 80, "sl/g")
+    Wu = synth.normal_bf16((N, K), 0.02, 80, "sl/u")
+    xd, Wgd, Wud = bf16_dev(x), bf16_dev(Wg), bf16_dev(Wu)
+    y = run_guarded(lambda out: aqg.swiglu_bf16(xd[:M], Wgd, Wud, out=out), M, N)
+    r = oracle.swiglu_bf16(x[:M], Wg, Wu)
+    tol = oracle.swiglu_tolerance(r["g"], r["u"], r["Ag"], r["Au"], r["out"])
+    assert_within(y, r["out"], tol, "swiglu %dx%dx%d" % (M, N, K))
+
+
 def test_swiglu_zero_weights_give_exact_zero():
     N, K = 300, 1536
     x = bf16_dev(synth.activations(synth.CFG_SWIGLU, K)[:4])
