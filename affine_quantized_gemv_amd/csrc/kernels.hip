@@ -86,16 +86,17 @@ LaunchCfg choose_mfma(bool swiglu, int M, int N, int K)
 }
 
 // Persistent matrix-core geometry for large N (M = 9..32, dense / SwiGLU):
-// at least 2048 row tiles of 16 rows, and x^T for the whole K plus the output
-// staging fit in LDS at M = 32 with one 4-wavefront workgroup per CU.  The
-// choice depends on (N, K) only, so every M = 9..32 of a shape takes it.
+// K a multiple of 64, at least 2048 row tiles of 16 rows, and x^T for the
+// whole K plus the output staging fit in LDS at M = 32 with one 8-wavefront
+// workgroup per CU.  The choice depends on (N, K) only, so every M = 9..32 of
+// a shape takes it.
 bool choose_mfma_stream(bool swiglu, int M, int N, int K, LaunchCfg& c)
 {
     c = LaunchCfg{};
-    if (K % 32 != 0) return false;
+    if (K % 64 != 0) return false;
     const int64_t T = ((int64_t)N + 15) / 16;
     if (T < 2048) return false;
-    const int64_t tmax = (T + 1023) / 1024;
+    const int64_t tmax = (T + 2047) / 2048;
     if (detail::mfma_stream_lds_bytes(32, K, tmax) > detail::kMfmaStreamLdsMax) return false;
     c.path = PATH_MFMA_STREAM;
     c.MT = M <= 16 ? 16 : 32;

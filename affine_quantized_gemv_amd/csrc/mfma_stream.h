@@ -6,12 +6,17 @@
 // walks its tile's K/32 k-steps, each one MFMA per 16-column block of x^T,
 // and keeps a ring of D k-steps of weights in flight across tile boundaries.
 //
-//   * A operands are read with buffer loads through a wave-uniform per-tile
-//     descriptor: lane (c, r) reads 16 bytes of row r at k = 32s + 8c, so an
-//     instruction covers 64 contiguous bytes of each of 16 rows and the next
-//     k-step the other half of those 128-byte lines; the k-step's byte offset
-//     is a uniform scalar offset, so loads cost no vector arithmetic.  Rows
-//     past N read as zero (outside the descriptor's range).
+//   * A operands are read two k-steps (64 k, 128 bytes per row) at a time
+//     with two buffer loads that each cover whole 128-byte lines: the first
+//     reads rows 0..7 of the tile, the second rows 8..15; in each 16-lane
+//     group g, lanes 0..7 take the 16-byte piece g of their row and lanes
+//     8..15 the piece 4 + g.  One v_cndmask with a row_ror:8 DPP operand per
+//     dword then forms the two MFMA A operands (all 16 rows, pieces 0..3 for
+//     the first k-step, 4..7 for the second).  (A layout where each load
+//     instruction covered 64 bytes of 16 rows measured ~25% slower.)  The
+//     loads go through a wave-uniform per-tile descriptor; the k-block and
+//     row-half offsets are uniform scalar offsets, so loads cost no vector
+//     arithmetic.  Rows past N read as zero (outside the descriptor's range).
 //   * x^T is staged once per workgroup in LDS in fragment order (for k-step s
 //     and column block b the 64 lanes' 16-byte B operands are contiguous).
 //   * Row tiles are dealt round-robin to all resident wavefronts, as in the
@@ -32,7 +37,7 @@
 namespace aqg {
 namespace detail {
 
-constexpr int kMfmaStreamThreads = 256;
+constexpr int kMfmaStreamThreads = 512;
 constexpr size_t kMfmaStreamLdsMax = 160 * 1024;
 
 template <int MT, bool SWIGLU, int D>
@@ -49,6 +54,7 @@ __global__ void __launch_bounds__(kMfmaStreamThreads) mfma_stream_kernel(ProjArg
     const int c = lane >> 4;             // k sub-block (A, B) / row quad (D)
     const int r = lane & 15;             // A row / B and D column
     const int KS = a.K / 32;             // k-steps per row
+    const int KP = a.K / 64;             // k-step pairs per row
     const int64_t row_bytes = (int64_t)a.K * 2;
     const int64_t T = ((int64_t)a.N + 15) / 16;
     const int64_t CT = a.tpw;
@@ -65,12 +71,14 @@ __global__ void __launch_bounds__(kMfmaStreamThreads) mfma_stream_kernel(ProjArg
     u32x4_t* xb = lds_m4;                                                    // [s][b][lane]
     float* obuf = reinterpret_cast<float*>(lds_m4 + (size_t)KS * NB * 64) + (size_t)wave * a.tmax * PER_TILE;
 
-    // ---- ring of D k-steps: slot d holds the A operands of one k-step
-    u32x4_t wa[D][S];
+    // ---- ring of D k-step pairs: slot d holds the two loads of one pair
+    u32x4_t wa[D][S][2];
     int64_t f_tile = wg * CT;            // tile being fetched (wave-uniform)
     int f_c = 0;                         // its index within the super-tile
-    int f_s = 0;                         // its k-step
-    const uint32_t voff = (uint32_t)(r * row_bytes + 16 * c);
+    int f_p = 0;                         // its k-step pair
+    const int h = lane & 15;
+    const uint32_t voff = (uint32_t)((h & 7) * row_bytes + 16 * ((h < 8 ? 0 : 4) + c));
+    const int half_off = (int)(8 * row_bytes);
     auto fetch = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
         const int64_t n0 = f_tile * 16;
@@ -79,12 +87,26 @@ __global__ void __launch_bounds__(kMfmaStreamThreads) mfma_stream_kernel(ProjArg
         for (int s = 0; s < S; ++s) {
             const __amdgpu_buffer_rsrc_t rs =
                 tile_rsrc(static_cast<const char*>(s == 0 ? a.w0 : a.w1) + n0 * row_bytes, bytes);
-            wa[d][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 64 * f_s, kLoadNT));
+            wa[d][s][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 128 * f_p, kLoadNT));
+            wa[d][s][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 128 * f_p + half_off, kLoadNT));
         }
-        if (++f_s == KS) {
-            f_s = 0;
-            ++f_tile;
-            if (++f_c == CT) { f_c = 0; f_tile += (W - 1) * CT; }
+        // advance (tile, pair) without branches: wave-uniform selects
+        const bool wrap = f_p + 1 == KP;
+        const bool stw = wrap && f_c + 1 == CT;
+        f_p = wrap ? 0 : f_p + 1;
+        f_c = wrap ? (stw ? 0 : f_c + 1) : f_c;
+        f_tile += wrap ? (stw ? (W - 1) * CT + 1 : 1) : 0;
+    };
+    // the two A operands of a pair: lanes 8..15 of each 16-lane group swap
+    // halves across the two loads (rotate by 8 within the group)
+    const bool hi8 = (lane & 8) != 0;
+    auto a_ops = [&](const u32x4_t& l0, const u32x4_t& l1, u32x4_t& s0, u32x4_t& s1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l0[i], 0x128, 0xF, 0xF, false);
+            const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l1[i], 0x128, 0xF, 0xF, false);
+            s0[i] = hi8 ? r1 : l0[i];
+            s1[i] = hi8 ? l1[i] : r0;
         }
     };
 
@@ -93,18 +115,23 @@ __global__ void __launch_bounds__(kMfmaStreamThreads) mfma_stream_kernel(ProjArg
     for (int s = 0; s < S; ++s)
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[s][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    int c_s = 0;                         // k-step being consumed
+    int c_s = 0;                         // k-step pair being consumed
     int ti = 0;                          // tiles finished by this wavefront
 
     auto consume = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
+        u32x4_t A[S][2];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const u32x4_t xv = xb[(c_s * NB + b) * 64 + lane];
+        for (int s = 0; s < S; ++s) a_ops(wa[d][s][0], wa[d][s][1], A[s][0], A[s][1]);
 #pragma unroll
-            for (int s = 0; s < S; ++s) acc[s][b] = mfma16x16x32(wa[d][s], xv, acc[s][b]);
-        }
-        if (++c_s == KS) {
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const u32x4_t xv = xb[((2 * c_s + t) * NB + b) * 64 + lane];
+#pragma unroll
+                for (int s = 0; s < S; ++s) acc[s][b] = mfma16x16x32(A[s][t], xv, acc[s][b]);
+            }
+        if (++c_s == KP) {
             // end of a row tile: lane holds rows 4c..4c+3 of column r of each
             // column block; stage them (fp32), then reset
             c_s = 0;
@@ -130,19 +157,32 @@ __global__ void __launch_bounds__(kMfmaStreamThreads) mfma_stream_kernel(ProjArg
     // prologue: D k-steps (past the wavefront's share they read zeros or
     // valid rows and are never consumed), then stage x^T
     static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
-    for (int t = threadIdx.x; t < KS * NB * 64; t += kMfmaStreamThreads) {
-        const int l = t & 63;
-        const int sb = t >> 6;           // s * NB + b
-        const int s = sb / NB, b = sb - s * NB;
-        const int m = 16 * b + (l & 15);
-        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (m < a.M) v = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)m * a.K + 32 * s + 8 * (l >> 4));
-        xb[t] = v;
+    // x^T staging, 8 loads in flight per thread before their stores
+    constexpr int XB = 8;
+    const int ntask = KS * NB * 64;
+    for (int t0 = threadIdx.x; t0 < ntask; t0 += XB * kMfmaStreamThreads) {
+        u32x4_t v[XB];
+#pragma unroll
+        for (int i = 0; i < XB; ++i) {
+            const int t = t0 + i * kMfmaStreamThreads;
+            const int l = t & 63;
+            const int sb = t >> 6;       // s * NB + b
+            const int s = sb / NB, b = sb - s * NB;
+            const int m = 16 * b + (l & 15);
+            v[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (t < ntask && m < a.M)
+                v[i] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)m * a.K + 32 * s + 8 * (l >> 4));
+        }
+#pragma unroll
+        for (int i = 0; i < XB; ++i) {
+            const int t = t0 + i * kMfmaStreamThreads;
+            if (t < ntask) xb[t] = v[i];
+        }
     }
     __syncthreads();
     if (my_tiles == 0) return;
 
-    const int64_t nitems = my_tiles * KS;
+    const int64_t nitems = my_tiles * KP;
     int64_t base = 0;
     for (; base + 2 * D <= nitems; base += D) {          // steady state
         static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
@@ -184,8 +224,8 @@ inline size_t mfma_stream_lds_bytes(int MT, int K, int64_t tmax)
     return (size_t)(K / 32) * (MT / 16) * 64 * 16 + (size_t)(kMfmaStreamThreads / 64) * tmax * 16 * MT * 4;
 }
 
-// Depth (k-steps in flight per wavefront).
-constexpr int kMfmaStreamDepth = 8;
+// Depth (k-step pairs, 2 KB per weight stream, in flight per wavefront).
+constexpr int kMfmaStreamDepth = 4;
 
 template <int MT, bool SW>
 hipError_t launch_mfma_stream_one(const ProjArgs& a, hipStream_t s)

@@ -80,9 +80,23 @@ template <int BITS, int J, int MT> struct PieceDepth {
     static constexpr int RD = J == 1 ? 2 : (J >= 4 ? 1 : ((MT >= 8 || (BITS != 0 && J == 2)) ? 2 : 1));
 };
 
-// x operands of one piece for one row m: dense, the 8 bf16 as they are;
-// affine, the piece plan's pre-scaled pairs plus X and T.  have = false gives
-// all zeros.
+// x operands of one piece for one row m from its KPP x values (as bf16 pair
+// words): dense, the 8 bf16 as they are; affine, the piece plan's pre-scaled
+// pairs plus X and T.
+template <int BITS>
+__device__ __forceinline__ void piece_operands(const uint32_t (&xw)[PieceGeo<BITS>::KPP / 2],
+                                               uint32_t (&xq)[PieceGeo<BITS>::NPP], float& X, float& T)
+{
+    if constexpr (BITS == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xq[i] = xw[i];
+        X = T = 0.0f;
+    } else {
+        plan_x_operands<PiecePlan<BITS>, PieceGeo<BITS>::KPP / 2>(xw, xq, X, T);
+    }
+}
+
+// The same from memory; have = false gives all zeros.
 template <int BITS>
 __device__ __forceinline__ void piece_x(const uint16_t* __restrict__ xrow, bool have,
                                         uint32_t (&xq)[PieceGeo<BITS>::NPP], float& X, float& T)
@@ -95,13 +109,7 @@ __device__ __forceinline__ void piece_x(const uint16_t* __restrict__ xrow, bool 
         const uint4 v = have ? src[i] : make_uint4(0, 0, 0, 0);
         xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
     }
-    if constexpr (BITS == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xq[i] = xw[i];
-        X = T = 0.0f;
-    } else {
-        plan_x_operands<PiecePlan<BITS>, KPP / 2>(xw, xq, X, T);
-    }
+    piece_operands<BITS>(xw, xq, X, T);
 }
 
 // Buffer descriptor over `bytes` bytes from p (clamped to the 32-bit range).
@@ -166,17 +174,38 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                                   xq[j][m], xX[j][m], xT[j][m]);
                 }
         } else {
-            // every wavefront of the workgroup stages, then all synchronize
-            for (int t = threadIdx.x; t < MT * PRP; t += kPieceThreads) {
-                const int m = t / PRP, p = t - m * PRP;
-                const bool have = m < a.M && p < PR;
-                uint32_t q[NPP];
-                float X, Tc;
-                piece_x<BITS>(a.x + (size_t)m * a.K + (size_t)(have ? p : 0) * KPP, have, q, X, Tc);
+            // every wavefront of the workgroup stages, then all synchronize;
+            // XB tasks per thread have their loads in flight together
+            constexpr int XB = BITS == 0 ? 8 : 2;
+            constexpr int KW = KPP / 2;                 // x words per piece
+            for (int t0 = threadIdx.x; t0 < MT * PRP; t0 += XB * kPieceThreads) {
+                uint32_t xw[XB][KW];
 #pragma unroll
-                for (int c = 0; c < NCHP; ++c)
-                    xp[(m * NCHP + c) * PRP + p] = make_uint4(q[4 * c], q[4 * c + 1], q[4 * c + 2], q[4 * c + 3]);
-                if constexpr (BITS != 0) xc[m * PRP + p] = make_float2(X, Tc);
+                for (int i = 0; i < XB; ++i) {
+                    const int t = t0 + i * kPieceThreads;
+                    const int m = t / PRP, p = t - m * PRP;
+                    const bool have = t < MT * PRP && m < a.M && p < PR;
+                    const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)(have ? m : 0) * a.K +
+                                                                      (size_t)(have ? p : 0) * KPP);
+#pragma unroll
+                    for (int w = 0; w < KW / 4; ++w) {
+                        const uint4 v = have ? src[w] : make_uint4(0, 0, 0, 0);
+                        xw[i][4 * w] = v.x; xw[i][4 * w + 1] = v.y; xw[i][4 * w + 2] = v.z; xw[i][4 * w + 3] = v.w;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < XB; ++i) {
+                    const int t = t0 + i * kPieceThreads;
+                    if (t >= MT * PRP) break;
+                    const int m = t / PRP, p = t - m * PRP;
+                    uint32_t q[NPP];
+                    float X, Tc;
+                    piece_operands<BITS>(xw[i], q, X, Tc);
+#pragma unroll
+                    for (int c = 0; c < NCHP; ++c)
+                        xp[(m * NCHP + c) * PRP + p] = make_uint4(q[4 * c], q[4 * c + 1], q[4 * c + 2], q[4 * c + 3]);
+                    if constexpr (BITS != 0) xc[m * PRP + p] = make_float2(X, Tc);
+                }
             }
             __syncthreads();
         }
