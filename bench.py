@@ -20,7 +20,8 @@ batches of back-to-back calls on the launch stream.  The other configurations
 reported under "other_configs" with the same per-call method.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--no-extra] [--copy-probe MIB]
+       [--no-extra] [--copy-probe MIB] [--counter-call LABEL]
+       [--summarize-profile DB]
 """
 from __future__ import annotations
 
@@ -51,6 +52,9 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     p.add_argument("--copy-probe", type=float, default=0.0,
                    help="only run a device copy of this many MiB (counter calibration) and exit")
+    p.add_argument("--counter-call", metavar="LABEL", default=None,
+                   help="only run the dense decode call with this label (as in the profile "
+                        "summary, e.g. 'dense lm_head M=32 100000x1536') 8 times, for counter runs")
     p.add_argument("--summarize-profile", metavar="DB", default=None,
                    help="print a markdown summary of a rocprofv3 database (rocpd) taken with "
                         "--kernel-trace --marker-trace --kernel-rename of this script, then exit")
@@ -274,7 +278,8 @@ def copy_probe(mib):
 
 
 def cpu_baseline(steps_bytes):
-    """The fp64 oracle on the host cores over whole steps of the same workload."""
+    """The fp64 oracle on the host cores over whole steps of the same workload
+    (as many whole steps as fit in about 10 s, at least one)."""
     import oracle
     import synth
     cfg = synth.CFG_DENSE_DECODE
@@ -291,7 +296,7 @@ def cpu_baseline(steps_bytes):
                 oracle.gemv_bf16(xs[K][:M], Ws[name])
         nsteps += 1
         el = time.perf_counter() - t0
-        if el >= 10.0 or nsteps >= 3:
+        if el >= 10.0 or nsteps >= 50:    # about 10 s of host work
             break
     gbps = steps_bytes * nsteps / el / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
@@ -326,23 +331,26 @@ def summarize_profile(db):
     rows = list(c.execute(
         "select region, name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
         "from kernels group by region, name order by sum(duration) desc"))
-    out = ["| region (call) | kernel | dispatches | avg us | min us | max us | GB/s at avg | % of 8 TB/s |",
+    def short(name):
+        return name.replace("void aqg::detail::", "").replace("(aqg::ProjArgs)", "")
+
+    out = ["| call | kernel | n | avg us | min | max | GB/s | % peak |",
            "|---|---|---|---|---|---|---|---|"]
     for region, name, n, avg, mn, mx, _ in rows:
         if not region or region.startswith("timed steps"):
             continue
         b = label_bytes(region)
         gbps = b / avg
-        out.append("| %s | `%s` | %d | %.2f | %.2f | %.2f | %.0f | %.1f |" % (
-            region, name, n, avg / 1e3, mn / 1e3, mx / 1e3, gbps, 100 * gbps / HBM_PEAK_GBPS))
+        out.append("| %s | `%s` | %d | %.2f | %.1f | %.1f | %.0f | %.1f |" % (
+            region, short(name), n, avg / 1e3, mn / 1e3, mx / 1e3, gbps, 100 * gbps / HBM_PEAK_GBPS))
     out.append("")
     out.append("Whole timed steps (graph replay and eager), by kernel symbol:")
     out.append("")
-    out.append("| region | kernel | dispatches | avg us | total ms |")
+    out.append("| region | kernel | n | avg us | total ms |")
     out.append("|---|---|---|---|---|")
     for region, name, n, avg, mn, mx, tot in rows:
         if region and region.startswith("timed steps"):
-            out.append("| %s | `%s` | %d | %.2f | %.3f |" % (region, name, n, avg / 1e3, tot / 1e6))
+            out.append("| %s | `%s` | %d | %.2f | %.3f |" % (region, short(name), n, avg / 1e3, tot / 1e6))
     print("\n".join(out))
     return 0
 
@@ -365,6 +373,16 @@ def main():
     MARKERS = Markers()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return 0
+    if args.counter_call:
+        calls = [c for c in dense_decode_calls() if label_of(c) == args.counter_call]
+        if not calls:
+            print("no dense decode call is labelled %r" % args.counter_call, file=sys.stderr)
+            return 2
+        for _ in range(8):
+            calls[0]()
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_call": args.counter_call, "launches": 8, "bytes_per_launch": calls[0].bytes}))
         return 0
 
     t_setup = time.perf_counter()
