@@ -205,14 +205,15 @@ bool choose_piece(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
     const int64_t row_bytes = (int64_t)PR * 16;
     int64_t ct = 8192 / (G * row_bytes);
     if (ct < 1) ct = 1;
-    const int64_t st = (T + ct - 1) / ct;
-    const int64_t tmax = ((st + 1023) / 1024) * ct;
-    const size_t x8 = xreg_at(8) ? 0 : (size_t)8 * PRP * (4 * NPP + (bits ? 8 : 0));
+    // tiles per wavefront with any super-tile size up to ct and at least one
+    // 4-wavefront workgroup per CU
+    const int64_t tmax = (T + 1023) / 1024 + ct;
+    const size_t x8 = (bits == 0 && xreg_at(8)) ? 0 : (size_t)8 * PRP * (4 * NPP + (bits ? 8 : 0));
     if (x8 + (size_t)4 * tmax * G * 8 * 4 > detail::kPieceLdsMax) return false;
     c.lpr_log2 = L;
     c.pieces_per_lane = J;
     c.xreg = xreg_at(c.MT) ? 1 : 0;
-    c.lds = c.xreg ? 0 : (size_t)c.MT * PRP * (4 * NPP + (bits ? 8 : 0));
+    c.lds = (bits == 0 && c.xreg) ? 0 : (size_t)c.MT * PRP * (4 * NPP + (bits ? 8 : 0));
     c.KT = K;
     c.nwaves = 4;
     c.R = 1;

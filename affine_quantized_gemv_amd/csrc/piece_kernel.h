@@ -162,8 +162,48 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
     float2* xc = reinterpret_cast<float2*>(lds_p4 + (size_t)MT * NCHP * PRP);  // [m][piece slot] (X, T)
     uint32_t xq[XREG ? J : 1][XREG ? MT : 1][NPP];
     float xX[XREG ? J : 1][XREG ? MT : 1], xT[XREG ? J : 1][XREG ? MT : 1];
+    // The workgroup computes every (m, piece slot) operand once into LDS
+    // (XB tasks per thread with their loads in flight together), then
+    // synchronizes.  Affine operands take ~100 VALU instructions per piece,
+    // so computing them per lane in every wavefront would delay the first
+    // weights by microseconds.
+    auto stage_x = [&]() __attribute__((always_inline)) {
+        constexpr int XB = BITS == 0 ? 8 : 2;
+        constexpr int KW = KPP / 2;                     // x words per piece
+        for (int t0 = threadIdx.x; t0 < MT * PRP; t0 += XB * kPieceThreads) {
+            uint32_t xw[XB][KW];
+#pragma unroll
+            for (int i = 0; i < XB; ++i) {
+                const int t = t0 + i * kPieceThreads;
+                const int m = t / PRP, p = t - m * PRP;
+                const bool have = t < MT * PRP && m < a.M && p < PR;
+                const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)(have ? m : 0) * a.K +
+                                                                  (size_t)(have ? p : 0) * KPP);
+#pragma unroll
+                for (int w = 0; w < KW / 4; ++w) {
+                    const uint4 v = have ? src[w] : make_uint4(0, 0, 0, 0);
+                    xw[i][4 * w] = v.x; xw[i][4 * w + 1] = v.y; xw[i][4 * w + 2] = v.z; xw[i][4 * w + 3] = v.w;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < XB; ++i) {
+                const int t = t0 + i * kPieceThreads;
+                if (t >= MT * PRP) break;
+                const int m = t / PRP, p = t - m * PRP;
+                uint32_t q[NPP];
+                float X, Tc;
+                piece_operands<BITS>(xw[i], q, X, Tc);
+#pragma unroll
+                for (int c = 0; c < NCHP; ++c)
+                    xp[(m * NCHP + c) * PRP + p] = make_uint4(q[4 * c], q[4 * c + 1], q[4 * c + 2], q[4 * c + 3]);
+                if constexpr (BITS != 0) xc[m * PRP + p] = make_float2(X, Tc);
+            }
+        }
+        __syncthreads();
+    };
     auto load_x = [&]() __attribute__((always_inline)) {
-        if constexpr (XREG) {
+        if constexpr (XREG && BITS == 0) {
+            // dense operands are x itself: each lane loads its own
 #pragma unroll
             for (int j = 0; j < J; ++j)
 #pragma unroll
@@ -174,46 +214,31 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                                   xq[j][m], xX[j][m], xT[j][m]);
                 }
         } else {
-            // every wavefront of the workgroup stages, then all synchronize;
-            // XB tasks per thread have their loads in flight together
-            constexpr int XB = BITS == 0 ? 8 : 2;
-            constexpr int KW = KPP / 2;                 // x words per piece
-            for (int t0 = threadIdx.x; t0 < MT * PRP; t0 += XB * kPieceThreads) {
-                uint32_t xw[XB][KW];
+            stage_x();
+            if constexpr (XREG) {
+                // affine, registers: each lane copies its own operands
 #pragma unroll
-                for (int i = 0; i < XB; ++i) {
-                    const int t = t0 + i * kPieceThreads;
-                    const int m = t / PRP, p = t - m * PRP;
-                    const bool have = t < MT * PRP && m < a.M && p < PR;
-                    const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)(have ? m : 0) * a.K +
-                                                                      (size_t)(have ? p : 0) * KPP);
+                for (int j = 0; j < J; ++j)
 #pragma unroll
-                    for (int w = 0; w < KW / 4; ++w) {
-                        const uint4 v = have ? src[w] : make_uint4(0, 0, 0, 0);
-                        xw[i][4 * w] = v.x; xw[i][4 * w + 1] = v.y; xw[i][4 * w + 2] = v.z; xw[i][4 * w + 3] = v.w;
+                    for (int m = 0; m < MT; ++m) {
+                        const int p = li + P * j;
+#pragma unroll
+                        for (int c = 0; c < NCHP; ++c) {
+                            const uint4 v = xp[(m * NCHP + c) * PRP + p];
+                            xq[j][m][4 * c] = v.x; xq[j][m][4 * c + 1] = v.y;
+                            xq[j][m][4 * c + 2] = v.z; xq[j][m][4 * c + 3] = v.w;
+                        }
+                        const float2 v = xc[m * PRP + p];
+                        xX[j][m] = v.x;
+                        xT[j][m] = v.y;
                     }
-                }
-#pragma unroll
-                for (int i = 0; i < XB; ++i) {
-                    const int t = t0 + i * kPieceThreads;
-                    if (t >= MT * PRP) break;
-                    const int m = t / PRP, p = t - m * PRP;
-                    uint32_t q[NPP];
-                    float X, Tc;
-                    piece_operands<BITS>(xw[i], q, X, Tc);
-#pragma unroll
-                    for (int c = 0; c < NCHP; ++c)
-                        xp[(m * NCHP + c) * PRP + p] = make_uint4(q[4 * c], q[4 * c + 1], q[4 * c + 2], q[4 * c + 3]);
-                    if constexpr (BITS != 0) xc[m * PRP + p] = make_float2(X, Tc);
-                }
             }
-            __syncthreads();
         }
     };
 
     // ---- output staging: G*MT fp32 per finished tile, wavefront-private
     float* obuf = reinterpret_cast<float*>(
-                      XREG ? lds_p4
+                      (XREG && BITS == 0) ? lds_p4
                            : lds_p4 + (size_t)MT * NCHP * PRP + (BITS != 0 ? ((size_t)MT * PRP + 1) / 2 : 0))
                   + (size_t)wave * a.tmax * PER_TILE;
 
@@ -430,7 +455,8 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
     }
 }
 
-// LDS bytes of one workgroup: staged x (none when x is in registers) plus the
+// LDS bytes of one workgroup: staged x operands (none for dense x in
+// registers; affine operands are staged on the way to registers) plus the
 // output staging for `tmax` tiles per wavefront.
 template <int BITS>
 size_t piece_lds_bytes(int MT, bool xreg, int L, int J, int K, int64_t tmax)
@@ -438,7 +464,7 @@ size_t piece_lds_bytes(int MT, bool xreg, int L, int J, int K, int64_t tmax)
     (void)K;
     const int G = 64 >> L;
     const size_t out = (size_t)(kPieceThreads / 64) * tmax * G * MT * 4;
-    if (xreg) return out;
+    if (xreg && BITS == 0) return out;       // dense x goes straight to registers
     const size_t PRP = (size_t)J << L;
     const size_t x16 = (size_t)MT * (PieceGeo<BITS>::NPP / 4) * PRP + (BITS != 0 ? ((size_t)MT * PRP + 1) / 2 : 0);
     return x16 * 16 + out;
@@ -464,9 +490,21 @@ hipError_t launch_piece_one(const ProjArgs& a, hipStream_t s)
     constexpr int NW = kPieceThreads / 64;
     const int64_t T = ((int64_t)a.N + G - 1) / G;
     const int64_t row_bytes = BITS == 0 ? (int64_t)a.K * 2 : (int64_t)a.K * BITS / 8;
-    // super-tiles of ~8 KB of consecutive rows
+    // super-tiles of ~8 KB of consecutive rows, but no fewer super-tiles than
+    // wavefront slots (a small matrix is spread over all CUs, not batched
+    // onto a few wavefronts)
     int64_t ct = 8192 / (G * row_bytes);
     if (ct < 1) ct = 1;
+    {
+        int bpc = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &bpc, fn, kPieceThreads, piece_lds_bytes<BITS>(MT, XREG, L, J, a.K, (T + (int64_t)cus * NW - 1) / ((int64_t)cus * NW) + ct));
+        if (e != hipSuccess) return e;
+        if (bpc < 1) bpc = 1;
+        if (bpc * NW > piece_max_waves_per_cu<BITS>()) bpc = piece_max_waves_per_cu<BITS>() / NW;
+        const int64_t slots = (int64_t)bpc * cus * NW;
+        if (ct > 1 && T / ct < slots) ct = T / slots > 1 ? T / slots : 1;
+    }
     const int64_t st = (T + ct - 1) / ct;
     // Grid: the wavefront slots the device holds at once at this LDS size, at
     // most piece_max_waves_per_cu per CU (the output staging depends on the
