@@ -25,7 +25,7 @@ struct ProjArgs {
     int64_t tmax;            // stream path: most row tiles any wavefront finishes
 };
 
-enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4 };
+enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5 };
 
 // Launch geometry chosen for a call.
 struct LaunchCfg {
@@ -64,6 +64,11 @@ hipError_t launch_mfma(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 // Persistent dense / SwiGLU matrix-core launcher for large N (mfma_stream.hip).
 template <bool SWIGLU>
 hipError_t launch_mfma_stream(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+// Dense / SwiGLU matrix-core launcher for small N, k split over one
+// workgroup per 16-row tile (mfma_stream.hip).
+template <bool SWIGLU>
+hipError_t launch_mfma_split(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // bits: 0 = dense bf16, 2..8 = affine width.
 LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K);

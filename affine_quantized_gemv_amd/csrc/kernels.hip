@@ -3,7 +3,7 @@
 // streaming or tiled VALU kernels (proj_b*.hip); matrix-core kernels
 // (mfma_dense.hip) for dense and SwiGLU calls with M = 9..32, tiled VALU
 // kernels for affine M = 9..32; plus the code-unpack kernel.
-#include "mfma_stream.h"
+#include "mfma_split.h"
 #include "piece_kernel.h"
 #include "stream_kernel.h"
 
@@ -104,6 +104,24 @@ bool choose_mfma_stream(bool swiglu, int M, int N, int K, LaunchCfg& c)
     c.nwaves = detail::kMfmaStreamThreads / 64;
     c.R = 1;
     (void)swiglu;
+    return true;
+}
+
+// Small-N matrix-core geometry (M = 9..32, dense / SwiGLU): fewer than 2048
+// row tiles of 16 and K/32 k-steps that split evenly into pairs over at most
+// 16 wavefronts.  Depends on (N, K) only.
+bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)
+{
+    c = LaunchCfg{};
+    const int64_t T = ((int64_t)N + 15) / 16;
+    const int spw = detail::mfma_split_spw(K, swiglu);
+    if (T >= 2048 || spw == 0) return false;
+    c.path = PATH_MFMA_SPLIT;
+    c.MT = M <= 16 ? 16 : 32;
+    c.KT = K;
+    c.nwaves = (K / 32) / spw;
+    c.blocks = (int)T;
+    c.R = 1;
     return true;
 }
 
@@ -226,6 +244,7 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 {
     LaunchCfg c;
     if (bits == 0 && M > 8 && choose_mfma_stream(swiglu, M, N, K, c)) return c;
+    if (bits == 0 && M > 8 && choose_mfma_split(swiglu, M, N, K, c)) return c;
     if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
     if (choose_piece(bits, swiglu, M, N, K, c)) return c;
     if (choose_stream(bits, swiglu, M, N, K, c)) return c;
@@ -234,6 +253,10 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 
 hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
+    if (c.path == PATH_MFMA_SPLIT) {
+        if (bits != 0) return hipErrorInvalidValue;
+        return swiglu ? launch_mfma_split<true>(a, c, s) : launch_mfma_split<false>(a, c, s);
+    }
     if (c.path == PATH_MFMA_STREAM) {
         if (bits != 0) return hipErrorInvalidValue;
         return swiglu ? launch_mfma_stream<true>(a, c, s) : launch_mfma_stream<false>(a, c, s);

@@ -1,0 +1,185 @@
+// Matrix-core kernel for small-N dense projections and fused SwiGLU at
+// M = 9..32 (M padded to 16 or 32) on gfx950: one workgroup per 16-row tile,
+// K split over NKS wavefronts.
+//
+// A small matrix (a few MB) is latency-bound: what matters is how soon every
+// CU has its loads in flight.  Here nothing waits before the loads: each
+// wavefront issues, at once, the A operands of its SPW k-steps (whole-line
+// pair loads with the DPP half-swap, as in mfma_stream.h) and the x^T B
+// operands of the same k-steps straight from global memory (L2-resident; no
+// LDS staging, no barrier), then runs its MFMAs.  The NKS partial 16 x MT
+// tiles are summed through LDS in a fixed order (wavefront 0 + 1 + ...), so
+// results are deterministic and the same for every M of the path.
+//
+// Shapes and fused up/gate SwiGLU: AstrAI decode_linear_benchmark.md (commit
+// message; q/k/v/out, MLP shapes at M = 1..32).
+#pragma once
+#include "mfma_stream.h"
+
+namespace aqg {
+namespace detail {
+
+constexpr int kMfmaSplitMaxWaves = 16;
+
+template <int MT, bool SWIGLU, int SPW>
+__global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(ProjArgs a)
+{
+    extern __shared__ float lds_red[];
+    constexpr int NB = MT / 16;
+    constexpr int S = SWIGLU ? 2 : 1;
+    constexpr int NP = SPW / 2;                  // k-step pairs per wavefront
+    static_assert(SPW % 2 == 0, "k-steps come in pairs");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nks = blockDim.x >> 6;
+    const int c = lane >> 4;
+    const int r = lane & 15;
+    const int h = lane & 15;
+    const int64_t row_bytes = (int64_t)a.K * 2;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int s0 = wave * SPW;                   // first k-step of this wavefront
+
+    // A: pair p covers k-steps s0 + 2p, s0 + 2p + 1 (64 k, 128 bytes per row)
+    const uint32_t voff = (uint32_t)((h & 7) * row_bytes + 16 * ((h < 8 ? 0 : 4) + c));
+    const int half_off = (int)(8 * row_bytes);
+    u32x4_t wa[NP][S][2];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const __amdgpu_buffer_rsrc_t rs =
+            tile_rsrc(static_cast<const char*>(s == 0 ? a.w0 : a.w1) + n0 * row_bytes, (a.N - n0) * row_bytes);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int koff = 64 * (s0 + 2 * p);  // bytes: 32 k per step, 2 bytes each
+            wa[p][s][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, koff, kLoadNT));
+            wa[p][s][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, koff + half_off, kLoadNT));
+        }
+    }
+    // B: lane (c, column r) of block b holds x[16b + r][32 s + 8c .. + 7]
+    u32x4_t xb[SPW][NB];
+#pragma unroll
+    for (int t = 0; t < SPW; ++t)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int m = 16 * b + r;
+            xb[t][b] = u32x4_t{0u, 0u, 0u, 0u};
+            if (m < a.M)
+                xb[t][b] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)m * a.K + 32 * (s0 + t) + 8 * c);
+        }
+
+    const bool hi8 = (lane & 8) != 0;
+    f32x4_t acc[S][NB];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[s][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            u32x4_t A0, A1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t l0 = wa[p][s][0][i], l1 = wa[p][s][1][i];
+                const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l0, 0x128, 0xF, 0xF, false);
+                const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l1, 0x128, 0xF, 0xF, false);
+                A0[i] = hi8 ? r1 : l0;
+                A1[i] = hi8 ? l1 : r0;
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                acc[s][b] = mfma16x16x32(A0, xb[2 * p][b], acc[s][b]);
+                acc[s][b] = mfma16x16x32(A1, xb[2 * p + 1][b], acc[s][b]);
+            }
+        }
+
+    // fixed-order sum of the k-splits: every wavefront stores its partial,
+    // wavefront 0 adds them in order 0, 1, ..., nks-1 and stores the tile
+    constexpr int PER = S * NB * 4;              // floats per lane
+    if (wave != 0) {
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_red[((size_t)(wave * PER) + (s * NB + b) * 4 + i) * 64 + lane] = acc[s][b][i];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 1; w < nks; ++w)
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[s][b][i] += lds_red[((size_t)(w * PER) + (s * NB + b) * 4 + i) * 64 + lane];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int m = 16 * b + r;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t n = n0 + 4 * c + i;
+            if (n >= a.N) continue;
+            float v = acc[0][b][i];
+            if constexpr (SWIGLU) {
+                const float u = acc[1][b][i];
+                v = (v / (1.0f + __expf(-v))) * u;
+            }
+            const size_t o = (size_t)m * a.N + n;
+            if (a.out_f32) reinterpret_cast<float*>(a.y)[o] = v;
+            else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16_rne(v);
+        }
+    }
+}
+
+// k-steps per wavefront for a K: the smallest of 2, 4, 6, 8 that splits the
+// K/32 steps over at most 16 wavefronts (0 if none does; SwiGLU stops at 6,
+// where its two weight streams still fit in registers at M = 32).
+inline int mfma_split_spw(int K, bool swiglu)
+{
+    if (K % 64 != 0) return 0;
+    const int ks = K / 32;
+    for (int spw : {2, 4, 6, 8})
+        if (ks % spw == 0 && ks / spw <= kMfmaSplitMaxWaves) return (swiglu && spw > 6) ? 0 : spw;
+    return 0;
+}
+
+template <int MT, bool SW, int SPW>
+hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
+{
+    const int nks = (a.K / 32) / SPW;
+    const size_t lds = (size_t)nks * (SW ? 2 : 1) * (MT / 16) * 4 * 64 * 4;
+    const int64_t tiles = ((int64_t)a.N + 15) / 16;
+    hipLaunchKernelGGL((mfma_split_kernel<MT, SW, SPW>), dim3((unsigned)tiles), dim3(64 * nks), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int MT, bool SW>
+hipError_t launch_mfma_split_mt(const ProjArgs& a, hipStream_t s)
+{
+    switch (mfma_split_spw(a.K, SW)) {
+        case 2: return launch_mfma_split_one<MT, SW, 2>(a, s);
+        case 4: return launch_mfma_split_one<MT, SW, 4>(a, s);
+        case 6: return launch_mfma_split_one<MT, SW, 6>(a, s);
+        case 8:
+            if constexpr (!SW) return launch_mfma_split_one<MT, SW, 8>(a, s);
+            else return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool SW>
+hipError_t launch_mfma_split_impl(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+{
+    switch (c.MT) {
+        case 16: return launch_mfma_split_mt<16, SW>(a, s);
+        case 32: return launch_mfma_split_mt<32, SW>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace detail
+}  // namespace aqg
