@@ -221,7 +221,7 @@ bool choose_piece(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
     const int PRP = J << L;
     const int64_t T = ((int64_t)N + G - 1) / G;
     const int64_t row_bytes = (int64_t)PR * 16;
-    int64_t ct = 8192 / (G * row_bytes);
+    int64_t ct = (bits == 0 ? 8192 : 4096) / (G * row_bytes);
     if (ct < 1) ct = 1;
     // tiles per wavefront with any super-tile size up to ct and at least one
     // 4-wavefront workgroup per CU

@@ -72,12 +72,11 @@ template <> struct PieceGeo<0> {
 template <int BITS, int MT, int J>
 constexpr bool piece_xreg_ok() { return PieceGeo<BITS>::NPP * J * MT <= piece_xreg_budget<BITS>(); }
 
-// Row tiles in flight per wavefront (measured on the LM-head shapes): 2 when
-// a lane has one piece per row, and for affine codes with two; dense with
-// 2..3 pieces: 1 for M <= 4, 2 for M = 8 (fewer wavefronts fit, each needs
-// more in flight); 1 from 4 pieces.
+// Row tiles in flight per wavefront (measured on the LM-head shapes): 2 while
+// a lane has at most 3 pieces per row (1 for dense M <= 2, whose arithmetic
+// per row is short), 1 from 4 pieces.
 template <int BITS, int J, int MT> struct PieceDepth {
-    static constexpr int RD = J == 1 ? 2 : (J >= 4 ? 1 : ((MT >= 8 || (BITS != 0 && J == 2)) ? 2 : 1));
+    static constexpr int RD = J >= 4 ? 1 : ((BITS == 0 && MT <= 2) ? 1 : 2);
 };
 
 // x operands of one piece for one row m from its KPP x values (as bf16 pair
@@ -417,15 +416,28 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 
     // prologue: RD rows, unconditionally (tiles past the wavefront's share --
     // all of them for a wavefront with no tiles -- read as zero or as valid
-    // rows; they are never consumed), then x
-    static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
-    load_x();
+    // rows; they are never consumed), and x.  Dense x in registers is loaded
+    // first: the loop reads it, and a load issued after the weights would
+    // make every wait in the loop a wait for all loads in flight.  Staged
+    // operands end in a barrier that waits for everything anyway, so there
+    // the weights go first and their latency overlaps the staging.
+    if constexpr (XREG && BITS == 0) {
+        load_x();
+        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
+    } else {
+        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
+        load_x();
+    }
     if (my_tiles == 0) return;
     int64_t bt = 0;
     for (; bt + 2 * RD <= my_tiles; bt += RD) {          // steady state
         static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
             consume(Dd);
             fetch(Dd);
+            // keep this order: without the barrier the scheduler sinks the
+            // loads below the next slots' arithmetic, and each slot then waits
+            // for every load in flight (vmcnt(0)) instead of its own
+            __builtin_amdgcn_sched_barrier(0);
         });
     }
     for (; bt < my_tiles; bt += RD) {                   // drain
@@ -490,10 +502,10 @@ hipError_t launch_piece_one(const ProjArgs& a, hipStream_t s)
     constexpr int NW = kPieceThreads / 64;
     const int64_t T = ((int64_t)a.N + G - 1) / G;
     const int64_t row_bytes = BITS == 0 ? (int64_t)a.K * 2 : (int64_t)a.K * BITS / 8;
-    // super-tiles of ~8 KB of consecutive rows, but no fewer super-tiles than
-    // wavefront slots (a small matrix is spread over all CUs, not batched
-    // onto a few wavefronts)
-    int64_t ct = 8192 / (G * row_bytes);
+    // super-tiles of consecutive rows (sizes measured on the LM heads), but
+    // no fewer super-tiles than wavefront slots (a small matrix is spread
+    // over all CUs, not batched onto a few wavefronts)
+    int64_t ct = (BITS == 0 ? 8192 : 4096) / (G * row_bytes);    // ~8 KB dense, ~4 KB affine
     if (ct < 1) ct = 1;
     {
         int bpc = 0;
