@@ -25,7 +25,7 @@ struct ProjArgs {
     int64_t tmax;            // stream path: most row tiles any wavefront finishes
 };
 
-enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5 };
+enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6 };
 
 // Launch geometry chosen for a call.
 struct LaunchCfg {
@@ -69,6 +69,9 @@ hipError_t launch_mfma_stream(const ProjArgs& a, const LaunchCfg& c, hipStream_t
 // workgroup per 16-row tile (mfma_stream.hip).
 template <bool SWIGLU>
 hipError_t launch_mfma_split(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+// 4-bit affine matrix-core launcher for large N (affine_mfma.hip).
+hipError_t launch_affine4_mfma(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // bits: 0 = dense bf16, 2..8 = affine width.
 LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K);

@@ -3,6 +3,7 @@
 // streaming or tiled VALU kernels (proj_b*.hip); matrix-core kernels
 // (mfma_dense.hip) for dense and SwiGLU calls with M = 9..32, tiled VALU
 // kernels for affine M = 9..32; plus the code-unpack kernel.
+#include "affine_mfma.h"
 #include "mfma_split.h"
 #include "piece_kernel.h"
 #include "stream_kernel.h"
@@ -121,6 +122,24 @@ bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)
     c.KT = K;
     c.nwaves = (K / 32) / spw;
     c.blocks = (int)T;
+    c.R = 1;
+    return true;
+}
+
+// 4-bit affine matrix-core geometry (M = 9..32): K a multiple of 256, at
+// least 2048 row tiles of 16, and x^T plus the output staging fit in LDS at
+// M = 32 with one 8-wavefront workgroup per CU.  Depends on (N, K) only.
+bool choose_affine_mfma(int bits, int M, int N, int K, LaunchCfg& c)
+{
+    c = LaunchCfg{};
+    if (bits != 4 || K % 256 != 0) return false;
+    const int64_t T = ((int64_t)N + 15) / 16;
+    if (T < 2048) return false;
+    if (detail::affine_mfma_lds_bytes(32, K, (T + 2047) / 2048) > detail::kMfmaStreamLdsMax) return false;
+    c.path = PATH_AFFINE_MFMA;
+    c.MT = M <= 16 ? 16 : 32;
+    c.KT = K;
+    c.nwaves = detail::kAffineMfmaThreads / 64;
     c.R = 1;
     return true;
 }
@@ -245,6 +264,7 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     LaunchCfg c;
     if (bits == 0 && M > 8 && choose_mfma_stream(swiglu, M, N, K, c)) return c;
     if (bits == 0 && M > 8 && choose_mfma_split(swiglu, M, N, K, c)) return c;
+    if (!swiglu && M > 8 && choose_affine_mfma(bits, M, N, K, c)) return c;
     if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
     if (choose_piece(bits, swiglu, M, N, K, c)) return c;
     if (choose_stream(bits, swiglu, M, N, K, c)) return c;
@@ -253,6 +273,10 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 
 hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
+    if (c.path == PATH_AFFINE_MFMA) {
+        if (bits != 4 || swiglu) return hipErrorInvalidValue;
+        return launch_affine4_mfma(a, c, s);
+    }
     if (c.path == PATH_MFMA_SPLIT) {
         if (bits != 0) return hipErrorInvalidValue;
         return swiglu ? launch_mfma_split<true>(a, c, s) : launch_mfma_split<false>(a, c, s);

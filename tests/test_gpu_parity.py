@@ -407,6 +407,73 @@ def test_affine_one_hot_every_group_position_m8(bits, K):
         assert np.array_equal(y, codes[:, c].T.astype(np.float64)), "cols %s" % c
 
 
+@functools.lru_cache(maxsize=None)
+def affine4_large_n_case():
+    N, K = 40001, 1024
+    x = synth.normal_bf16((32, K), 1.0, 81, "a4l/x")
+    aw = synth.affine_weight(81, "a4l", 4, N, K)
+    return x, aw, bf16_dev(x), u32_dev(aw.words), bf16_dev(aw.scales), bf16_dev(aw.biases)
+
+
+@pytest.mark.parametrize("M", [9, 16, 17, 32])
+def test_affine4_large_n_matrix_core(M):
+    """4-bit, N = 40001 (>= 2048 row tiles of 16, last one ragged), M = 9..32:
+    the matrix-core path, within tolerance, and bit for bit equal to the first
+    rows of the M = 32 call."""
+    x, aw, xd, wq, sd, bd = affine4_large_n_case()
+    N, K = aw.scales.shape[0], x.shape[1]
+    y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, 4, M), M, N)
+    ref, A = oracle.gemv_affine(x[:M], aw.words, aw.scales, aw.biases, 4)
+    assert_within(y, ref, oracle.tolerance(A), "q4 %dx%dx%d" % (M, N, K))
+    y32 = aqg.gemv_affine(xd[:32], wq, sd, bd, 4, out_dtype=torch.float32).cpu().numpy()
+    yM = aqg.gemv_affine(xd[:M], wq, sd, bd, 4, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(yM, y32[:M])
+
+
+@functools.lru_cache(maxsize=None)
+def affine4_multi_tile_case():
+    N, K = 131072, 1024
+    x = synth.normal_bf16((32, K), 1.0, 83, "a4m/x")
+    aw = synth.affine_weight(83, "a4m", 4, N, K)
+    return x, aw, bf16_dev(x), u32_dev(aw.words), bf16_dev(aw.scales), bf16_dev(aw.biases)
+
+
+@pytest.mark.parametrize("M", [12, 16, 32])
+def test_affine4_matrix_core_several_tiles_per_wavefront(M):
+    """4-bit, N = 131072 (8192 row tiles): each wavefront of the persistent
+    matrix-core launch owns two to four tiles, so most k-blocks go through the
+    pipelined steady-state loop.  Sampled tiles from the start, the middle and
+    the end against the oracle, and y(M) equal to the first rows of y(32)."""
+    x, aw, xd, wq, sd, bd = affine4_multi_tile_case()
+    y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, 4, M), M, aw.scales.shape[0])
+    tiles = [0, 1, 2, 2047, 2048, 2049, 4095, 4096, 6143, 6144, 8190, 8191]
+    rows = np.concatenate([np.arange(16 * t, 16 * t + 16) for t in tiles])
+    ref, A = oracle.gemv_affine(x[:M], aw.words[rows], aw.scales[rows], aw.biases[rows], 4)
+    assert_within(y[:, rows], ref, oracle.tolerance(A), "q4 %dx131072x1024 sampled tiles" % M)
+    y32 = aqg.gemv_affine(xd[:32], wq, sd, bd, 4, out_dtype=torch.float32).cpu().numpy()
+    yM = aqg.gemv_affine(xd[:M], wq, sd, bd, 4, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(yM, y32[:M])
+
+
+def test_affine4_large_n_one_hot_every_group_position_m16():
+    """Matrix-core path, s = 1, bias = 0, one-hot x: y = q exactly for all 64
+    positions of a group (each in a different group), 16 columns per call."""
+    N, K = 33000, 1024
+    words = synth.random_words((N, K // 8), 82, "oh16")
+    codes = oracle.unpack(words, 4, K)
+    G = K // 64
+    cols = np.array([((r * 7 + 1) % G) * 64 + r for r in range(64)])
+    ones = np.full((N, G), 0x3F80, np.uint16)
+    zeros = np.zeros((N, G), np.uint16)
+    wq, sd, bd = u32_dev(words), bf16_dev(ones), bf16_dev(zeros)
+    for c0 in range(0, 64, 16):
+        c = cols[c0:c0 + 16]
+        x = np.zeros((16, K), np.uint16)
+        x[np.arange(16), c] = 0x3F80
+        y = run_guarded(gemv_affine_gpu(bf16_dev(x), wq, sd, bd, 4, 16), 16, N)
+        assert np.array_equal(y, codes[:, c].T.astype(np.float64)), "cols %s" % c
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_affine_small_integers_exact(bits):
     M, N, K = 3, 5, 192
