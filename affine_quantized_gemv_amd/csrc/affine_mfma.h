@@ -1,4 +1,4 @@
-// Matrix-core kernel for 4-bit affine GEMVs at M = 9..32 (M padded to 16 or
+// Matrix-core kernel for 4-bit affine GEMVs at M = 3..32 (M padded to 16 or
 // 32) on gfx950, for large N: persistent over 16-row tiles like
 // mfma_stream.h.
 //
@@ -20,9 +20,15 @@
 //     dword c of piece t, codes 8c .. 8c + 7 of that k-step;
 //   * each dword becomes four bf16 pairs (codes (0,4), (1,5), (2,6), (3,7)),
 //     and x^T is staged in LDS in the same order, so the products pair up;
-//   * two k-steps (one group) accumulate into a fresh 16 x 16 tile; the
-//     group's scale and bias (one bf16 load per lane per k-block, shared with
-//     ds_bpermute) and X (staged per (group, row of x) in LDS) finish it.
+//   * two k-steps (one group) accumulate into a fresh 16 x 16 tile, which the
+//     group's scale (from a small wavefront-private LDS table filled from one
+//     bf16 load per lane per k-block) adds into the tile's sum in fp32;
+//   * the bias and the 128 offset of the codes do not depend on the codes:
+//     over the whole tile they are sum_g bias_g X_g - 128 sum_g scale_g X_g,
+//     two small contractions over the groups that the matrix core also does
+//     at the end of each tile (A = the tile's biases or scales, bf16, staged
+//     per row in LDS; B = the group sums X split into bf16 high and low parts,
+//     X - hi(X) being exact in bf16 to within 2^-16 of X).
 // Codes of one group never mix with another group's in an MFMA, and each
 // output is the same chain of MFMAs and fp32 operations for every M.
 //
@@ -59,13 +65,20 @@ __device__ __forceinline__ u32x4_t codes4_to_bf16(uint32_t w, uint32_t m, uint32
     return u32x4_t{(w & m) | c, ((w >> 4) & m) | c, ((w >> 8) & m) | c, ((w >> 12) & m) | c};
 }
 
-template <int MT, int D>
+// LDS bytes private to one wavefront: the k-block's scales (bf16, 4 x 16)
+// and the tile's bias and scale tables (bf16, 16 rows x 32-group multiples).
+__host__ __device__ inline size_t affine_mfma_wave_bytes(int K)
+{
+    const int gps = ((K / 64 + 31) / 32) * 32;
+    return 256 + (size_t)2 * 16 * gps * 2;
+}
+
+template <int MT, int D, int KSG>
 __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjArgs a)
 {
     extern __shared__ u32x4_t lds_a4[];
     constexpr int NB = MT / 16;
     constexpr int NW = kAffineMfmaThreads / 64;
-    constexpr int PER_TILE = 16 * MT;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -74,6 +87,9 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
     const int KS = a.K / 32;             // k-steps per row
     const int KBL = a.K / 256;           // 128-byte k-blocks per row (4 groups each)
     const int gpr = a.K / 64;
+    // KSG: 32-group steps of the bias contractions (ceil(gpr / 32), a
+    // template parameter so that the tile-end code has no loop of its own)
+    constexpr int GPS = KSG * 32;        // groups per row in the bias tables (zero past gpr)
     const int64_t row_bytes = (int64_t)a.K / 2;
     const int64_t T = ((int64_t)a.N + 15) / 16;
     const int64_t CT = a.tpw;
@@ -87,12 +103,21 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
         if ((ST - 1 - wg) % W == 0) my_tiles -= ST * CT - T;
     }
 
-    u32x4_t* xb = lds_a4;                                                     // [s][b][lane]
-    float* xs = reinterpret_cast<float*>(lds_a4 + (size_t)KS * NB * 64);      // [group][m] sums of x
-    float* obuf = xs + (size_t)gpr * MT + (size_t)wave * a.tmax * PER_TILE;
+    // LDS: x^T fragments [s][b][lane]; X hi/lo fragments [ks][b][2][lane];
+    // group sums [g][m] (prologue only); then per wavefront: scales of the
+    // k-block in use [group][row], bias and scale tables [row][GPS] (all
+    // bf16).
+    u32x4_t* xb = lds_a4;
+    u32x4_t* xh = xb + (size_t)KS * NB * 64;
+    float* xs = reinterpret_cast<float*>(xh + (size_t)KSG * NB * 2 * 64);
+    char* wbase = reinterpret_cast<char*>(xs + (size_t)gpr * MT) +
+                  (size_t)wave * affine_mfma_wave_bytes(a.K);
+    uint16_t* sbuf = reinterpret_cast<uint16_t*>(wbase);                        // [4][16] bf16
+    uint16_t* btab = reinterpret_cast<uint16_t*>(wbase + 256);                  // [16][GPS]
+    uint16_t* stab = btab + 16 * GPS;                                           // [16][GPS]
 
     // ---- ring of D k-blocks: two whole-line loads + one scale and one bias
-    // per lane (lane (c, r): row 4c + r/4, group r%4 of the k-block)
+    // per lane (lane l: row l/4, group l%4 of the k-block)
     u32x4_t wa[D][2];
     uint32_t sw[D], bw[D];
     int64_t f_tile = wg * CT;
@@ -101,7 +126,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
     const int h = lane & 15;
     const uint32_t voff = (uint32_t)((h & 7) * row_bytes + 16 * ((h < 8 ? 0 : 4) + c));
     const int half_off = (int)(8 * row_bytes);
-    const uint32_t goff = (uint32_t)(((4 * c + (r >> 2)) * gpr + (r & 3)) * 2);
+    const uint32_t goff = (uint32_t)(((lane >> 2) * gpr + (lane & 3)) * 2);
     auto fetch = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
         const int64_t n0 = f_tile * 16;
@@ -120,11 +145,12 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
         f_tile += wrap ? (stw ? (W - 1) * CT + 1 : 1) : 0;
     };
 
-    f32x4_t acc[NB];
+    f32x4_t acc[NB], accb[NB], accs[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b) acc[b] = accb[b] = accs[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     int c_b = 0;
-    int ti = 0;
+    int64_t c_tile = wg * CT;            // tile being consumed
+    int c_c = 0;                         // its index within the super-tile
     const bool hi8 = (lane & 8) != 0;
     uint32_t cmask = 0x000F000Fu, cbias = 0x43004300u;
     asm volatile("" : "+s"(cmask));      // no instruction: only hides the constants
@@ -132,6 +158,16 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
 
     auto consume = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
+        // the k-block's scales and biases into the wavefront's tables (LDS
+        // operations of one wavefront take effect in program order)
+        {
+            // raw 16-bit values straight from the loads: arithmetic on them
+            // here would be hoisted into the loop latch and wait there
+            sbuf[(lane & 3) * 16 + (lane >> 2)] = (uint16_t)sw[d];
+            const int ti2 = (lane >> 2) * GPS + 4 * c_b + (lane & 3);
+            btab[ti2] = (uint16_t)bw[d];
+            stab[ti2] = (uint16_t)sw[d];
+        }
         // pieces: s[0] = pieces 0..3 of row j in lane-row g, s[1] = pieces 4..7
         uint32_t pc[2][4];
 #pragma unroll
@@ -146,42 +182,66 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
         transpose4x4_rows(pc[1]);        // pc[1][t]: k-step 4 + t
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
-            // scale and bias of rows 4c + i, group gi, from lane (c, 4i + gi)
-            float sc[4], bm[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int src = (16 * c + 4 * i + gi) * 4;
-                sc[i] = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sw[d]) << 16);
-                const float bi = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)bw[d]) << 16);
-                bm[i] = bi - 128.0f * sc[i];
-            }
+            // scales of rows 4c .. 4c + 3, group gi
+            const uint2 s4 = *reinterpret_cast<const uint2*>(sbuf + gi * 16 + 4 * c);
+            const float sc[4] = {__uint_as_float(s4.x << 16), __uint_as_float(s4.x & 0xFFFF0000u),
+                                 __uint_as_float(s4.y << 16), __uint_as_float(s4.y & 0xFFFF0000u)};
             const u32x4_t A0 = codes4_to_bf16(pc[gi >> 1][2 * (gi & 1)], cmask, cbias);
             const u32x4_t A1 = codes4_to_bf16(pc[gi >> 1][2 * (gi & 1) + 1], cmask, cbias);
             const int S0 = 8 * c_b + 2 * gi;
-            const int g = 4 * c_b + gi;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 f32x4_t dg = mfma16x16x32(A0, xb[(S0 * NB + b) * 64 + lane], f32x4_t{0.f, 0.f, 0.f, 0.f});
                 dg = mfma16x16x32(A1, xb[((S0 + 1) * NB + b) * 64 + lane], dg);
-                const float X = xs[g * MT + 16 * b + r];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(sc[i], dg[i], fmaf(bm[i], X, acc[b][i]));
+                for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(sc[i], dg[i], acc[b][i]);
             }
         }
         if (++c_b == KBL) {
+            // end of the tile: bias and code-offset terms, then stage
             c_b = 0;
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int ks = 0; ks < KSG; ++ks) {
+                const u32x4_t Ab = *reinterpret_cast<const u32x4_t*>(btab + r * GPS + 32 * ks + 8 * c);
+                const u32x4_t As = *reinterpret_cast<const u32x4_t*>(stab + r * GPS + 32 * ks + 8 * c);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) obuf[ti * PER_TILE + (4 * c + i) * MT + 16 * b + r] = acc[b][i];
+                for (int b = 0; b < NB; ++b) {
+                    const u32x4_t Xh = xh[((ks * NB + b) * 2 + 0) * 64 + lane];
+                    const u32x4_t Xl = xh[((ks * NB + b) * 2 + 1) * 64 + lane];
+                    accb[b] = mfma16x16x32(Ab, Xh, accb[b]);
+                    accb[b] = mfma16x16x32(Ab, Xl, accb[b]);
+                    accs[b] = mfma16x16x32(As, Xh, accs[b]);
+                    accs[b] = mfma16x16x32(As, Xl, accs[b]);
+                }
+            }
+            // lane (c, r) holds rows 4c .. 4c + 3 of column 16b + r: store
+            // them now (no staging: either way consecutive lanes write
+            // different rows of y)
+            const int64_t n0 = c_tile * 16 + 4 * c;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            ++ti;
+            for (int b = 0; b < NB; ++b) {
+                const int m = 16 * b + r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = fmaf(-128.0f, accs[b][i], acc[b][i] + accb[b][i]);
+                    if (m < a.M && n0 + i < a.N) {
+                        const size_t o = (size_t)m * a.N + (size_t)(n0 + i);
+                        if (a.out_f32) reinterpret_cast<float*>(a.y)[o] = v;
+                        else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16_rne(v);
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[b] = accb[b] = accs[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // next tile of this wavefront
+            ++c_c;
+            if (c_c == CT) { c_c = 0; c_tile += (W - 1) * CT + 1; } else { ++c_tile; }
         }
     };
 
-    // prologue: D k-blocks, then stage x^T (pair order within each 8-k chunk)
-    // and the per-(group, row) sums X
+    // prologue: D k-blocks, then stage x^T (pair order within each 8-k chunk),
+    // the group sums X, their bf16 high/low fragments, and clear the bias
+    // tables (groups past gpr stay zero)
     static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
     {
         constexpr int XB = 4;
@@ -228,7 +288,38 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
             }
             xs[t] = sum;
         }
+        for (int t = lane; t < 2 * 16 * GPS / 2; t += 64)          // both tables, as 32-bit words
+            reinterpret_cast<uint32_t*>(btab)[t] = 0u;
     }
+    __syncthreads();
+    for (int t = threadIdx.x; t < KSG * NB * 64; t += kAffineMfmaThreads) {
+        // X fragment: lane (c, col) of block b holds groups 32ks + 8c .. + 7 of column 16b + col
+        const int l = t & 63;
+        const int kb = t >> 6;
+        const int ks = kb / NB, b = kb - ks * NB;
+        const int m = 16 * b + (l & 15);
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t hh[2], ll[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int g = 32 * ks + 8 * (l >> 4) + 2 * j + e;
+                const float X = g < gpr ? xs[g * MT + m] : 0.0f;
+                const uint16_t hb = f32_to_bf16_rne(X);
+                hh[e] = hb;
+                ll[e] = f32_to_bf16_rne(X - bf16_to_f32(hb));
+            }
+            hw[j] = hh[0] | (hh[1] << 16);
+            lw[j] = ll[0] | (ll[1] << 16);
+        }
+        xh[(kb * 2 + 0) * 64 + l] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+        xh[(kb * 2 + 1) * 64 + l] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+    }
+    // Every load issued so far is complete (the x loads came after the
+    // weights and loads complete in order); saying so keeps a possibly
+    // pending staging load out of the loop's waits.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (my_tiles == 0) return;
 
@@ -251,33 +342,25 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
         });
     }
 
-    for (int v = lane; v < ti * PER_TILE; v += 64) {
-        const int t2 = v / PER_TILE;
-        const int rem = v % PER_TILE;
-        const int m = rem % MT;
-        const int64_t tile = (wg + (int64_t)(t2 / CT) * W) * CT + t2 % CT;
-        const int64_t n = tile * 16 + rem / MT;
-        if (m < a.M && n < a.N) {
-            const float val = obuf[v];
-            const size_t o = (size_t)m * a.N + n;
-            if (a.out_f32) reinterpret_cast<float*>(a.y)[o] = val;
-            else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16_rne(val);
-        }
-    }
 }
 
-constexpr int kAffineMfmaDepth = 3;
+// k-blocks in flight per wavefront and workgroups per CU: on the 151936 x
+// 1024 LM head at M = 16, depth 4 with 2 workgroups (16 wavefronts) per CU
+// measured fastest (3 workgroups, i.e. more bytes in flight, ~20% slower).
+constexpr int kAffineMfmaDepth = 4;
+constexpr int kAffineMfmaWgPerCu = 2;
 
-inline size_t affine_mfma_lds_bytes(int MT, int K, int64_t tmax)
+inline size_t affine_mfma_lds_bytes(int MT, int K)
 {
-    return (size_t)(K / 32) * (MT / 16) * 64 * 16 + (size_t)(K / 64) * MT * 4 +
-           (size_t)(kAffineMfmaThreads / 64) * tmax * 16 * MT * 4;
+    const int gpr = K / 64, ksg = (gpr + 31) / 32;
+    return (size_t)(K / 32) * (MT / 16) * 64 * 16 + (size_t)ksg * (MT / 16) * 2 * 64 * 16 + (size_t)gpr * MT * 4 +
+           (size_t)(kAffineMfmaThreads / 64) * affine_mfma_wave_bytes(K);
 }
 
-template <int MT>
+template <int MT, int KSG>
 hipError_t launch_affine_mfma_one(const ProjArgs& a, hipStream_t s)
 {
-    const void* fn = reinterpret_cast<const void*>(&affine4_mfma_kernel<MT, kAffineMfmaDepth>);
+    const void* fn = reinterpret_cast<const void*>(&affine4_mfma_kernel<MT, kAffineMfmaDepth, KSG>);
     {
         static std::atomic<int> raised{0};
         if (!raised.load(std::memory_order_acquire)) {
@@ -291,40 +374,29 @@ hipError_t launch_affine_mfma_one(const ProjArgs& a, hipStream_t s)
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     constexpr int NW = kAffineMfmaThreads / 64;
-    const int64_t T = ((int64_t)a.N + 15) / 16;
-    int64_t waves = T, tmax = 0;
-    size_t lds = 0;
-    for (int round = 0; round < 3; ++round) {
-        tmax = (T + waves - 1) / waves;
-        lds = affine_mfma_lds_bytes(MT, a.K, tmax);
-        if (lds > kMfmaStreamLdsMax) return hipErrorInvalidValue;
-        int bpc = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, kAffineMfmaThreads, lds);
-        if (e != hipSuccess) return e;
-        if (bpc < 1) bpc = 1;
-        int64_t w = (int64_t)bpc * cus * NW;
-        if (w > T) w = T;
-        if (w == waves && round > 0) break;
-        waves = w;
-    }
-    const int blocks = (int)((waves + NW - 1) / NW);
-    tmax = (T + (int64_t)blocks * NW - 1) / ((int64_t)blocks * NW);
-    lds = affine_mfma_lds_bytes(MT, a.K, tmax);
+    const size_t lds = affine_mfma_lds_bytes(MT, a.K);
     if (lds > kMfmaStreamLdsMax) return hipErrorInvalidValue;
+    int bpc = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, kAffineMfmaThreads, lds);
+    if (e != hipSuccess) return e;
+    if (bpc < 1) bpc = 1;
+    if (bpc > kAffineMfmaWgPerCu) bpc = kAffineMfmaWgPerCu;
+    const int64_t T = ((int64_t)a.N + 15) / 16;
+    int64_t waves = (int64_t)bpc * cus * NW;
+    if (waves > T) waves = T;
+    const int blocks = (int)((waves + NW - 1) / NW);
     ProjArgs a2 = a;
     a2.tpw = 1;
-    a2.tmax = tmax;
-    hipLaunchKernelGGL((affine4_mfma_kernel<MT, kAffineMfmaDepth>), dim3(blocks), dim3(kAffineMfmaThreads), lds, s, a2);
+    hipLaunchKernelGGL((affine4_mfma_kernel<MT, kAffineMfmaDepth, KSG>), dim3(blocks), dim3(kAffineMfmaThreads), lds, s, a2);
     return hipGetLastError();
 }
 
 inline hipError_t launch_affine_mfma_impl(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
-    switch (c.MT) {
-        case 16: return launch_affine_mfma_one<16>(a, s);
-        case 32: return launch_affine_mfma_one<32>(a, s);
-        default: return hipErrorInvalidValue;
-    }
+    const int ksg = (a.K / 64 + 31) / 32;
+    if (ksg == 1) return c.MT == 16 ? launch_affine_mfma_one<16, 1>(a, s) : launch_affine_mfma_one<32, 1>(a, s);
+    if (ksg == 2) return c.MT == 16 ? launch_affine_mfma_one<16, 2>(a, s) : launch_affine_mfma_one<32, 2>(a, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace detail

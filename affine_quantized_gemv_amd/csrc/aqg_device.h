@@ -9,6 +9,10 @@ namespace aqg {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their
+// maximum, i.e. not waited for): gfx9-family encoding.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // (a & m) | c -- one v_and_or_b32.  Written as asm because, with m and c
 // compile-time constants, the compiler would otherwise emit v_and_b32 +
 // v_or_b32 with literal operands (a 3-operand VALU op cannot take literals

@@ -126,18 +126,21 @@ bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)
     return true;
 }
 
-// 4-bit affine matrix-core geometry (M = 9..32): K a multiple of 256, at
-// least 2048 row tiles of 16, and x^T plus the output staging fit in LDS at
-// M = 32 with one 8-wavefront workgroup per CU.  Depends on (N, K) only.
+// 4-bit affine matrix-core geometry (M = 3..32): K a multiple of 256 and at
+// most 4096 (at most two 32-group steps in the bias contractions), at least
+// 2048 row tiles of 16, and the workgroup's LDS (x^T, the group sums and the
+// wavefronts' scale and bias tables) within a CU's.  Depends on (N, K) and
+// on whether M fits 16 columns.
 bool choose_affine_mfma(int bits, int M, int N, int K, LaunchCfg& c)
 {
     c = LaunchCfg{};
-    if (bits != 4 || K % 256 != 0) return false;
+    if (bits != 4 || K % 256 != 0 || K > 4096) return false;
     const int64_t T = ((int64_t)N + 15) / 16;
     if (T < 2048) return false;
-    if (detail::affine_mfma_lds_bytes(32, K, (T + 2047) / 2048) > detail::kMfmaStreamLdsMax) return false;
+    const int MT = M <= 16 ? 16 : 32;
+    if (detail::affine_mfma_lds_bytes(MT, K) > detail::kMfmaStreamLdsMax) return false;
     c.path = PATH_AFFINE_MFMA;
-    c.MT = M <= 16 ? 16 : 32;
+    c.MT = MT;
     c.KT = K;
     c.nwaves = detail::kAffineMfmaThreads / 64;
     c.R = 1;
@@ -264,7 +267,10 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     LaunchCfg c;
     if (bits == 0 && M > 8 && choose_mfma_stream(swiglu, M, N, K, c)) return c;
     if (bits == 0 && M > 8 && choose_mfma_split(swiglu, M, N, K, c)) return c;
-    if (!swiglu && M > 8 && choose_affine_mfma(bits, M, N, K, c)) return c;
+    // 4-bit, M >= 3: the matrix core's cost does not grow with M (up to 16),
+    // the dot-product kernels' does (measured on the 151936 x 1024 LM head:
+    // 27.5 us at any M <= 16 against 32 us for the piece kernel at M = 4)
+    if (!swiglu && M >= 3 && choose_affine_mfma(bits, M, N, K, c)) return c;
     if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
     if (choose_piece(bits, swiglu, M, N, K, c)) return c;
     if (choose_stream(bits, swiglu, M, N, K, c)) return c;

@@ -415,9 +415,9 @@ def affine4_large_n_case():
     return x, aw, bf16_dev(x), u32_dev(aw.words), bf16_dev(aw.scales), bf16_dev(aw.biases)
 
 
-@pytest.mark.parametrize("M", [9, 16, 17, 32])
+@pytest.mark.parametrize("M", [3, 4, 8, 9, 16, 17, 32])
 def test_affine4_large_n_matrix_core(M):
-    """4-bit, N = 40001 (>= 2048 row tiles of 16, last one ragged), M = 9..32:
+    """4-bit, N = 40001 (>= 2048 row tiles of 16, last one ragged), M = 3..32:
     the matrix-core path, within tolerance, and bit for bit equal to the first
     rows of the M = 32 call."""
     x, aw, xd, wq, sd, bd = affine4_large_n_case()
@@ -438,7 +438,7 @@ def affine4_multi_tile_case():
     return x, aw, bf16_dev(x), u32_dev(aw.words), bf16_dev(aw.scales), bf16_dev(aw.biases)
 
 
-@pytest.mark.parametrize("M", [12, 16, 32])
+@pytest.mark.parametrize("M", [4, 12, 16, 32])
 def test_affine4_matrix_core_several_tiles_per_wavefront(M):
     """4-bit, N = 131072 (8192 row tiles): each wavefront of the persistent
     matrix-core launch owns two to four tiles, so most k-blocks go through the
