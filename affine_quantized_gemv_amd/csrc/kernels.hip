@@ -127,21 +127,38 @@ bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)
 }
 
 // 4-bit affine matrix-core geometry (M = 3..32): K a multiple of 256 and at
-// most 4096 (at most two 32-group steps in the bias contractions), at least
-// 2048 row tiles of 16, and the workgroup's LDS (x^T, the group sums and the
-// wavefronts' scale and bias tables) within a CU's.  Depends on (N, K) and
-// on whether M fits 16 columns.
+// most 4096.  With fewer than 2048 row tiles of 16 the workgroup's wavefronts
+// split K (2, 4 or 8 chunks, each at least one 256-k block) so that small
+// matrices still spread over the chip; the workgroup's LDS (x^T, the X
+// fragments, the wavefronts' tables and, with a split, the partial tiles)
+// must fit a CU's.  Depends on (N, K) and on whether M fits 16 columns.
 bool choose_affine_mfma(int bits, int M, int N, int K, LaunchCfg& c)
 {
     c = LaunchCfg{};
     if (bits != 4 || K % 256 != 0 || K > 4096) return false;
     const int64_t T = ((int64_t)N + 15) / 16;
-    if (T < 2048) return false;
     const int MT = M <= 16 ? 16 : 32;
-    if (detail::affine_mfma_lds_bytes(MT, K) > detail::kMfmaStreamLdsMax) return false;
+    const int kbl = K / 256;
+    int cus = 256, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    // smallest split that gives ~2048 work items, then more chunks while the
+    // LDS does not fit (smaller chunks need smaller bias tables)
+    auto fits = [&](int n) {
+        if (detail::affine_mfma_gps(K, n) == 0) return false;
+        int blocks = 0;
+        int64_t tmax = 0;
+        detail::affine_mfma_geometry(T, n, cus, 1, blocks, tmax);   // most tiles per slot (one workgroup per CU)
+        return detail::affine_mfma_lds_bytes(MT, K, n, tmax) <= detail::kMfmaStreamLdsMax;
+    };
+    int nkc = 1;
+    while (nkc < 8 && 2 * nkc <= kbl && T * nkc < 2048) nkc *= 2;
+    while (!fits(nkc) && nkc > 1 && nkc < 8 && 2 * nkc <= kbl) nkc *= 2;
+    if (!fits(nkc)) return false;
     c.path = PATH_AFFINE_MFMA;
     c.MT = MT;
     c.KT = K;
+    c.ksplit_log2 = nkc == 1 ? 0 : nkc == 2 ? 1 : nkc == 4 ? 2 : 3;
     c.nwaves = detail::kAffineMfmaThreads / 64;
     c.R = 1;
     return true;
@@ -270,7 +287,9 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     // 4-bit, M >= 3: the matrix core's cost does not grow with M (up to 16),
     // the dot-product kernels' does (measured on the 151936 x 1024 LM head:
     // 27.5 us at any M <= 16 against 32 us for the piece kernel at M = 4)
-    if (!swiglu && M >= 3 && choose_affine_mfma(bits, M, N, K, c)) return c;
+    // (with a K split, i.e. few row tiles, from M = 9 on: below that the
+    // piece kernel's shorter prologue wins)
+    if (!swiglu && M >= 3 && choose_affine_mfma(bits, M, N, K, c) && (c.ksplit_log2 == 0 || M > 8)) return c;
     if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
     if (choose_piece(bits, swiglu, M, N, K, c)) return c;
     if (choose_stream(bits, swiglu, M, N, K, c)) return c;

@@ -474,6 +474,51 @@ def test_affine4_large_n_one_hot_every_group_position_m16():
         assert np.array_equal(y, codes[:, c].T.astype(np.float64)), "cols %s" % c
 
 
+@pytest.mark.parametrize("N,K", [(1000, 1792), (3000, 512), (700, 3584), (2000, 256), (1024, 1024)])
+def test_affine4_matrix_core_k_split(N, K):
+    """4-bit, fewer than 2048 row tiles: the matrix-core path splits K over a
+    workgroup's wavefronts (chunks of unequal length when the 256-k blocks do
+    not divide evenly) and sums the partial tiles in chunk order.  Ragged N;
+    M = 9 and 16 against the oracle and bit for bit against each other, M = 32
+    as well where its x^T fits, and M = 3 (dot-product path) within
+    tolerance."""
+    x = synth.normal_bf16((32, K), 1.0, 84, "a4k/x/%d/%d" % (N, K))
+    aw = synth.affine_weight(84, "a4k/%d/%d" % (N, K), 4, N, K)
+    xd, wq, sd, bd = bf16_dev(x), u32_dev(aw.words), bf16_dev(aw.scales), bf16_dev(aw.biases)
+    ref, A = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, 4)
+    y16 = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, 4, 16), 16, N)
+    assert_within(y16, ref[:16], oracle.tolerance(A[:16]), "q4 16x%dx%d" % (N, K))
+    y9 = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, 4, 9), 9, N)
+    assert_within(y9, ref[:9], oracle.tolerance(A[:9]), "q4 9x%dx%d" % (N, K))
+    assert np.array_equal(y9, y16[:9])
+    y3 = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, 4, 3), 3, N)
+    assert_within(y3, ref[:3], oracle.tolerance(A[:3]), "q4 3x%dx%d" % (N, K))
+    if K <= 1024:
+        y32 = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, 4, 32), 32, N)
+        assert_within(y32, ref, oracle.tolerance(A), "q4 32x%dx%d" % (N, K))
+        assert np.array_equal(y16, y32[:16])
+
+
+def test_affine4_k_split_one_hot_every_group_position_m16():
+    """K split (1000 x 1792: 7 blocks of 256 k in 4 chunks), s = 1, bias = 0,
+    one-hot x: y = q exactly at every position of a group, whichever chunk
+    holds it (the other chunks add exact zeros)."""
+    N, K = 1000, 1792
+    words = synth.random_words((N, K // 8), 85, "oh16k")
+    codes = oracle.unpack(words, 4, K)
+    G = K // 64
+    cols = np.array([((r * 5 + 3) % G) * 64 + r for r in range(64)])
+    ones = np.full((N, G), 0x3F80, np.uint16)
+    zeros = np.zeros((N, G), np.uint16)
+    wq, sd, bd = u32_dev(words), bf16_dev(ones), bf16_dev(zeros)
+    for c0 in range(0, 64, 16):
+        c = cols[c0:c0 + 16]
+        x = np.zeros((16, K), np.uint16)
+        x[np.arange(16), c] = 0x3F80
+        y = run_guarded(gemv_affine_gpu(bf16_dev(x), wq, sd, bd, 4, 16), 16, N)
+        assert np.array_equal(y, codes[:, c].T.astype(np.float64)), "cols %s" % c
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_affine_small_integers_exact(bits):
     M, N, K = 3, 5, 192
@@ -525,7 +570,9 @@ def test_affine_ragged_shapes(M, N, K, bits):
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_affine_rows_independent_of_m(bits):
     """M <= 8 (streaming path, x in registers or LDS) matches one-row calls bit
-    for bit; M = 9..32 (tiled path) matches the 32-row call bit for bit."""
+    for bit; M = 9..16 and M = 17..32 match the 16- and 32-row calls bit for
+    bit (the two buckets may take different paths: 16 columns of x^T fit in
+    LDS where 32 do not)."""
     name, N, K = synth.MIXED_SHAPES[0]
     x, aw, xd, wq, sd, bd = affine_case(synth.CFG_MIXED_WIDTH, name, bits, N, K)
     y1 = torch.cat([aqg.gemv_affine(xd[m:m + 1], wq, sd, bd, bits, out_dtype=torch.float32)
@@ -533,7 +580,11 @@ def test_affine_rows_independent_of_m(bits):
     for M in (2, 3, 4, 7, 8):
         yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
         assert np.array_equal(yM, y1[:M]), "M=%d" % M
+    y16 = aqg.gemv_affine(xd[:16], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
+    for M in (9, 12):
+        yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
+        assert np.array_equal(yM, y16[:M]), "M=%d" % M
     y32 = aqg.gemv_affine(xd[:32], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
-    for M in (9, 16, 20):
+    for M in (17, 20):
         yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
         assert np.array_equal(yM, y32[:M]), "M=%d" % M
