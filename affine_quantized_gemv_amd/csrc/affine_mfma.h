@@ -1,36 +1,40 @@
-// Matrix-core kernel for 4-bit affine GEMVs at M = 3..32 (M padded to 16 or
-// 32) on gfx950, for large N: persistent over 16-row tiles like
-// mfma_stream.h.
+// Matrix-core kernel for affine GEMVs with 2-, 4- and 8-bit codes at M up
+// to 32 (M padded to 16 or 32) on gfx950: persistent over 16-row tiles like
+// mfma_stream.h, with the K range split over a workgroup's wavefronts when
+// there are few tiles.
 //
 // y^T[N, M] = W[N, K] . x^T[K, M] with W = scale * q + bias per 64-code
 // group.  The A operand of v_mfma_f32_16x16x32_bf16 is built from the codes
 // themselves: a field placed in a bf16 mantissa with 0x4300 gives exactly
-// 128 + q (mask placement, no lookup), so one group's MFMA result is
-// D = sum_k (128 + q_k) x_k, and the group contributes
-// scale * D + (bias - 128 * scale) * X with X = sum_k x_k -- the exact
-// factored form of sum_k x_k (scale * q_k + bias), in fp32.
+// 128 + q (mask placement, no lookup); 8-bit codes go in as two nibbles, the
+// high one in a second MFMA chain weighted 16 in fp32.  So one group's result
+// is D = sum_k (C + q_k) x_k with C = 128 (2176 for 8 bits), and the group
+// contributes scale * D + (bias - C * scale) * X with X = sum_k x_k -- the
+// exact factored form of sum_k x_k (scale * q_k + bias), in fp32.
 //
-// Operand flow per 128-byte k-block of the tile's 16 rows (256 codes per row):
+// Operand flow per 128-byte k-block of the tile's 16 rows:
 //   * two buffer loads cover rows 0..7 and 8..15 with whole 128-byte lines,
 //     and a row_ror:8 DPP select gives each lane one 16-byte piece of its
-//     row (as in mfma_stream.h): lane (g, j) holds piece g (then 4 + g) of
-//     row j, i.e. 32 codes of one half-group;
+//     row (as in mfma_stream.h);
 //   * a 4 x 4 transpose across the four 16-lane rows (v_permlane32_swap then
-//     v_permlane16_swap) turns piece t into MFMA k-step t: lane (c, j) gets
-//     dword c of piece t, codes 8c .. 8c + 7 of that k-step;
-//   * each dword becomes four bf16 pairs (codes (0,4), (1,5), (2,6), (3,7)),
-//     and x^T is staged in LDS in the same order, so the products pair up;
-//   * two k-steps (one group) accumulate into a fresh 16 x 16 tile, which the
-//     group's scale (from a small wavefront-private LDS table filled from one
-//     bf16 load per lane per k-block) adds into the tile's sum in fp32;
-//   * the bias and the 128 offset of the codes do not depend on the codes:
-//     over the whole tile they are sum_g bias_g X_g - 128 sum_g scale_g X_g,
-//     two small contractions over the groups that the matrix core also does
-//     at the end of each tile (A = the tile's biases or scales, bf16, staged
-//     per row in LDS; B = the group sums X split into bf16 high and low parts,
-//     X - hi(X) being exact in bf16 to within 2^-16 of X).
+//     v_permlane16_swap) leaves lane (c, r) with dword c of each of the
+//     block's 8 pieces of row r;
+//   * a group's 64 codes are 16 per lane (one dword at 2 bits, two at 4,
+//     four at 8 bits); they become the A operands of two k-steps, and x^T is
+//     staged in LDS with the matching k order, so the products pair up (the
+//     k order inside a group is free: it only has to agree on both sides);
+//   * the two k-steps of a group accumulate into a fresh 16 x 16 tile, which
+//     the group's scale (from a small wavefront-private LDS table filled from
+//     the scale loads) adds into the tile's sum in fp32;
+//   * the bias and the code offset do not depend on the codes: over the tile
+//     they are sum_g bias_g X_g - C sum_g scale_g X_g, two small contractions
+//     over the groups that the matrix core also does at the end of each tile
+//     (A = the tile's biases or scales, bf16, staged per row in LDS; B = the
+//     group sums X split into bf16 high and low parts, X - hi(X) being exact
+//     in bf16 to within 2^-16 of X).
 // Codes of one group never mix with another group's in an MFMA, and each
-// output is the same chain of MFMAs and fp32 operations for every M.
+// output is the same chain of MFMAs and fp32 operations for every M of a
+// 16-column bucket.
 //
 // Format: TensorFold PR #849, "qwen3_5 cuda: mixed-width MLX checkpoints, 2
 // to 8 bits in groups of 64" (MLX affine mode, groups of 64).
@@ -65,13 +69,73 @@ __device__ __forceinline__ u32x4_t codes4_to_bf16(uint32_t w, uint32_t m, uint32
     return u32x4_t{(w & m) | c, ((w >> 4) & m) | c, ((w >> 8) & m) | c, ((w >> 12) & m) | c};
 }
 
-// Groups per row of a K-chunk's tables: the chunk's groups (K/256 k-blocks
-// split into nkc chunks of at most ceil(K/256 / nkc) blocks, 4 groups each)
-// rounded up to 8, 16, 32 or 64.
-inline int affine_mfma_gps(int K, int nkc)
+// Sixteen 2-bit codes (code i at bits 2i) -> bf16 pairs (q_i, q_{i+8}) for
+// i = 4h .. 4h + 3 (h = 0, 1): the A operands of the group's two k-steps.
+// m = 0x00030003 and c = 0x43004300 as opaque registers.
+__device__ __forceinline__ u32x4_t codes2_to_bf16(uint32_t w, int h, uint32_t m, uint32_t c)
 {
-    const int g = 4 * ((K / 256 + nkc - 1) / nkc);
+    const uint32_t v = w >> (8 * h);
+    return u32x4_t{(v & m) | c, ((v >> 2) & m) | c, ((v >> 4) & m) | c, ((v >> 6) & m) | c};
+}
+
+// Eight 8-bit codes, a0..a3 in dword a and b0..b3 in dword b (byte i = code
+// i), as two nibble operands in the order (a0, a2), (a1, a3), (b0, b2),
+// (b1, b3): lo holds 128 + the low nibbles, hi 128 + the high nibbles.
+__device__ __forceinline__ void codes8_to_bf16(uint32_t a, uint32_t b, uint32_t m, uint32_t c, u32x4_t& lo, u32x4_t& hi)
+{
+    lo = u32x4_t{(a & m) | c, ((a >> 8) & m) | c, (b & m) | c, ((b >> 8) & m) | c};
+    hi = u32x4_t{((a >> 4) & m) | c, ((a >> 12) & m) | c, ((b >> 4) & m) | c, ((b >> 12) & m) | c};
+}
+
+// Per-width geometry: groups per 128-byte k-block of a row, the code offset C
+// of the A operands, and the field mask.
+template <int BITS> struct AffineMma;
+template <> struct AffineMma<2> { static constexpr int GPK = 8; static constexpr float OFF = 128.0f; static constexpr uint32_t MASK = 0x00030003u; };
+template <> struct AffineMma<4> { static constexpr int GPK = 4; static constexpr float OFF = 128.0f; static constexpr uint32_t MASK = 0x000F000Fu; };
+template <> struct AffineMma<8> { static constexpr int GPK = 2; static constexpr float OFF = 2176.0f; static constexpr uint32_t MASK = 0x000F000Fu; };
+
+// k-blocks (128 bytes) per row.
+inline int affine_mfma_kbl(int K, int bits) { return K * bits / 1024; }
+
+// Groups per row of a K-chunk's tables: the chunk's groups (the row's
+// k-blocks split into nkc chunks of at most ceil(kbl / nkc) blocks) rounded
+// up to 8, 16, 32 or 64.
+inline int affine_mfma_gps(int K, int bits, int nkc)
+{
+    const int kbl = affine_mfma_kbl(K, bits);
+    const int g = (16 / bits) * ((kbl + nkc - 1) / nkc);
     return g <= 8 ? 8 : g <= 16 ? 16 : g <= 32 ? 32 : g <= 64 ? 64 : 0;
+}
+
+// Staged x^T operand of k-step S (group S / 2, half S % 2) for lane quarter
+// c, in the k order of that width's A operands, from row xr of x; also the
+// sum of its 8 values.
+template <int BITS>
+__device__ __forceinline__ u32x4_t stage_x_operand(const uint16_t* xr, int S, int c, float& sum)
+{
+    const int base = 64 * (S >> 1), t = S & 1;
+    uint32_t o[4];
+    if constexpr (BITS == 4) {
+        // x at 32t + 8c + {0,4,1,5,2,6,3,7}
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + base + 32 * t + 8 * c);
+        o[0] = (v.x & 0xFFFFu) | (v.z << 16); o[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
+        o[2] = (v.y & 0xFFFFu) | (v.w << 16); o[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
+    } else if constexpr (BITS == 2) {
+        // x at 16c + 4t + {0,8,1,9,2,10,3,11}
+        const uint2 p = *reinterpret_cast<const uint2*>(xr + base + 16 * c + 4 * t);
+        const uint2 q = *reinterpret_cast<const uint2*>(xr + base + 16 * c + 4 * t + 8);
+        o[0] = (p.x & 0xFFFFu) | (q.x << 16); o[1] = (p.x >> 16) | (q.x & 0xFFFF0000u);
+        o[2] = (p.y & 0xFFFFu) | (q.y << 16); o[3] = (p.y >> 16) | (q.y & 0xFFFF0000u);
+    } else {
+        // x at 32t + 4c + {0,2,1,3, 16,18,17,19}
+        const uint2 p = *reinterpret_cast<const uint2*>(xr + base + 32 * t + 4 * c);
+        const uint2 q = *reinterpret_cast<const uint2*>(xr + base + 32 * t + 4 * c + 16);
+        o[0] = (p.x & 0xFFFFu) | (p.y << 16); o[1] = (p.x >> 16) | (p.y & 0xFFFF0000u);
+        o[2] = (q.x & 0xFFFFu) | (q.y << 16); o[3] = (q.x >> 16) | (q.y & 0xFFFF0000u);
+    }
+    sum = ((bf16_to_f32(o[0] & 0xFFFFu) + bf16_to_f32(o[0] >> 16)) + (bf16_to_f32(o[1] & 0xFFFFu) + bf16_to_f32(o[1] >> 16))) +
+          ((bf16_to_f32(o[2] & 0xFFFFu) + bf16_to_f32(o[2] >> 16)) + (bf16_to_f32(o[3] & 0xFFFFu) + bf16_to_f32(o[3] >> 16)));
+    return u32x4_t{o[0], o[1], o[2], o[3]};
 }
 
 // LDS bytes private to one wavefront: the k-block's scales (bf16, 4 x 16)
@@ -81,13 +145,14 @@ __host__ __device__ inline size_t affine_mfma_wave_bytes(int gps)
     return 256 + (size_t)2 * 16 * gps * 2;
 }
 
-template <int MT, int D, int GPS>
-__global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjArgs a)
+template <int BITS, int MT, int D, int GPS>
+__global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArgs a)
 {
     extern __shared__ u32x4_t lds_a4[];
     constexpr int NB = MT / 16;
     constexpr int NW = kAffineMfmaThreads / 64;
     constexpr int PER_TILE = 16 * MT;
+    constexpr int GPK = AffineMma<BITS>::GPK;   // groups per 128-byte k-block
     // GPS: groups per row in a chunk's tables (zero past the chunk's end);
     // the bias contractions take 32 groups per step (KSG steps) and only the
     // first LV lanes of their operands can be non-zero
@@ -99,9 +164,9 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
     const int c = lane >> 4;
     const int r = lane & 15;
     const int KS = a.K / 32;             // k-steps per row
-    const int KBL = a.K / 256;           // 128-byte k-blocks per row (4 groups each)
+    const int KBL = a.K * BITS / 1024;   // 128-byte k-blocks per row (GPK groups each)
     const int gpr = a.K / 64;
-    const int64_t row_bytes = (int64_t)a.K / 2;
+    const int64_t row_bytes = (int64_t)a.K * BITS / 8;
     const int64_t T = ((int64_t)a.N + 15) / 16;
 
     // K split: wavefront w of a workgroup takes chunk j = w % nkc of the
@@ -131,8 +196,10 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
     uint16_t* stab = btab + 16 * GPS;                                           // [16][GPS]
     float* pbuf = reinterpret_cast<float*>(wbase0 + (size_t)NW * affine_mfma_wave_bytes(GPS));
 
-    // ---- ring of D k-blocks: two whole-line loads + one scale and one bias
-    // per lane (lane l: row l/4, group l%4 of the k-block)
+    // ---- ring of D k-blocks: two whole-line loads + the block's scales and
+    // biases (lane l: 4 bits: row l/4, group l%4; 2 bits: row l/4, groups
+    // 2(l%4) and 2(l%4) + 1 in one 32-bit load; 8 bits: row (l/2)%16, group
+    // l%2)
     u32x4_t wa[D][2];
     uint32_t sw[D], bw[D];
     int64_t f_tile = u;
@@ -140,7 +207,9 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
     const int h = lane & 15;
     const uint32_t voff = (uint32_t)((h & 7) * row_bytes + 16 * ((h < 8 ? 0 : 4) + c));
     const int half_off = (int)(8 * row_bytes);
-    const uint32_t goff = (uint32_t)(((lane >> 2) * gpr + (lane & 3)) * 2);
+    const uint32_t goff = BITS == 4 ? (uint32_t)(((lane >> 2) * gpr + (lane & 3)) * 2)
+                        : BITS == 2 ? (uint32_t)(((lane >> 2) * gpr + 2 * (lane & 3)) * 2)
+                                    : (uint32_t)((((lane >> 1) & 15) * gpr + (lane & 1)) * 2);
     auto fetch = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
         const int64_t n0 = f_tile * 16;
@@ -148,8 +217,13 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
         const __amdgpu_buffer_rsrc_t rw = tile_rsrc(static_cast<const char*>(a.w0) + n0 * row_bytes, rows * row_bytes);
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(a.scales + n0 * gpr, rows * gpr * 2);
         const __amdgpu_buffer_rsrc_t rb = tile_rsrc(a.biases + n0 * gpr, rows * gpr * 2);
-        sw[d] = __builtin_amdgcn_raw_buffer_load_b16(rs, goff, 8 * f_b, kLoadNT);
-        bw[d] = __builtin_amdgcn_raw_buffer_load_b16(rb, goff, 8 * f_b, kLoadNT);
+        if constexpr (BITS == 2) {
+            sw[d] = __builtin_amdgcn_raw_buffer_load_b32(rs, goff, 2 * GPK * f_b, kLoadNT);
+            bw[d] = __builtin_amdgcn_raw_buffer_load_b32(rb, goff, 2 * GPK * f_b, kLoadNT);
+        } else {
+            sw[d] = __builtin_amdgcn_raw_buffer_load_b16(rs, goff, 2 * GPK * f_b, kLoadNT);
+            bw[d] = __builtin_amdgcn_raw_buffer_load_b16(rb, goff, 2 * GPK * f_b, kLoadNT);
+        }
         wa[d][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, 128 * f_b, kLoadNT));
         wa[d][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, 128 * f_b + half_off, kLoadNT));
         const bool wrap = f_b + 1 == kb_hi;
@@ -164,7 +238,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
     int64_t c_tile = u;                  // its tile
     int ti = 0;                          // tiles finished (K split: partials staged)
     const bool hi8 = (lane & 8) != 0;
-    uint32_t cmask = 0x000F000Fu, cbias = 0x43004300u;
+    uint32_t cmask = AffineMma<BITS>::MASK, cbias = 0x43004300u;
     asm volatile("" : "+s"(cmask));      // no instruction: only hides the constants
     asm volatile("" : "+v"(cbias));
     const u32x4_t* xhj = xh + (size_t)j * KSG * NB * 2 * LV;
@@ -174,12 +248,27 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
         // the k-block's scales and biases into the wavefront's tables (LDS
         // operations of one wavefront take effect in program order)
         {
-            // raw 16-bit values straight from the loads: arithmetic on them
-            // here would be hoisted into the loop latch and wait there
-            sbuf[(lane & 3) * 16 + (lane >> 2)] = (uint16_t)sw[d];
-            const int ti2 = (lane >> 2) * GPS + 4 * (c_b - kb_lo) + (lane & 3);
-            btab[ti2] = (uint16_t)bw[d];
-            stab[ti2] = (uint16_t)sw[d];
+            // raw values straight from the loads: arithmetic on them here
+            // would be hoisted into the loop latch and wait there
+            const int rel = GPK * (c_b - kb_lo);
+            if constexpr (BITS == 4) {
+                sbuf[(lane & 3) * 16 + (lane >> 2)] = (uint16_t)sw[d];
+                const int ti2 = (lane >> 2) * GPS + rel + (lane & 3);
+                btab[ti2] = (uint16_t)bw[d];
+                stab[ti2] = (uint16_t)sw[d];
+            } else if constexpr (BITS == 2) {
+                sbuf[(2 * (lane & 3)) * 16 + (lane >> 2)] = (uint16_t)sw[d];
+                sbuf[(2 * (lane & 3) + 1) * 16 + (lane >> 2)] = (uint16_t)(sw[d] >> 16);
+                const int ti2 = ((lane >> 2) * GPS + rel + 2 * (lane & 3)) >> 1;   // even group: one 32-bit word
+                reinterpret_cast<uint32_t*>(btab)[ti2] = bw[d];
+                reinterpret_cast<uint32_t*>(stab)[ti2] = sw[d];
+            } else {
+                // lanes 32..63 repeat lanes 0..31 (same values, same places)
+                sbuf[(lane & 1) * 16 + ((lane >> 1) & 15)] = (uint16_t)sw[d];
+                const int ti2 = ((lane >> 1) & 15) * GPS + rel + (lane & 1);
+                btab[ti2] = (uint16_t)bw[d];
+                stab[ti2] = (uint16_t)sw[d];
+            }
         }
         // pieces: s[0] = pieces 0..3 of row j in lane-row g, s[1] = pieces 4..7
         uint32_t pc[2][4];
@@ -194,18 +283,35 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
         transpose4x4_rows(pc[0]);        // pc[0][t]: codes of k-step t of the block
         transpose4x4_rows(pc[1]);        // pc[1][t]: k-step 4 + t
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
+        for (int gi = 0; gi < GPK; ++gi) {
             // scales of rows 4c .. 4c + 3, group gi
             const uint2 s4 = *reinterpret_cast<const uint2*>(sbuf + gi * 16 + 4 * c);
             const float sc[4] = {__uint_as_float(s4.x << 16), __uint_as_float(s4.x & 0xFFFF0000u),
                                  __uint_as_float(s4.y << 16), __uint_as_float(s4.y & 0xFFFF0000u)};
-            const u32x4_t A0 = codes4_to_bf16(pc[gi >> 1][2 * (gi & 1)], cmask, cbias);
-            const u32x4_t A1 = codes4_to_bf16(pc[gi >> 1][2 * (gi & 1) + 1], cmask, cbias);
-            const int S0 = 8 * c_b + 2 * gi;
+            // the group's 16 codes of this lane as the A operands of its two k-steps
+            u32x4_t A0, A1, H0, H1;
+            if constexpr (BITS == 4) {
+                A0 = codes4_to_bf16(pc[gi >> 1][2 * (gi & 1)], cmask, cbias);
+                A1 = codes4_to_bf16(pc[gi >> 1][2 * (gi & 1) + 1], cmask, cbias);
+            } else if constexpr (BITS == 2) {
+                A0 = codes2_to_bf16(pc[gi >> 2][gi & 3], 0, cmask, cbias);
+                A1 = codes2_to_bf16(pc[gi >> 2][gi & 3], 1, cmask, cbias);
+            } else {
+                codes8_to_bf16(pc[gi][0], pc[gi][1], cmask, cbias, A0, H0);
+                codes8_to_bf16(pc[gi][2], pc[gi][3], cmask, cbias, A1, H1);
+            }
+            const int S0 = 2 * (GPK * c_b + gi);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                f32x4_t dg = mfma16x16x32(A0, xb[(S0 * NB + b) * 64 + lane], f32x4_t{0.f, 0.f, 0.f, 0.f});
-                dg = mfma16x16x32(A1, xb[((S0 + 1) * NB + b) * 64 + lane], dg);
+                const u32x4_t B0 = xb[(S0 * NB + b) * 64 + lane], B1 = xb[((S0 + 1) * NB + b) * 64 + lane];
+                f32x4_t dg = mfma16x16x32(A0, B0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                dg = mfma16x16x32(A1, B1, dg);
+                if constexpr (BITS == 8) {
+                    f32x4_t dh = mfma16x16x32(H0, B0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    dh = mfma16x16x32(H1, B1, dh);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dg[i] = fmaf(16.0f, dh[i], dg[i]);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(sc[i], dg[i], acc[b][i]);
             }
@@ -239,7 +345,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
                     const int m = 16 * b + r;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float v = fmaf(-128.0f, accs[b][i], acc[b][i] + accb[b][i]);
+                        const float v = fmaf(-AffineMma<BITS>::OFF, accs[b][i], acc[b][i] + accb[b][i]);
                         if (m < a.M && n0 + i < a.N) {
                             const size_t o = (size_t)m * a.N + (size_t)(n0 + i);
                             if (a.out_f32) reinterpret_cast<float*>(a.y)[o] = v;
@@ -253,7 +359,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        pt[(4 * c + i) * MT + 16 * b + r] = fmaf(-128.0f, accs[b][i], acc[b][i] + accb[b][i]);
+                        pt[(4 * c + i) * MT + 16 * b + r] = fmaf(-AffineMma<BITS>::OFF, accs[b][i], acc[b][i] + accb[b][i]);
             }
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[b] = accb[b] = accs[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -272,37 +378,34 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
         const int ntask = KS * NB * 64;
         for (int t0 = threadIdx.x; t0 < ntask; t0 += XB * kAffineMfmaThreads) {
             u32x4_t v[XB];
+            float p8[XB];
 #pragma unroll
             for (int i = 0; i < XB; ++i) {
                 const int t = t0 + i * kAffineMfmaThreads;
                 const int l = t & 63;
                 const int sb = t >> 6;
-                const int s = sb / NB, b = sb - s * NB;
+                const int S = sb / NB, b = sb - S * NB;
                 const int m = 16 * b + (l & 15);
                 v[i] = u32x4_t{0u, 0u, 0u, 0u};
-                if (t < ntask && m < a.M)
-                    v[i] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)m * a.K + 32 * s + 8 * (l >> 4));
+                p8[i] = 0.0f;
+                if (t < ntask && m < a.M) v[i] = stage_x_operand<BITS>(a.x + (size_t)m * a.K, S, l >> 4, p8[i]);
             }
 #pragma unroll
             for (int i = 0; i < XB; ++i) {
                 const int t = t0 + i * kAffineMfmaThreads;
                 if (t < ntask) {
-                    // x words (x0|x1), (x2|x3), (x4|x5), (x6|x7) -> (x0|x4), (x1|x5), (x2|x6), (x3|x7)
-                    const uint32_t w0 = v[i][0], w1 = v[i][1], w2 = v[i][2], w3 = v[i][3];
-                    xb[t] = u32x4_t{(w0 & 0xFFFFu) | (w2 << 16), (w0 >> 16) | (w2 & 0xFFFF0000u),
-                                    (w1 & 0xFFFFu) | (w3 << 16), (w1 >> 16) | (w3 & 0xFFFF0000u)};
+                    xb[t] = v[i];
                     // sum of the k-step's 32 x of column m: this lane's 8,
                     // then across the four quarters (lanes 16 apart; the whole
                     // wavefront is here: ntask is a multiple of 64)
                     const int l = t & 63;
                     const int sb = t >> 6;
-                    const int s = sb / NB, b = sb - s * NB;
+                    const int S = sb / NB, b = sb - S * NB;
                     const int m = 16 * b + (l & 15);
-                    float p8 = ((bf16_to_f32(w0 & 0xFFFFu) + bf16_to_f32(w0 >> 16)) + (bf16_to_f32(w1 & 0xFFFFu) + bf16_to_f32(w1 >> 16))) +
-                               ((bf16_to_f32(w2 & 0xFFFFu) + bf16_to_f32(w2 >> 16)) + (bf16_to_f32(w3 & 0xFFFFu) + bf16_to_f32(w3 >> 16)));
-                    p8 += __shfl_xor(p8, 16);
-                    p8 += __shfl_xor(p8, 32);
-                    if (l < 16) xs[s * MT + m] = p8;
+                    float q = p8[i];
+                    q += __shfl_xor(q, 16);
+                    q += __shfl_xor(q, 32);
+                    if (l < 16) xs[S * MT + m] = q;
                 }
             }
         }
@@ -319,7 +422,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine4_mfma_kernel(ProjAr
         const int rem = kb - jj * (KSG * NB);
         const int ks = rem / NB, b = rem - ks * NB;
         const int m = 16 * b + (l & 15);
-        const int g_lo = 4 * (jj * KBL / nkc), g_hi = 4 * ((jj + 1) * KBL / nkc);
+        const int g_lo = GPK * (jj * KBL / nkc), g_hi = GPK * ((jj + 1) * KBL / nkc);
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -396,9 +499,9 @@ constexpr int kAffineMfmaWgPerCu = 2;
 
 // LDS bytes of one workgroup with nkc K-chunks per tile and, for nkc > 1,
 // tmax tiles per slot staged as partials.
-inline size_t affine_mfma_lds_bytes(int MT, int K, int nkc, int64_t tmax)
+inline size_t affine_mfma_lds_bytes(int MT, int K, int bits, int nkc, int64_t tmax)
 {
-    const int gps = affine_mfma_gps(K, nkc);
+    const int gps = affine_mfma_gps(K, bits, nkc);
     const int ksg = (gps + 31) / 32, lv = gps * 2 < 64 ? gps * 2 : 64;
     const int nw = kAffineMfmaThreads / 64;
     size_t b = (size_t)(K / 32) * (MT / 16) * 64 * 16 + (size_t)nkc * ksg * (MT / 16) * 2 * lv * 16 +
@@ -418,10 +521,10 @@ inline void affine_mfma_geometry(int64_t T, int nkc, int cus, int bpc, int& bloc
     tmax = (T + (int64_t)blocks * ts - 1) / ((int64_t)blocks * ts);
 }
 
-template <int MT, int GPS>
+template <int BITS, int MT, int GPS>
 hipError_t launch_affine_mfma_one(const ProjArgs& a, int nkc, hipStream_t s)
 {
-    const void* fn = reinterpret_cast<const void*>(&affine4_mfma_kernel<MT, kAffineMfmaDepth, GPS>);
+    const void* fn = reinterpret_cast<const void*>(&affine_mfma_kernel<BITS, MT, kAffineMfmaDepth, GPS>);
     {
         static std::atomic<int> raised{0};
         if (!raised.load(std::memory_order_acquire)) {
@@ -440,7 +543,7 @@ hipError_t launch_affine_mfma_one(const ProjArgs& a, int nkc, hipStream_t s)
     size_t lds = 0;
     for (;;) {
         affine_mfma_geometry(T, nkc, cus, bpc, blocks, tmax);
-        lds = affine_mfma_lds_bytes(MT, a.K, nkc, tmax);
+        lds = affine_mfma_lds_bytes(MT, a.K, BITS, nkc, tmax);
         if (lds > kMfmaStreamLdsMax) return hipErrorInvalidValue;
         int occ = 0;
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAffineMfmaThreads, lds);
@@ -454,20 +557,22 @@ hipError_t launch_affine_mfma_one(const ProjArgs& a, int nkc, hipStream_t s)
     int lk = 0;
     while ((1 << lk) < nkc) ++lk;
     a2.ksplit_log2 = lk;
-    hipLaunchKernelGGL((affine4_mfma_kernel<MT, kAffineMfmaDepth, GPS>), dim3(blocks), dim3(kAffineMfmaThreads), lds, s, a2);
+    hipLaunchKernelGGL((affine_mfma_kernel<BITS, MT, kAffineMfmaDepth, GPS>), dim3(blocks), dim3(kAffineMfmaThreads), lds, s, a2);
     return hipGetLastError();
 }
 
-inline hipError_t launch_affine_mfma_impl(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+template <int BITS>
+hipError_t launch_affine_mfma_impl(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
     const int nkc = 1 << c.ksplit_log2;
-    if (nkc > kAffineMfmaThreads / 64 || nkc > a.K / 256) return hipErrorInvalidValue;   // every chunk >= 1 k-block
+    // every chunk at least one k-block
+    if (nkc > kAffineMfmaThreads / 64 || nkc > affine_mfma_kbl(a.K, BITS)) return hipErrorInvalidValue;
     const bool w = c.MT == 16;
-    switch (affine_mfma_gps(a.K, nkc)) {
-        case 8: return w ? launch_affine_mfma_one<16, 8>(a, nkc, s) : launch_affine_mfma_one<32, 8>(a, nkc, s);
-        case 16: return w ? launch_affine_mfma_one<16, 16>(a, nkc, s) : launch_affine_mfma_one<32, 16>(a, nkc, s);
-        case 32: return w ? launch_affine_mfma_one<16, 32>(a, nkc, s) : launch_affine_mfma_one<32, 32>(a, nkc, s);
-        case 64: return w ? launch_affine_mfma_one<16, 64>(a, nkc, s) : launch_affine_mfma_one<32, 64>(a, nkc, s);
+    switch (affine_mfma_gps(a.K, BITS, nkc)) {
+        case 8: return w ? launch_affine_mfma_one<BITS, 16, 8>(a, nkc, s) : launch_affine_mfma_one<BITS, 32, 8>(a, nkc, s);
+        case 16: return w ? launch_affine_mfma_one<BITS, 16, 16>(a, nkc, s) : launch_affine_mfma_one<BITS, 32, 16>(a, nkc, s);
+        case 32: return w ? launch_affine_mfma_one<BITS, 16, 32>(a, nkc, s) : launch_affine_mfma_one<BITS, 32, 32>(a, nkc, s);
+        case 64: return w ? launch_affine_mfma_one<BITS, 16, 64>(a, nkc, s) : launch_affine_mfma_one<BITS, 32, 64>(a, nkc, s);
         default: return hipErrorInvalidValue;
     }
 }

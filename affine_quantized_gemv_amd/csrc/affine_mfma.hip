@@ -1,9 +1,11 @@
-// Instantiation of the 4-bit affine matrix-core kernels (M padded to 16 or 32).
+// Instantiation of the affine matrix-core kernels for 4-bit codes (M padded
+// to 16 or 32; every chunk-table size).
 #include "affine_mfma.h"
 
 namespace aqg {
-hipError_t launch_affine4_mfma(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+template <>
+hipError_t launch_affine_mfma<4>(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
-    return detail::launch_affine_mfma_impl(a, c, s);
+    return detail::launch_affine_mfma_impl<4>(a, c, s);
 }
 }  // namespace aqg

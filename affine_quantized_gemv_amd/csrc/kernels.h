@@ -70,8 +70,9 @@ hipError_t launch_mfma_stream(const ProjArgs& a, const LaunchCfg& c, hipStream_t
 template <bool SWIGLU>
 hipError_t launch_mfma_split(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
-// 4-bit affine matrix-core launcher for large N (affine_mfma.hip).
-hipError_t launch_affine4_mfma(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+// Affine matrix-core launcher, BITS = 2, 4 or 8 (affine_mfma*.hip).
+template <int BITS>
+hipError_t launch_affine_mfma(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // bits: 0 = dense bf16, 2..8 = affine width.
 LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K);

@@ -126,30 +126,31 @@ bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)
     return true;
 }
 
-// 4-bit affine matrix-core geometry (M = 3..32): K a multiple of 256 and at
-// most 4096.  With fewer than 2048 row tiles of 16 the workgroup's wavefronts
-// split K (2, 4 or 8 chunks, each at least one 256-k block) so that small
-// matrices still spread over the chip; the workgroup's LDS (x^T, the X
-// fragments, the wavefronts' tables and, with a split, the partial tiles)
-// must fit a CU's.  Depends on (N, K) and on whether M fits 16 columns.
+// Affine matrix-core geometry (2-, 4- and 8-bit codes): whole 128-byte
+// k-blocks per row (K a multiple of 1024/bits) and K at most 4096.  With fewer
+// than 2048 row tiles of 16 the workgroup's wavefronts split K (2, 4 or 8
+// chunks, each at least one k-block) so that small matrices still spread over
+// the chip; the workgroup's LDS (x^T, the X fragments, the wavefronts' tables
+// and, with a split, the partial tiles) must fit a CU's.  Depends on (N, K,
+// bits) and on whether M fits 16 columns.
 bool choose_affine_mfma(int bits, int M, int N, int K, LaunchCfg& c)
 {
     c = LaunchCfg{};
-    if (bits != 4 || K % 256 != 0 || K > 4096) return false;
+    if ((bits != 2 && bits != 4 && bits != 8) || (K * bits) % 1024 != 0 || K > 4096) return false;
     const int64_t T = ((int64_t)N + 15) / 16;
     const int MT = M <= 16 ? 16 : 32;
-    const int kbl = K / 256;
+    const int kbl = detail::affine_mfma_kbl(K, bits);
     int cus = 256, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
     // smallest split that gives ~2048 work items, then more chunks while the
     // LDS does not fit (smaller chunks need smaller bias tables)
     auto fits = [&](int n) {
-        if (detail::affine_mfma_gps(K, n) == 0) return false;
+        if (detail::affine_mfma_gps(K, bits, n) == 0) return false;
         int blocks = 0;
         int64_t tmax = 0;
         detail::affine_mfma_geometry(T, n, cus, 1, blocks, tmax);   // most tiles per slot (one workgroup per CU)
-        return detail::affine_mfma_lds_bytes(MT, K, n, tmax) <= detail::kMfmaStreamLdsMax;
+        return detail::affine_mfma_lds_bytes(MT, K, bits, n, tmax) <= detail::kMfmaStreamLdsMax;
     };
     int nkc = 1;
     while (nkc < 8 && 2 * nkc <= kbl && T * nkc < 2048) nkc *= 2;
@@ -284,12 +285,14 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     LaunchCfg c;
     if (bits == 0 && M > 8 && choose_mfma_stream(swiglu, M, N, K, c)) return c;
     if (bits == 0 && M > 8 && choose_mfma_split(swiglu, M, N, K, c)) return c;
-    // 4-bit, M >= 3: the matrix core's cost does not grow with M (up to 16),
-    // the dot-product kernels' does (measured on the 151936 x 1024 LM head:
-    // 27.5 us at any M <= 16 against 32 us for the piece kernel at M = 4)
-    // (with a K split, i.e. few row tiles, from M = 9 on: below that the
-    // piece kernel's shorter prologue wins)
-    if (!swiglu && M >= 3 && choose_affine_mfma(bits, M, N, K, c) && (c.ksplit_log2 == 0 || M > 8)) return c;
+    // Affine matrix core: its cost does not grow with M (up to 16), the
+    // dot-product kernels' does.  4-bit from M = 3 on (measured on the 151936
+    // x 1024 LM head: 27.5 us at any M <= 16 against 32 us for the piece
+    // kernel at M = 4), 2- and 8-bit from M = 9 on; with a K split (few row
+    // tiles) from M = 9 on, below which the piece kernel's shorter prologue
+    // wins.
+    if (!swiglu && M >= 3 && choose_affine_mfma(bits, M, N, K, c) &&
+        (M > 8 || (bits == 4 && c.ksplit_log2 == 0))) return c;
     if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
     if (choose_piece(bits, swiglu, M, N, K, c)) return c;
     if (choose_stream(bits, swiglu, M, N, K, c)) return c;
@@ -299,8 +302,13 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
     if (c.path == PATH_AFFINE_MFMA) {
-        if (bits != 4 || swiglu) return hipErrorInvalidValue;
-        return launch_affine4_mfma(a, c, s);
+        if (swiglu) return hipErrorInvalidValue;
+        switch (bits) {
+            case 2: return launch_affine_mfma<2>(a, c, s);
+            case 4: return launch_affine_mfma<4>(a, c, s);
+            case 8: return launch_affine_mfma<8>(a, c, s);
+            default: return hipErrorInvalidValue;
+        }
     }
     if (c.path == PATH_MFMA_SPLIT) {
         if (bits != 0) return hipErrorInvalidValue;

@@ -519,6 +519,54 @@ def test_affine4_k_split_one_hot_every_group_position_m16():
         assert np.array_equal(y, codes[:, c].T.astype(np.float64)), "cols %s" % c
 
 
+@functools.lru_cache(maxsize=None)
+def affine_mma_case(bits, N, K):
+    x = synth.normal_bf16((32, K), 1.0, 86, "amw/x/%d/%d/%d" % (bits, N, K))
+    aw = synth.affine_weight(86, "amw/%d/%d/%d" % (bits, N, K), bits, N, K)
+    return x, aw, bf16_dev(x), u32_dev(aw.words), bf16_dev(aw.scales), bf16_dev(aw.biases)
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("N,K", [(40001, 1024), (1000, 1536), (700, 4096), (3000, 512)])
+def test_affine_matrix_core_2_and_8_bit(bits, N, K):
+    """2- and 8-bit codes on the matrix core (8-bit codes as two nibble
+    chains): N = 40001 streams whole tiles, the others split K.  M = 9, 16
+    and 32 against the oracle; 9 and 16 bit for bit against each other, and
+    32 as well where its x^T fits."""
+    x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
+    ref, A = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
+    y16 = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, 16), 16, N)
+    assert_within(y16, ref[:16], oracle.tolerance(A[:16]), "q%d 16x%dx%d" % (bits, N, K))
+    y9 = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, 9), 9, N)
+    assert_within(y9, ref[:9], oracle.tolerance(A[:9]), "q%d 9x%dx%d" % (bits, N, K))
+    assert np.array_equal(y9, y16[:9])
+    y32 = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, 32), 32, N)
+    assert_within(y32, ref, oracle.tolerance(A), "q%d 32x%dx%d" % (bits, N, K))
+    if K <= 1024:
+        assert np.array_equal(y16, y32[:16])
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("N,K", [(33000, 1024), (1000, 1536)])
+def test_affine_matrix_core_2_and_8_bit_one_hot_m16(bits, N, K):
+    """s = 1, bias = 0, one-hot x: y = q exactly at all 64 positions of a
+    group (each in a different group), on the matrix core, whole tiles and
+    K split."""
+    words = synth.random_words((N, K * bits // 32), 87, "ohw/%d/%d" % (bits, N))
+    codes = oracle.unpack(words, bits, K)
+    G = K // 64
+    cols = np.array([((r * 7 + 1) % G) * 64 + r for r in range(64)])
+    ones = np.full((N, G), 0x3F80, np.uint16)
+    zeros = np.zeros((N, G), np.uint16)
+    wq, sd, bd = u32_dev(words), bf16_dev(ones), bf16_dev(zeros)
+    for c0 in range(0, 64, 16):
+        c = cols[c0:c0 + 16]
+        x = np.zeros((16, K), np.uint16)
+        x[np.arange(16), c] = 0x3F80
+        y = run_guarded(gemv_affine_gpu(bf16_dev(x), wq, sd, bd, bits, 16), 16, N)
+        assert np.array_equal(y, codes[:, c].T.astype(np.float64)), "cols %s" % c
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_affine_small_integers_exact(bits):
     M, N, K = 3, 5, 192
