@@ -21,7 +21,7 @@ reported under "other_configs" with the same per-call method.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        [--no-extra] [--copy-probe MIB] [--counter-call LABEL]
-       [--summarize-profile DB]
+       [--summarize-profile DB] [--summarize-counters DIR LABEL]
 """
 from __future__ import annotations
 
@@ -58,6 +58,10 @@ def parse():
     p.add_argument("--summarize-profile", metavar="DB", default=None,
                    help="print a markdown summary of a rocprofv3 database (rocpd) taken with "
                         "--kernel-trace --marker-trace --kernel-rename of this script, then exit")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("DIR", "LABEL"), default=None,
+                   help="from DIR/pmc_FETCH_SIZE and DIR/pmc_WRITE_SIZE (rocprofv3 --pmc CSV runs of "
+                        "--counter-call LABEL named 'call' and of --copy-probe 256 named 'copy'), write "
+                        "profiles/traffic.json for the current kernel sources and print a summary, then exit")
     return p.parse_args()
 
 
@@ -322,6 +326,68 @@ def label_bytes(label):
     return N * K * bits // 8 + 4 * N * (K // 64) + 2 * M * K + 2 * M * N
 
 
+def summarize_counters(d, label):
+    """HBM bytes per launch of one call from two counter runs (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch), each scaled by the bytes/KiB that the same
+    counter reads for a device copy of known size."""
+    import csv
+    import statistics
+
+    def rows(ctr, name):
+        path = os.path.join(d, "pmc_" + ctr, name + "_counter_collection.csv")
+        with open(path) as f:
+            return [r for r in csv.DictReader(f) if r["Counter_Name"] == ctr]
+
+    out = {}
+    kernel = None
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy = [float(r["Counter_Value"]) for r in rows(ctr, "copy") if "copyBuffer" in r["Kernel_Name"]]
+        call = rows(ctr, "call")
+        if not copy or not call:
+            raise SystemExit("no %s rows in %s" % (ctr, d))
+        kernel = call[0]["Kernel_Name"]
+        kib_copy = statistics.median(copy)
+        nbytes = 256 * (1 << 20)
+        scale = nbytes / (kib_copy * 1024.0)
+        raw = statistics.mean(float(r["Counter_Value"]) for r in call)
+        out[ctr] = {"kib_copy": kib_copy, "scale": scale, "kib_raw": raw, "bytes": raw * 1024.0 * scale,
+                    "dispatches": len(call)}
+    parts = label.split()
+    M = int(parts[2].split("=")[1])
+    N, K = (int(v) for v in parts[3].split("x"))
+    alg = label_bytes(label)
+    total = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
+    sym = kernel.replace("void aqg::detail::", "").replace("(aqg::ProjArgs)", "")
+    doc = {
+        "sources_sha256_16": kernel_sources_hash(),
+        "method": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (separate runs), KiB per dispatch, each "
+                  "scaled by bytes/counter of a 256 MiB device copy (__amd_rocclr_copyBuffer) in the same kind of run",
+        "calibration": {"copy_bytes": 256 * (1 << 20),
+                        "fetch_kib_per_copy": round(out["FETCH_SIZE"]["kib_copy"], 1),
+                        "write_kib_per_copy": round(out["WRITE_SIZE"]["kib_copy"], 1),
+                        "fetch_scale": round(out["FETCH_SIZE"]["scale"], 5),
+                        "write_scale": round(out["WRITE_SIZE"]["scale"], 5)},
+        "kernels": {"dense_M%d_N%d_K%d" % (M, N, K): {
+            "call": label, "kernel": sym, "dispatches": out["FETCH_SIZE"]["dispatches"],
+            "fetch_kib_raw": round(out["FETCH_SIZE"]["kib_raw"], 1),
+            "write_kib_raw": round(out["WRITE_SIZE"]["kib_raw"], 1),
+            "hbm_read_bytes_per_launch": int(round(out["FETCH_SIZE"]["bytes"])),
+            "hbm_write_bytes_per_launch": int(round(out["WRITE_SIZE"]["bytes"])),
+            "hbm_bytes_per_launch": int(round(total)),
+            "algorithmic_bytes_per_launch": alg,
+            "traffic_over_algorithmic": round(total / alg, 4)}},
+    }
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(doc, f, indent=1)
+    print("| counter | raw KiB / dispatch | copy KiB | scale | bytes / launch |")
+    print("|---|---|---|---|---|")
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        o = out[ctr]
+        print("| %s | %.1f | %.1f | %.5f | %d |" % (ctr, o["kib_raw"], o["kib_copy"], o["scale"], round(o["bytes"])))
+    print("\n%s (`%s`): %d HBM bytes per launch against %d algorithmic (ratio %.4f); sources hash %s"
+          % (label, sym, round(total), alg, total / alg, doc["sources_sha256_16"]))
+
+
 def summarize_profile(db):
     """Per-call kernel durations from a rocprofv3 database of a run of this
     script: dispatches inside each call's timing region are grouped under the
@@ -361,6 +427,8 @@ def main():
     args = parse()
     if args.summarize_profile:
         return summarize_profile(args.summarize_profile)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the projections run on a single MI355X and this "
               "build has no multi-GPU path (requested --gpus %d)." % args.gpus, file=sys.stderr)
