@@ -25,7 +25,8 @@ struct ProjArgs {
     int64_t tmax;            // stream path: most row tiles any wavefront finishes
 };
 
-enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6 };
+enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6,
+            PATH_MFMA_TILE = 7 };
 
 // Launch geometry chosen for a call.
 struct LaunchCfg {
@@ -69,6 +70,10 @@ hipError_t launch_mfma_stream(const ProjArgs& a, const LaunchCfg& c, hipStream_t
 // workgroup per 16-row tile (mfma_stream.hip).
 template <bool SWIGLU>
 hipError_t launch_mfma_split(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+// Dense matrix-core launcher for large N with whole tiles copied into LDS
+// (mfma_tile.hip).
+hipError_t launch_mfma_tile(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // Affine matrix-core launcher, BITS = 2, 4 or 8 (affine_mfma*.hip).
 template <int BITS>

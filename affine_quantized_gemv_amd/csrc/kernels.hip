@@ -1,10 +1,12 @@
 // Launch-geometry choice and dispatch: for M <= 8 the 16-byte-piece streaming
 // kernels (piece_b*.hip: dense, SwiGLU, affine b = 2, 4, 8), else the group
 // streaming or tiled VALU kernels (proj_b*.hip); matrix-core kernels
-// (mfma_dense.hip) for dense and SwiGLU calls with M = 9..32, tiled VALU
-// kernels for affine M = 9..32; plus the code-unpack kernel.
+// (mfma_*.hip) for dense and SwiGLU calls with M = 9..32 and for large-N
+// dense calls from M = 5 on; affine matrix-core kernels (affine_mfma*.hip) for
+// 2-, 4- and 8-bit codes; plus the code-unpack kernel.
 #include "affine_mfma.h"
 #include "mfma_split.h"
+#include "mfma_tile.h"
 #include "piece_kernel.h"
 #include "stream_kernel.h"
 
@@ -105,6 +107,21 @@ bool choose_mfma_stream(bool swiglu, int M, int N, int K, LaunchCfg& c)
     c.nwaves = detail::kMfmaStreamThreads / 64;
     c.R = 1;
     (void)swiglu;
+    return true;
+}
+
+// Large-N dense matrix-core geometry with whole tiles copied into LDS
+// (mfma_tile.h): M = 5..32 padded to 16 or 32 columns, K = 512 .. 2048 in
+// steps of 512, at least 2048 row tiles.  Depends on (N, K) only.
+bool choose_mfma_tile(bool swiglu, int M, int N, int K, LaunchCfg& c)
+{
+    c = LaunchCfg{};
+    if (!detail::mfma_tile_supported(N, K, swiglu)) return false;
+    c.path = PATH_MFMA_TILE;
+    c.MT = M <= 16 ? 16 : 32;
+    c.KT = K;
+    c.nwaves = detail::kMfmaTileWaves;
+    c.R = 1;
     return true;
 }
 
@@ -283,6 +300,11 @@ bool choose_piece(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
 LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 {
     LaunchCfg c;
+    // Large-N dense from M = 5 on: the tile kernel streams the 100000 x 1536
+    // LM head at ~50 us for any M <= 16 (against ~64 us for the dot-product
+    // kernel at M = 5..8, which pads M to 8); M <= 4 stays on the latter
+    // (~45-49 us).
+    if (bits == 0 && M >= 5 && choose_mfma_tile(swiglu, M, N, K, c)) return c;
     if (bits == 0 && M > 8 && choose_mfma_stream(swiglu, M, N, K, c)) return c;
     if (bits == 0 && M > 8 && choose_mfma_split(swiglu, M, N, K, c)) return c;
     // Affine matrix core: its cost does not grow with M (up to 16), the
@@ -309,6 +331,10 @@ hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg
             case 8: return launch_affine_mfma<8>(a, c, s);
             default: return hipErrorInvalidValue;
         }
+    }
+    if (c.path == PATH_MFMA_TILE) {
+        if (bits != 0 || swiglu) return hipErrorInvalidValue;
+        return launch_mfma_tile(a, c, s);
     }
     if (c.path == PATH_MFMA_SPLIT) {
         if (bits != 0) return hipErrorInvalidValue;

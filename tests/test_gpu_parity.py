@@ -201,19 +201,19 @@ def test_dense_small_integers_exact():
                                    synth.DENSE_DECODE_SHAPES[7]], ids=lambda s: s[0])
 def test_dense_rows_independent_of_m(shape):
     """Within one code path each output row is computed the same way whatever M
-    is: M <= 8 (vector ALU path) matches one-row calls bit for bit, M = 9..32
-    (matrix-core path) matches the 32-row call bit for bit.  Across the two
-    paths only the tolerance applies (checked by the parity tests)."""
+    is.  The vector ALU path (M <= 8; on large N only M <= 4) matches one-row
+    calls bit for bit; the matrix-core paths (M = 9..32; on large N from M = 5
+    on) match the first rows of the 32-row call bit for bit.  Across paths only
+    the tolerance applies (checked by the parity tests)."""
     name, N, K = shape
     x, W, xd, Wd = dense_case(synth.CFG_DENSE_DECODE, name, N, K)
+    valu_max = 4 if N >= 32768 else 8
     y1 = torch.cat([aqg.gemv_bf16(xd[m:m + 1], Wd, out_dtype=torch.float32) for m in range(8)]).cpu().numpy()
-    for M in (2, 3, 4, 5, 8):
-        yM = aqg.gemv_bf16(xd[:M], Wd, out_dtype=torch.float32).cpu().numpy()
-        assert np.array_equal(yM, y1[:M]), "M=%d" % M
     y32 = aqg.gemv_bf16(xd[:32], Wd, out_dtype=torch.float32).cpu().numpy()
-    for M in (9, 13, 16, 17, 24, 31):
+    for M in (2, 3, 4, 5, 8, 9, 13, 16, 17, 24, 31):
         yM = aqg.gemv_bf16(xd[:M], Wd, out_dtype=torch.float32).cpu().numpy()
-        assert np.array_equal(yM, y32[:M]), "M=%d" % M
+        want = y1[:M] if M <= valu_max else y32[:M]
+        assert np.array_equal(yM, want), "M=%d" % M
 
 
 def test_swiglu_rows_independent_of_m():
@@ -259,13 +259,15 @@ def test_swiglu_against_unfused_oracle_chain(M):
 
 
 @pytest.mark.parametrize("M", [9, 16, 32])
-def test_dense_large_n_ragged_matrix_core_stream(M):
+@pytest.mark.parametrize("K", [576, 512])
+def test_dense_large_n_ragged_matrix_core(K, M):
     """N = 40001 (>= 2048 row tiles of 16, last one ragged): the persistent
-    matrix-core path, within tolerance, and M = 9..31 bit for bit equal to the
+    matrix-core paths (K = 576: per-wavefront stream; K = 512: whole tiles
+    through LDS), within tolerance, and M = 9..31 bit for bit equal to the
     first rows of the M = 32 call."""
-    N, K = 40001, 512
-    x = synth.normal_bf16((32, K), 1.0, 79, "ln/x")
-    W = synth.normal_bf16((N, K), 0.02, 79, "ln/W")
+    N = 40001
+    x = synth.normal_bf16((32, K), 1.0, 79, "ln/x/%d" % K)
+    W = synth.normal_bf16((N, K), 0.02, 79, "ln/W/%d" % K)
     xd, Wd = bf16_dev(x), bf16_dev(W)
     y = run_guarded(gemv_dense_gpu(xd, Wd, M), M, N)
     ref, A = oracle.gemv_bf16(x[:M], W)
@@ -273,6 +275,42 @@ def test_dense_large_n_ragged_matrix_core_stream(M):
     y32 = aqg.gemv_bf16(xd[:32], Wd, out_dtype=torch.float32).cpu().numpy()
     yM = aqg.gemv_bf16(xd[:M], Wd, out_dtype=torch.float32).cpu().numpy()
     assert np.array_equal(yM, y32[:M])
+
+
+@pytest.mark.parametrize("N,K", [(32769, 1536), (33000, 1024), (32800, 2048), (40001, 512)])
+def test_dense_tile_path_every_k(N, K):
+    """Large-N dense calls with K = 512 .. 2048 (tile ring of 4, 3, 2, 2
+    buffers) at M = 5, 8, 9, 16, 17, 32: parity with the oracle, bf16 = RNE of
+    fp32, no write outside the output, and every M bit for bit equal to the
+    first rows of the M = 32 call.  N leaves a ragged last tile (or none)."""
+    x = synth.normal_bf16((32, K), 1.0, 80, "tp/x/%d" % K)
+    W = synth.normal_bf16((N, K), 0.02, 80, "tp/W/%d/%d" % (N, K))
+    xd, Wd = bf16_dev(x), bf16_dev(W)
+    ref, A = oracle.gemv_bf16(x, W)
+    y32 = None
+    for M in (32, 5, 8, 9, 16, 17):
+        y = run_guarded(gemv_dense_gpu(xd, Wd, M), M, N)
+        assert_within(y, ref[:M], oracle.tolerance(A[:M]), "dense tile %dx%dx%d" % (M, N, K))
+        if M == 32:
+            y32 = y
+        else:
+            assert np.array_equal(y, y32[:M]), "M=%d" % M
+
+
+@pytest.mark.parametrize("K", [1536, 1024])
+def test_dense_tile_path_one_hot_exact(K):
+    """One-hot rows of x at k positions in every wavefront's share of K and in
+    every 1 KB piece of a row: y[m, n] = W[n, k_m] exactly, over a ragged last
+    tile.  Pins the copy into LDS (piece, row and column placement) and the
+    operand reads."""
+    N, M = 32769, 32
+    W = synth.normal_bf16((N, K), 0.02, 81, "tpoh/W/%d" % K)
+    cols = np.array([(m * (K // 32) + 5 * (m % 8) + 3) % K for m in range(M)])
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), cols] = 0x3F80
+    for Mc in (32, 7):
+        y = run_guarded(gemv_dense_gpu(bf16_dev(x), bf16_dev(W), Mc), Mc, N)
+        assert np.array_equal(y, oracle.bf16_to_f64(W[:, cols[:Mc]]).T), "M=%d" % Mc
 
 
 @pytest.mark.parametrize("M", [12, 32])
