@@ -26,7 +26,7 @@ struct ProjArgs {
 };
 
 enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6,
-            PATH_MFMA_TILE = 7 };
+            PATH_MFMA_TILE = 7, PATH_AFFINE_TILE = 8 };
 
 // Launch geometry chosen for a call.
 struct LaunchCfg {
@@ -74,6 +74,11 @@ hipError_t launch_mfma_split(const ProjArgs& a, const LaunchCfg& c, hipStream_t 
 // Dense matrix-core launcher for large N with whole tiles copied into LDS
 // (mfma_tile.hip).
 hipError_t launch_mfma_tile(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+// Affine matrix-core launcher with whole tiles copied into LDS, BITS = 2, 4
+// or 8 (affine_tile_b*.hip).
+template <int BITS>
+hipError_t launch_affine_tile(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // Affine matrix-core launcher, BITS = 2, 4 or 8 (affine_mfma*.hip).
 template <int BITS>

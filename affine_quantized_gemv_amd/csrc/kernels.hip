@@ -5,6 +5,7 @@
 // dense calls from M = 5 on; affine matrix-core kernels (affine_mfma*.hip) for
 // 2-, 4- and 8-bit codes; plus the code-unpack kernel.
 #include "affine_mfma.h"
+#include "affine_tile.h"
 #include "mfma_split.h"
 #include "mfma_tile.h"
 #include "piece_kernel.h"
@@ -139,6 +140,23 @@ bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)
     c.KT = K;
     c.nwaves = (K / 32) / spw;
     c.blocks = (int)T;
+    c.R = 1;
+    return true;
+}
+
+// Affine matrix-core geometry with whole tiles copied into LDS (2-, 4- and
+// 8-bit codes; affine_tile.h): M = 5..32 padded to 16 or 32 columns, the
+// (bits, K) pairs with a tile ring.  Depends on (bits, N, K) and the column
+// bucket.
+bool choose_affine_tile(int bits, int M, int N, int K, LaunchCfg& c)
+{
+    c = LaunchCfg{};
+    const int MT = M <= 16 ? 16 : 32;
+    if (!(bits == 2 || bits == 4 || bits == 8) || !detail::affine_tile_supported(bits, N, K, MT)) return false;
+    c.path = PATH_AFFINE_TILE;
+    c.MT = MT;
+    c.KT = K;
+    c.nwaves = detail::kMfmaTileWaves;
     c.R = 1;
     return true;
 }
@@ -313,6 +331,9 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     // kernel at M = 4), 2- and 8-bit from M = 9 on; with a K split (few row
     // tiles) from M = 9 on, below which the piece kernel's shorter prologue
     // wins.
+    // Affine tiles through LDS from M = 5 on where they serve (K = 2048 / 4096
+    // and 8-bit K = 1024: 14336 x 4096 at M = 16 54.7 -> 18.4 us at 4 bits).
+    if (!swiglu && M >= 5 && choose_affine_tile(bits, M, N, K, c)) return c;
     if (!swiglu && M >= 3 && choose_affine_mfma(bits, M, N, K, c) &&
         (M > 8 || (bits == 4 && c.ksplit_log2 == 0))) return c;
     if (bits == 0 && M > 8 && K % 32 == 0) return choose_mfma(swiglu, M, N, K);
@@ -323,6 +344,15 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 
 hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
+    if (c.path == PATH_AFFINE_TILE) {
+        if (swiglu) return hipErrorInvalidValue;
+        switch (bits) {
+            case 2: return launch_affine_tile<2>(a, c, s);
+            case 4: return launch_affine_tile<4>(a, c, s);
+            case 8: return launch_affine_tile<8>(a, c, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (c.path == PATH_AFFINE_MFMA) {
         if (swiglu) return hipErrorInvalidValue;
         switch (bits) {

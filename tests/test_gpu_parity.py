@@ -584,6 +584,49 @@ def test_affine_matrix_core_2_and_8_bit(bits, N, K):
         assert np.array_equal(y16, y32[:16])
 
 
+@pytest.mark.parametrize("bits,N,K", [(4, 3001, 2048), (4, 2049, 4096), (2, 1000, 4096), (2, 3000, 2048),
+                                      (8, 2000, 1024), (8, 1000, 2048), (8, 999, 4096)])
+def test_affine_tile_path(bits, N, K):
+    """Affine tiles copied into LDS (2/4-bit K = 2048, 4096; 8-bit K = 1024,
+    2048, and 4096 up to 16 columns): M = 5, 9, 16, 17, 32 against the oracle
+    (bf16 = RNE of fp32, no write outside the output), ragged last tile, and
+    every M of a path bit for bit equal to the first rows of its widest call."""
+    x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
+    ref, A = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
+    Ms = (16, 5, 9) if (bits == 8 and K == 4096) else (32, 5, 9, 16, 17)
+    top = None
+    for M in Ms:
+        y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, M), M, N)
+        assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q%d tile %dx%dx%d" % (bits, M, N, K))
+        if top is None:
+            top = y
+        else:
+            assert np.array_equal(y, top[:M]), "M=%d" % M
+
+
+@pytest.mark.parametrize("bits,K", [(2, 4096), (4, 2048), (8, 1024), (8, 4096)])
+def test_affine_tile_path_one_hot_exact(bits, K):
+    """s = 1, bias = 0, one-hot x: y = q exactly, with the ones at every
+    position of a group, in every wavefront's share of K (M = 16, tile path);
+    then s = 2, bias = -1 on the same codes: y = 2 q - 1 exactly."""
+    N = 1001
+    words = synth.random_words((N, K * bits // 32), 88, "toh/%d/%d" % (bits, K))
+    codes = oracle.unpack(words, bits, K)
+    G = K // 64
+    cols = np.array([((r * 5 + 3) % G) * 64 + r for r in range(64)])
+    wq = u32_dev(words)
+    for sv, bv in ((0x3F80, 0x0000), (0x4000, 0xBF80)):
+        sd = bf16_dev(np.full((N, G), sv, np.uint16))
+        bd = bf16_dev(np.full((N, G), bv, np.uint16))
+        want_s, want_b = oracle.bf16_to_f64(np.array([sv], np.uint16))[0], oracle.bf16_to_f64(np.array([bv], np.uint16))[0]
+        for c0 in range(0, 64, 16):
+            c = cols[c0:c0 + 16]
+            x = np.zeros((16, K), np.uint16)
+            x[np.arange(16), c] = 0x3F80
+            y = run_guarded(gemv_affine_gpu(bf16_dev(x), wq, sd, bd, bits, 16), 16, N)
+            assert np.array_equal(y, (want_s * codes[:, c] + want_b).T.astype(np.float64)), "cols %s" % c
+
+
 @pytest.mark.parametrize("bits", [2, 8])
 @pytest.mark.parametrize("N,K", [(33000, 1024), (1000, 1536)])
 def test_affine_matrix_core_2_and_8_bit_one_hot_m16(bits, N, K):
@@ -655,19 +698,20 @@ def test_affine_ragged_shapes(M, N, K, bits):
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_affine_rows_independent_of_m(bits):
-    """M <= 8 (streaming path, x in registers or LDS) matches one-row calls bit
-    for bit; M = 9..16 and M = 17..32 match the 16- and 32-row calls bit for
-    bit (the two buckets may take different paths: 16 columns of x^T fit in
-    LDS where 32 do not)."""
+    """On 4096 x 4096, M <= 4 (streaming path, x in registers or LDS) matches
+    one-row calls bit for bit; M = 5..16 (tiles through LDS) match the 16-row
+    call and M = 17..32 the 32-row call bit for bit (the two buckets may take
+    different paths: 8-bit tiles of K = 4096 fit a CU's LDS only beside 16
+    columns)."""
     name, N, K = synth.MIXED_SHAPES[0]
     x, aw, xd, wq, sd, bd = affine_case(synth.CFG_MIXED_WIDTH, name, bits, N, K)
     y1 = torch.cat([aqg.gemv_affine(xd[m:m + 1], wq, sd, bd, bits, out_dtype=torch.float32)
-                    for m in range(8)]).cpu().numpy()
-    for M in (2, 3, 4, 7, 8):
+                    for m in range(4)]).cpu().numpy()
+    for M in (2, 3, 4):
         yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
         assert np.array_equal(yM, y1[:M]), "M=%d" % M
     y16 = aqg.gemv_affine(xd[:16], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
-    for M in (9, 12):
+    for M in (5, 8, 9, 12):
         yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
         assert np.array_equal(yM, y16[:M]), "M=%d" % M
     y32 = aqg.gemv_affine(xd[:32], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
