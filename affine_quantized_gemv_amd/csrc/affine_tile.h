@@ -2,6 +2,10 @@
 // (M padded to 16 or 32) that copies whole 16-row tiles into LDS, as the
 // dense tile kernel (mfma_tile.h) does.
 //
+// Widths: 2, 4 and 8 bits take the operand orders of affine_mfma.h; 3, 5, 6
+// and 7 bits a natural order, each lane quarter extracting its 16 codes of a
+// group from a bit window (AffineTileWidth, codes_window_to_bf16).
+//
 // A tile is RB blocks of 16 rows of codes (16 RB K b / 8 consecutive bytes
 // of HBM) plus the rows' scales and biases.  Each of the 8 wavefronts of a
 // workgroup copies its share of the code bytes (1 KB per instruction, 16
@@ -71,6 +75,46 @@ __device__ __forceinline__ void copy_dword_to_lds(u32x4v_t rs, uint32_t lds, uin
                  :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
 }
 
+// Widths 3, 5, 6, 7: lane quarter c of a row takes codes 16c .. 16c + 15 of
+// each group, and k-step h the codes 16c + 8h .. + 7, in natural order (2, 4
+// and 8 bits keep the orders of affine_mfma.h).
+template <int B> struct AffineTileWidth {
+    static constexpr bool NATURAL = B != 2 && B != 4 && B != 8;
+    static constexpr int NWN = (16 * B + 31) / 32;   // words of a lane's 16-code window
+    static constexpr uint32_t MASK = (1u << B) - 1u;
+};
+
+// x^T operand of k-step S (group S / 2, half S % 2) in natural k order for
+// lane quarter c: x[64 (S / 2) + 16 c + 8 (S % 2) .. + 7]; also its sum.
+__device__ __forceinline__ u32x4_t stage_x_natural(const uint16_t* xr, int S, int c, float& sum)
+{
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + 64 * (S >> 1) + 16 * c + 8 * (S & 1));
+    sum = ((bf16_to_f32(v.x & 0xFFFFu) + bf16_to_f32(v.x >> 16)) + (bf16_to_f32(v.y & 0xFFFFu) + bf16_to_f32(v.y >> 16))) +
+          ((bf16_to_f32(v.z & 0xFFFFu) + bf16_to_f32(v.z >> 16)) + (bf16_to_f32(v.w & 0xFFFFu) + bf16_to_f32(v.w >> 16)));
+    return u32x4_t{v.x, v.y, v.z, v.w};
+}
+
+// Codes 8H .. 8H + 7 of a lane's window wn (code i at bits B i, LSB first)
+// as bf16 pairs (128 + q_{2t}, 128 + q_{2t+1}), t = 0..3.  m = the B-bit
+// mask, mh = m << 16, cb = 0x43004300, all opaque registers, and only plain
+// C, so the compiler sees every write of these MFMA operands.
+template <int B, int H>
+__device__ __forceinline__ u32x4_t codes_window_to_bf16(const uint32_t (&wn)[AffineTileWidth<B>::NWN], uint32_t m,
+                                                       uint32_t mh, uint32_t cb)
+{
+    u32x4_t o;
+    static_for<0, 4>([&](auto Tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(Tc)::value;
+        constexpr int bit = (8 * H + 2 * t) * B;
+        constexpr int k = bit >> 5, sh = bit & 31;
+        uint32_t w;
+        if constexpr (sh + 2 * B <= 32) w = wn[k] >> sh;
+        else w = __builtin_amdgcn_alignbit(wn[k + 1], wn[k], sh);
+        o[t] = (w & m) | ((w << (16 - B)) & mh) | cb;
+    });
+    return o;
+}
+
 template <int BITS, int MT, int K, int RB, int NBUF>
 __global__ void __launch_bounds__(kMfmaTileThreads) affine_tile_kernel(ProjArgs a)
 {
@@ -78,7 +122,8 @@ __global__ void __launch_bounds__(kMfmaTileThreads) affine_tile_kernel(ProjArgs 
     constexpr int KS = L::KS;
     constexpr int NB = L::NB;
     constexpr int GW = L::GW;
-    constexpr float OFF = AffineMma<BITS>::OFF;
+    using WD = AffineTileWidth<BITS>;
+    constexpr float OFF = BITS == 8 ? 2176.0f : 128.0f;
     static_assert(NBUF >= 2 && NBUF <= 6, "ring of 2..6 tiles");
 
     const int lane = threadIdx.x & 63;
@@ -138,8 +183,13 @@ __global__ void __launch_bounds__(kMfmaTileThreads) affine_tile_kernel(ProjArgs 
 #pragma unroll
         for (int g = 0; g < GW; ++g) {
             float s0 = 0.f, s1 = 0.f;
-            xr[2 * g][b] = stage_x_operand<BITS>(xrow, 2 * g, c, s0);
-            xr[2 * g + 1][b] = stage_x_operand<BITS>(xrow, 2 * g + 1, c, s1);
+            if constexpr (WD::NATURAL) {
+                xr[2 * g][b] = stage_x_natural(xrow, 2 * g, c, s0);
+                xr[2 * g + 1][b] = stage_x_natural(xrow, 2 * g + 1, c, s1);
+            } else {
+                xr[2 * g][b] = stage_x_operand<BITS>(xrow, 2 * g, c, s0);
+                xr[2 * g + 1][b] = stage_x_operand<BITS>(xrow, 2 * g + 1, c, s1);
+            }
             if (m >= a.M) {
                 xr[2 * g][b] = xr[2 * g + 1][b] = u32x4_t{0u, 0u, 0u, 0u};
                 s0 = s1 = 0.f;
@@ -155,9 +205,14 @@ __global__ void __launch_bounds__(kMfmaTileThreads) affine_tile_kernel(ProjArgs 
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     barrier_only();
 
-    uint32_t cmask = AffineMma<BITS>::MASK, cbias = 0x43004300u;
+    uint32_t cmask = WD::NATURAL ? WD::MASK : AffineMma<BITS == 2 || BITS == 4 ? BITS : 8>::MASK;
+    uint32_t cmaskh = WD::MASK << 16, cbias = 0x43004300u;
     asm volatile("" : "+s"(cmask));      // no instruction: only hides the constants
+    asm volatile("" : "+s"(cmaskh));
     asm volatile("" : "+v"(cbias));
+    // natural widths: first word and bit of the lane's 16-code window in a group
+    const int lw0 = (16 * c * BITS) >> 5;
+    const bool lodd = ((16 * c * BITS) & 31) != 0;
 
     const int t = threadIdx.x;
     const int esz = a.out_f32 ? 4 : 2;
@@ -188,10 +243,25 @@ __global__ void __launch_bounds__(kMfmaTileThreads) affine_tile_kernel(ProjArgs 
         // row r's codes: byte offset of group g0 + g within the tile
 #pragma unroll
         for (int g = 0; g < GW; ++g) {
-            const int off = (16 * rb + r) * L::ROWB + (gw0 + g) * 8 * BITS;   // group start, never straddles a piece
+            const int off = (16 * rb + r) * L::ROWB + (gw0 + g) * 8 * BITS;   // group start
+            // 2, 4, 8 bits: a group never straddles a 1 KB piece
             const char* gp = tb + (off >> 10) * 1040 + (off & 1023) + 4 * c;
             u32x4_t A0, A1, H0, H1;
-            if constexpr (BITS == 4) {
+            if constexpr (WD::NATURAL) {
+                // the window's words (each placed by its own piece: odd-width
+                // groups can straddle pieces), shifted by 16 bits when the
+                // window starts mid-word
+                uint32_t raw[WD::NWN + 1], wn[WD::NWN];
+#pragma unroll
+                for (int k = 0; k <= WD::NWN; ++k) {
+                    const int ab = off + 4 * (lw0 + k);
+                    raw[k] = *reinterpret_cast<const uint32_t*>(tb + (ab >> 10) * 1040 + (ab & 1023));
+                }
+#pragma unroll
+                for (int k = 0; k < WD::NWN; ++k) wn[k] = lodd ? __builtin_amdgcn_alignbit(raw[k + 1], raw[k], 16) : raw[k];
+                A0 = codes_window_to_bf16<BITS, 0>(wn, cmask, cmaskh, cbias);
+                A1 = codes_window_to_bf16<BITS, 1>(wn, cmask, cmaskh, cbias);
+            } else if constexpr (BITS == 4) {
                 A0 = codes4_to_bf16(*reinterpret_cast<const uint32_t*>(gp), cmask, cbias);
                 A1 = codes4_to_bf16(*reinterpret_cast<const uint32_t*>(gp + 16), cmask, cbias);
             } else if constexpr (BITS == 2) {
@@ -290,6 +360,9 @@ inline int affine_tile_nbuf(int bits, int K, int MT)
     if (bits == 8 && K == 1024) return 3;
     if (bits == 8 && K == 2048) return 2;
     if (bits == 8 && K == 4096 && MT == 16) return 2;
+    if (bits == 3 && K == 4096) return 3;
+    if ((bits == 5 || bits == 6 || bits == 7) && K == 4096) return 2;
+    if (bits == 6 && K == 2048) return 3;
     return 0;
 }
 
@@ -331,6 +404,16 @@ hipError_t launch_affine_tile_mt(const ProjArgs& a, hipStream_t s)
         switch (a.K) {
             case 2048: return launch_affine_tile_one<2, MT, 2048, 1, 5>(a, s);
             case 4096: return launch_affine_tile_one<2, MT, 4096, 1, 3>(a, s);
+            default: return hipErrorInvalidValue;
+        }
+    } else if constexpr (BITS == 3) {
+        return a.K == 4096 ? launch_affine_tile_one<3, MT, 4096, 1, 3>(a, s) : hipErrorInvalidValue;
+    } else if constexpr (BITS == 5 || BITS == 7) {
+        return a.K == 4096 ? launch_affine_tile_one<BITS, MT, 4096, 1, 2>(a, s) : hipErrorInvalidValue;
+    } else if constexpr (BITS == 6) {
+        switch (a.K) {
+            case 2048: return launch_affine_tile_one<6, MT, 2048, 1, 3>(a, s);
+            case 4096: return launch_affine_tile_one<6, MT, 4096, 1, 2>(a, s);
             default: return hipErrorInvalidValue;
         }
     } else {

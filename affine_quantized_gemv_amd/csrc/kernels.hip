@@ -144,15 +144,15 @@ bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)
     return true;
 }
 
-// Affine matrix-core geometry with whole tiles copied into LDS (2-, 4- and
-// 8-bit codes; affine_tile.h): M = 5..32 padded to 16 or 32 columns, the
+// Affine matrix-core geometry with whole tiles copied into LDS (2- to 8-bit
+// codes; affine_tile.h): M = 5..32 padded to 16 or 32 columns, the
 // (bits, K) pairs with a tile ring.  Depends on (bits, N, K) and the column
 // bucket.
 bool choose_affine_tile(int bits, int M, int N, int K, LaunchCfg& c)
 {
     c = LaunchCfg{};
     const int MT = M <= 16 ? 16 : 32;
-    if (!(bits == 2 || bits == 4 || bits == 8) || !detail::affine_tile_supported(bits, N, K, MT)) return false;
+    if (bits < 2 || bits > 8 || !detail::affine_tile_supported(bits, N, K, MT)) return false;
     c.path = PATH_AFFINE_TILE;
     c.MT = MT;
     c.KT = K;
@@ -348,7 +348,11 @@ hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg
         if (swiglu) return hipErrorInvalidValue;
         switch (bits) {
             case 2: return launch_affine_tile<2>(a, c, s);
+            case 3: return launch_affine_tile<3>(a, c, s);
             case 4: return launch_affine_tile<4>(a, c, s);
+            case 5: return launch_affine_tile<5>(a, c, s);
+            case 6: return launch_affine_tile<6>(a, c, s);
+            case 7: return launch_affine_tile<7>(a, c, s);
             case 8: return launch_affine_tile<8>(a, c, s);
             default: return hipErrorInvalidValue;
         }

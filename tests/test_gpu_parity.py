@@ -585,10 +585,12 @@ def test_affine_matrix_core_2_and_8_bit(bits, N, K):
 
 
 @pytest.mark.parametrize("bits,N,K", [(4, 3001, 2048), (4, 2049, 4096), (2, 1000, 4096), (2, 3000, 2048),
-                                      (8, 2000, 1024), (8, 1000, 2048), (8, 999, 4096)])
+                                      (8, 2000, 1024), (8, 1000, 2048), (8, 999, 4096), (3, 1000, 4096),
+                                      (5, 1001, 4096), (6, 999, 2048), (6, 500, 4096), (7, 777, 4096)])
 def test_affine_tile_path(bits, N, K):
     """Affine tiles copied into LDS (2/4-bit K = 2048, 4096; 8-bit K = 1024,
-    2048, and 4096 up to 16 columns): M = 5, 9, 16, 17, 32 against the oracle
+    2048, and 4096 up to 16 columns; 3, 5, 7 bits K = 4096 and 6 bits K =
+    2048, 4096 with codes taken from bit windows): M = 5, 9, 16, 17, 32 against the oracle
     (bf16 = RNE of fp32, no write outside the output), ragged last tile, and
     every M of a path bit for bit equal to the first rows of its widest call."""
     x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
@@ -604,7 +606,8 @@ def test_affine_tile_path(bits, N, K):
             assert np.array_equal(y, top[:M]), "M=%d" % M
 
 
-@pytest.mark.parametrize("bits,K", [(2, 4096), (4, 2048), (8, 1024), (8, 4096)])
+@pytest.mark.parametrize("bits,K", [(2, 4096), (4, 2048), (8, 1024), (8, 4096), (3, 4096), (5, 4096), (6, 2048),
+                                    (7, 4096)])
 def test_affine_tile_path_one_hot_exact(bits, K):
     """s = 1, bias = 0, one-hot x: y = q exactly, with the ones at every
     position of a group, in every wavefront's share of K (M = 16, tile path);
@@ -696,7 +699,7 @@ def test_affine_ragged_shapes(M, N, K, bits):
     assert_within(y, ref, oracle.tolerance(A), "q%d %dx%dx%d" % (bits, M, N, K))
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_affine_rows_independent_of_m(bits):
     """On 4096 x 4096, M <= 4 (streaming path, x in registers or LDS) matches
     one-row calls bit for bit; M = 5..16 (tiles through LDS) match the 16-row
