@@ -1,6 +1,6 @@
 // Matrix-core kernel for small-N dense projections and fused SwiGLU at
-// M = 9..32 (M padded to 16 or 32) on gfx950: one workgroup per 16-row tile,
-// K split over NKS wavefronts.
+// M = 9..32 (from M = 5 on wide matrices; M padded to 16 or 32) on gfx950:
+// one workgroup per 16-row tile, K split over NKS wavefronts.
 //
 // A small matrix (a few MB) is latency-bound: what matters is how soon every
 // CU has its loads in flight.  Here nothing waits before the loads: each
@@ -93,45 +93,36 @@ __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(Pro
             }
         }
 
-    // fixed-order sum of the k-splits: every wavefront stores its partial,
-    // wavefront 0 adds them in order 0, 1, ..., nks-1 and stores the tile
+    // fixed-order sum of the k-splits: every wavefront stores its partial
+    // tile (rows of 65 floats: conflict-free reads below), then every thread
+    // adds one output's partials in order 0, 1, ..., nks-1 and stores it
     constexpr int PER = S * NB * 4;              // floats per lane
-    if (wave != 0) {
 #pragma unroll
-        for (int s = 0; s < S; ++s)
+    for (int s = 0; s < S; ++s)
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    lds_red[((size_t)(wave * PER) + (s * NB + b) * 4 + i) * 64 + lane] = acc[s][b][i];
-    }
+            for (int i = 0; i < 4; ++i)
+                lds_red[((size_t)(wave * PER) + (s * NB + b) * 4 + i) * 65 + lane] = acc[s][b][i];
     __syncthreads();
-    if (wave != 0) return;
-    for (int w = 1; w < nks; ++w)
-#pragma unroll
-        for (int s = 0; s < S; ++s)
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[s][b][i] += lds_red[((size_t)(w * PER) + (s * NB + b) * 4 + i) * 64 + lane];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int m = 16 * b + r;
-        if (m >= a.M) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t n = n0 + 4 * c + i;
-            if (n >= a.N) continue;
-            float v = acc[0][b][i];
-            if constexpr (SWIGLU) {
-                const float u = acc[1][b][i];
-                v = (v / (1.0f + __expf(-v))) * u;
-            }
-            const size_t o = (size_t)m * a.N + n;
-            if (a.out_f32) reinterpret_cast<float*>(a.y)[o] = v;
-            else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16_rne(v);
+    // output (m, n0 + n16) lives in lane (n16 / 4) * 16 + m % 16, element
+    // (block m / 16, n16 % 4) of each partial
+    for (int o = threadIdx.x; o < 16 * MT; o += blockDim.x) {
+        const int m = o >> 4, n16 = o & 15;
+        const int j0 = ((m >> 4) * 4 + (n16 & 3)) * 65 + (n16 >> 2) * 16 + (m & 15);
+        float v = lds_red[j0];
+        float u = 0.f;
+        if constexpr (SWIGLU) u = lds_red[j0 + NB * 4 * 65];
+        for (int w = 1; w < nks; ++w) {
+            v += lds_red[(size_t)(w * PER) * 65 + j0];
+            if constexpr (SWIGLU) u += lds_red[(size_t)(w * PER + NB * 4) * 65 + j0];
         }
+        const int64_t n = n0 + n16;
+        if (m >= a.M || n >= a.N) continue;
+        if constexpr (SWIGLU) v = (v / (1.0f + __expf(-v))) * u;
+        const size_t oi = (size_t)m * a.N + n;
+        if (a.out_f32) reinterpret_cast<float*>(a.y)[oi] = v;
+        else reinterpret_cast<uint16_t*>(a.y)[oi] = f32_to_bf16_rne(v);
     }
 }
 
@@ -151,7 +142,7 @@ template <int MT, bool SW, int SPW>
 hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
 {
     const int nks = (a.K / 32) / SPW;
-    const size_t lds = (size_t)nks * (SW ? 2 : 1) * (MT / 16) * 4 * 64 * 4;
+    const size_t lds = (size_t)nks * (SW ? 2 : 1) * (MT / 16) * 4 * 65 * 4;
     const int64_t tiles = ((int64_t)a.N + 15) / 16;
     hipLaunchKernelGGL((mfma_split_kernel<MT, SW, SPW>), dim3((unsigned)tiles), dim3(64 * nks), lds, s, a);
     return hipGetLastError();
