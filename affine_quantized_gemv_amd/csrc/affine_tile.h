@@ -43,28 +43,30 @@
 namespace aqg {
 namespace detail {
 
-template <int BITS, int MT, int K, int RB, int NBUF>
+template <int BITS, int MT, int K, int RB, int NBUF, int NWV = kMfmaTileWaves>
 struct AffineTileLayout {
-    static constexpr int KS = kMfmaTileWaves / RB; // k chunks per row block
+    static constexpr int NT = 64 * NWV;           // threads per workgroup
+    static constexpr int KS = NWV / RB;           // k chunks per row block
     static constexpr int ROWB = K * BITS / 8;     // code bytes per row
     static constexpr int CP = 16 * RB * ROWB / 1024;   // 1 KB code pieces per tile
-    static constexpr int CPW = CP / kMfmaTileWaves;
+    static constexpr int CPW = CP / NWV;
     static constexpr int CODE = CP * 1040;        // LDS: pieces with a 16-byte pad each
     static constexpr int GW = K / (64 * KS);      // groups per wavefront
     static constexpr int GPR = K / 64;            // groups per row
     static constexpr int SBW = 16 * GW * 2;       // bytes of one wavefront's scales (16 rows x GW)
     static constexpr int SBL = SBW / 4;           // lanes copying them, 4 bytes each
-    static constexpr int TILE = CODE + 2 * kMfmaTileWaves * SBW;
+    static constexpr int TILE = CODE + 2 * NWV * SBW;
     static constexpr int OPT = CPW + 2;           // copies per wavefront per tile
     static constexpr int NB = MT / 16;
     static constexpr int PW = NB * 4 * 65;
-    static constexpr int PART = kMfmaTileWaves * PW * 4;
-    static constexpr int NSTO = (16 * RB * MT + kMfmaTileThreads - 1) / kMfmaTileThreads;   // stores per thread per tile
-    static constexpr int TAB = kMfmaTileWaves * 2 * GW * 16 * 4;   // per-wavefront (s, c) tables
+    static constexpr int PART = NWV * PW * 4;
+    static constexpr int NSTO = (16 * RB * MT + NT - 1) / NT;   // stores per thread per tile
+    static constexpr int TAB = NWV * 2 * GW * 16 * 4;   // per-wavefront (s, c) tables
     static constexpr size_t LDS = (size_t)NBUF * TILE + PART + TAB;
     static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8, "row blocks divide the wavefronts");
     static_assert(K % (64 * KS) == 0, "whole groups per wavefront");
-    static_assert(CP % kMfmaTileWaves == 0 && CP > 0, "code pieces split evenly over the wavefronts");
+    static_assert(CP % NWV == 0 && CP > 0, "code pieces split evenly over the wavefronts");
+    static_assert(NWV % RB == 0, "row blocks divide the wavefronts");
     static_assert(GW % 2 == 0 && SBL <= 64, "scales come as pairs of groups, one copy instruction per wavefront");
 };
 
@@ -115,10 +117,10 @@ __device__ __forceinline__ u32x4_t codes_window_to_bf16(const uint32_t (&wn)[Aff
     return o;
 }
 
-template <int BITS, int MT, int K, int RB, int NBUF>
-__global__ void __launch_bounds__(kMfmaTileThreads) affine_tile_kernel(ProjArgs a)
+template <int BITS, int MT, int K, int RB, int NBUF, int NWV = kMfmaTileWaves>
+__global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
 {
-    using L = AffineTileLayout<BITS, MT, K, RB, NBUF>;
+    using L = AffineTileLayout<BITS, MT, K, RB, NBUF, NWV>;
     constexpr int KS = L::KS;
     constexpr int NB = L::NB;
     constexpr int GW = L::GW;
@@ -164,7 +166,7 @@ __global__ void __launch_bounds__(kMfmaTileThreads) affine_tile_kernel(ProjArgs 
         const u32x4v_t rb = buffer_words(a.biases + n0 * L::GPR, rows * L::GPR * 2);
         if (lane < L::SBL) {
             copy_dword_to_lds(rs, dst + L::CODE + wave * L::SBW, sb_voff, 0);
-            copy_dword_to_lds(rb, dst + L::CODE + (kMfmaTileWaves + wave) * L::SBW, sb_voff, 0);
+            copy_dword_to_lds(rb, dst + L::CODE + (NWV + wave) * L::SBW, sb_voff, 0);
         }
     };
 
@@ -230,7 +232,7 @@ __global__ void __launch_bounds__(kMfmaTileThreads) affine_tile_kernel(ProjArgs 
             if (e < 16 * GW) {
                 const int row = e & 15, g = e >> 4;
                 const uint16_t* sp = reinterpret_cast<const uint16_t*>(tb + L::CODE + wave * L::SBW);
-                const uint16_t* bp = reinterpret_cast<const uint16_t*>(tb + L::CODE + (kMfmaTileWaves + wave) * L::SBW);
+                const uint16_t* bp = reinterpret_cast<const uint16_t*>(tb + L::CODE + (NWV + wave) * L::SBW);
                 const float s = bf16_to_f32(sp[row * GW + g]);
                 const float bi = bf16_to_f32(bp[row * GW + g]);
                 tab[g * 16 + row] = s;
@@ -306,7 +308,7 @@ __global__ void __launch_bounds__(kMfmaTileThreads) affine_tile_kernel(ProjArgs 
         // consecutive rows of one column)
 #pragma unroll
         for (int u = 0; u < L::NSTO; ++u) {
-            const int o = t + kMfmaTileThreads * u;
+            const int o = t + L::NT * u;
             const bool valid = o < 16 * RB * MT;
             const int om = valid ? o / (16 * RB) : 0, nl = o % (16 * RB);
             const int rbo = nl >> 4, n16 = nl & 15;
@@ -366,21 +368,21 @@ inline int affine_tile_nbuf(int bits, int K, int MT)
     return 0;
 }
 
-template <int BITS, int MT, int K, int RB, int NBUF>
+template <int BITS, int MT, int K, int RB, int NBUF, int NWV = kMfmaTileWaves>
 hipError_t launch_affine_tile_one(const ProjArgs& a, hipStream_t s)
 {
-    static_assert(AffineTileLayout<BITS, MT, K, RB, NBUF>::LDS <= 160 * 1024, "fits one CU's LDS");
-    const void* fn = reinterpret_cast<const void*>(&affine_tile_kernel<BITS, MT, K, RB, NBUF>);
+    static_assert(AffineTileLayout<BITS, MT, K, RB, NBUF, NWV>::LDS <= 160 * 1024, "fits one CU's LDS");
+    const void* fn = reinterpret_cast<const void*>(&affine_tile_kernel<BITS, MT, K, RB, NBUF, NWV>);
     int dev = 0, cus = 0, bpc = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, kMfmaTileThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, 64 * NWV, 0);
     if (e != hipSuccess) return e;
     if (bpc < 1) bpc = 1;
     const int64_t T = ((int64_t)a.N + 16 * RB - 1) / (16 * RB);
     int64_t blocks = (int64_t)bpc * cus;
     if (blocks > T) blocks = T;
-    hipLaunchKernelGGL((affine_tile_kernel<BITS, MT, K, RB, NBUF>), dim3((unsigned)blocks), dim3(kMfmaTileThreads), 0, s, a);
+    hipLaunchKernelGGL((affine_tile_kernel<BITS, MT, K, RB, NBUF, NWV>), dim3((unsigned)blocks), dim3(64 * NWV), 0, s, a);
     return hipGetLastError();
 }
 

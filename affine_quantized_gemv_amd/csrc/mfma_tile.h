@@ -50,20 +50,23 @@ namespace detail {
 constexpr int kMfmaTileWaves = 8;
 constexpr int kMfmaTileThreads = 64 * kMfmaTileWaves;
 
-template <int MT, int KSW, int NBUF>
+template <int MT, int KSW, int NBUF, int NW = kMfmaTileWaves>
 struct MfmaTileLayout {
     static constexpr int K = 256 * KSW;           // k per row
+    static constexpr int NT = 64 * NW;            // threads per workgroup
+    static constexpr int KSTEPS = K / 32 / NW;    // k-steps per wavefront
     static constexpr int ROW = 2 * K;             // bytes per weight row
     static constexpr int RS = ROW + 16;           // LDS row stride (bank pad)
     static constexpr int TILE = 16 * RS;          // LDS bytes per tile buffer
-    static constexpr int CPW = KSW;               // 1 KB pieces per wavefront per tile
+    static constexpr int CPW = 8 * KSW / NW;      // 1 KB pieces per wavefront per tile
     static constexpr int CPR = ROW / 1024;        // 1 KB pieces per row
     static constexpr int NB = MT / 16;            // 16-column blocks of x^T
     static constexpr int PW = NB * 4 * 65;        // floats per wavefront partial (65: bank pad)
-    static constexpr int PART = kMfmaTileWaves * PW * 4;
+    static constexpr int PART = NW * PW * 4;
     static constexpr size_t LDS = (size_t)NBUF * TILE + PART;
     static_assert(ROW % 1024 == 0, "pieces never straddle rows");
-    static_assert(16 * ROW / 1024 == kMfmaTileWaves * CPW, "pieces split evenly over the wavefronts");
+    static_assert(16 * ROW / 1024 == NW * CPW, "pieces split evenly over the wavefronts");
+    static_assert(KSTEPS * 32 * NW == K, "k-steps split evenly over the wavefronts");
 };
 
 // Distinct LDS objects: buffer I of BYTES bytes.
@@ -103,10 +106,10 @@ __device__ __forceinline__ void barrier_only()
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <int MT, int KSW, int NBUF>
-__global__ void __launch_bounds__(kMfmaTileThreads) mfma_tile_kernel(ProjArgs a)
+template <int MT, int KSW, int NBUF, int NW = kMfmaTileWaves>
+__global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
 {
-    using L = MfmaTileLayout<MT, KSW, NBUF>;
+    using L = MfmaTileLayout<MT, KSW, NBUF, NW>;
     constexpr int NB = L::NB;
     static_assert(NBUF >= 1 && NBUF <= 4, "ring of 1..4 tiles");
 
@@ -147,10 +150,10 @@ __global__ void __launch_bounds__(kMfmaTileThreads) mfma_tile_kernel(ProjArgs a)
     static_for<0, NBUF>([&](auto Bc) __attribute__((always_inline)) {
         if (decltype(Bc)::value < ntile) issue(decltype(Bc)::value, Bc);
     });
-    u32x4_t xr[KSW][NB];
-    const int kw = wave * (L::K / 8);
+    u32x4_t xr[L::KSTEPS][NB];
+    const int kw = wave * (L::K / NW);
 #pragma unroll
-    for (int s = 0; s < KSW; ++s)
+    for (int s = 0; s < L::KSTEPS; ++s)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int m = 16 * b + r;
@@ -181,7 +184,7 @@ __global__ void __launch_bounds__(kMfmaTileThreads) mfma_tile_kernel(ProjArgs a)
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KSW; ++s) {
+        for (int s = 0; s < L::KSTEPS; ++s) {
             const u32x4_t A = *reinterpret_cast<const u32x4_t*>(src + 64 * s);
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[b] = mfma16x16x32(A, xr[s][b], acc[b]);
@@ -200,7 +203,7 @@ __global__ void __launch_bounds__(kMfmaTileThreads) mfma_tile_kernel(ProjArgs a)
         const float* p = part + (red ? pidx : 0);
         float v = p[0];
 #pragma unroll
-        for (int w = 1; w < kMfmaTileWaves; ++w) v += p[w * L::PW];
+        for (int w = 1; w < NW; ++w) v += p[w * L::PW];
         const int64_t n = (first + j * stride) * 16 + on;
         const uint32_t off = (red && om < a.M && n < a.N) ? (uint32_t)(((int64_t)om * a.N + n) * esz) : kDrop;
         if (a.out_f32) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, off, 0, 0);
@@ -256,21 +259,21 @@ inline bool mfma_tile_supported(int N, int K, bool swiglu)
            (int64_t)32 * N * 4 < 0x7FFFFFF0;
 }
 
-template <int MT, int KSW, int NBUF>
+template <int MT, int KSW, int NBUF, int NW = kMfmaTileWaves>
 hipError_t launch_mfma_tile_one(const ProjArgs& a, hipStream_t s)
 {
-    static_assert(MfmaTileLayout<MT, KSW, NBUF>::LDS <= 160 * 1024, "fits one CU's LDS");
-    const void* fn = reinterpret_cast<const void*>(&mfma_tile_kernel<MT, KSW, NBUF>);
+    static_assert(MfmaTileLayout<MT, KSW, NBUF, NW>::LDS <= 160 * 1024, "fits one CU's LDS");
+    const void* fn = reinterpret_cast<const void*>(&mfma_tile_kernel<MT, KSW, NBUF, NW>);
     int dev = 0, cus = 0, bpc = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, kMfmaTileThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, 64 * NW, 0);
     if (e != hipSuccess) return e;
     if (bpc < 1) bpc = 1;
     const int64_t T = ((int64_t)a.N + 15) / 16;
     int64_t blocks = (int64_t)bpc * cus;
     if (blocks > T) blocks = T;
-    hipLaunchKernelGGL((mfma_tile_kernel<MT, KSW, NBUF>), dim3((unsigned)blocks), dim3(kMfmaTileThreads), 0, s, a);
+    hipLaunchKernelGGL((mfma_tile_kernel<MT, KSW, NBUF, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
