@@ -1,4 +1,4 @@
-// Persistent matrix-core kernel for affine GEMVs with 2-, 4- and 8-bit codes
+// Persistent matrix-core kernel for affine GEMVs with codes of 2 to 8 bits
 // (M padded to 16 or 32) that copies whole 16-row tiles into LDS, as the
 // dense tile kernel (mfma_tile.h) does.
 //

@@ -1,9 +1,11 @@
 // Launch-geometry choice and dispatch: for M <= 8 the 16-byte-piece streaming
 // kernels (piece_b*.hip: dense, SwiGLU, affine b = 2, 4, 8), else the group
-// streaming or tiled VALU kernels (proj_b*.hip); matrix-core kernels
-// (mfma_*.hip) for dense and SwiGLU calls with M = 9..32 and for large-N
-// dense calls from M = 5 on; affine matrix-core kernels (affine_mfma*.hip) for
-// 2-, 4- and 8-bit codes; plus the code-unpack kernel.
+// streaming or tiled VALU kernels (proj_b*.hip); dense matrix-core kernels
+// (mfma_*.hip) for dense and SwiGLU calls with M = 9..32, for large-N dense
+// calls from M = 3 on and for wide small-N ones from M = 5 on; affine
+// matrix-core kernels for 2-, 4- and 8-bit codes (affine_mfma*.hip) and, where
+// a K fits their LDS ring, for every width from M = 5 on (affine_tile_b*.hip);
+// plus the code-unpack kernel.
 #include "affine_mfma.h"
 #include "affine_tile.h"
 #include "mfma_split.h"
@@ -126,7 +128,8 @@ bool choose_mfma_tile(bool swiglu, int M, int N, int K, LaunchCfg& c)
     return true;
 }
 
-// Small-N matrix-core geometry (M = 9..32, dense / SwiGLU): fewer than 2048
+// Small-N matrix-core geometry (dense / SwiGLU; used from M = 9, or from
+// M = 5 on matrices with N >= 4096 and K <= 2048): fewer than 2048
 // row tiles of 16 and K/32 k-steps that split evenly into pairs over at most
 // 16 wavefronts.  Depends on (N, K) only.
 bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)

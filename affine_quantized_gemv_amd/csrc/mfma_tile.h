@@ -1,4 +1,4 @@
-// Persistent matrix-core kernel for large-N dense projections at M = 9..32
+// Persistent matrix-core kernel for large-N dense projections at M = 3..32
 // (M padded to 16 or 32) with K = 512, 1024, 1536 or 2048, on gfx950.
 //
 // y^T[N, M] = W[N, K] . x^T[K, M] with v_mfma_f32_16x16x32_bf16 (operand
