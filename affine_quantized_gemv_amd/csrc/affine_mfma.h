@@ -45,6 +45,7 @@ namespace aqg {
 namespace detail {
 
 constexpr int kAffineMfmaThreads = 512;
+typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
 
 // 4 x 4 transpose of dwords across the four 16-lane rows: on return v[t] at
 // lane (row c, j) holds what v[c] held at lane (row t, j).
@@ -191,7 +192,12 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
     float* xs = reinterpret_cast<float*>(xh + (size_t)nkc * KSG * NB * 2 * LV);
     char* wbase0 = reinterpret_cast<char*>(xs + (size_t)KS * MT);
     char* wbase = wbase0 + (size_t)wave * affine_mfma_wave_bytes(GPS);
-    uint16_t* sbuf = reinterpret_cast<uint16_t*>(wbase);                        // [4][16] bf16
+    // the k-block's scales [group][row]: 4- and 8-bit as fp32 (each bf16 is
+    // written into the high half of a dword whose low half stays zero, so the
+    // dword reads back as the exact fp32 value with no conversion), 2-bit
+    // (8 groups) as bf16
+    constexpr bool SB32 = GPK <= 4;
+    uint16_t* sbuf = reinterpret_cast<uint16_t*>(wbase);                        // [GPK][16] bf16 / fp32
     uint16_t* btab = reinterpret_cast<uint16_t*>(wbase + 256);                  // [16][GPS]
     uint16_t* stab = btab + 16 * GPS;                                           // [16][GPS]
     float* pbuf = reinterpret_cast<float*>(wbase0 + (size_t)NW * affine_mfma_wave_bytes(GPS));
@@ -242,6 +248,12 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
     asm volatile("" : "+s"(cmask));      // no instruction: only hides the constants
     asm volatile("" : "+v"(cbias));
     const u32x4_t* xhj = xh + (size_t)j * KSG * NB * 2 * LV;
+    // vector stores of whole output quads: N % 4 == 0 and y addressable by a
+    // 32-bit buffer offset
+    const int esz = a.out_f32 ? 4 : 2;
+    const bool vec_store = a.N % 4 == 0 && (int64_t)a.M * a.N * esz < 0x7FFFFFF0;
+    const __amdgpu_buffer_rsrc_t ry = tile_rsrc(a.y, (int64_t)a.M * a.N * esz);
+    constexpr uint32_t kDrop = 0x80000000u;
 
     auto consume = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
@@ -252,7 +264,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
             // would be hoisted into the loop latch and wait there
             const int rel = GPK * (c_b - kb_lo);
             if constexpr (BITS == 4) {
-                sbuf[(lane & 3) * 16 + (lane >> 2)] = (uint16_t)sw[d];
+                sbuf[((lane & 3) * 16 + (lane >> 2)) * 2 + 1] = (uint16_t)sw[d];
                 const int ti2 = (lane >> 2) * GPS + rel + (lane & 3);
                 btab[ti2] = (uint16_t)bw[d];
                 stab[ti2] = (uint16_t)sw[d];
@@ -264,7 +276,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
                 reinterpret_cast<uint32_t*>(stab)[ti2] = sw[d];
             } else {
                 // lanes 32..63 repeat lanes 0..31 (same values, same places)
-                sbuf[(lane & 1) * 16 + ((lane >> 1) & 15)] = (uint16_t)sw[d];
+                sbuf[((lane & 1) * 16 + ((lane >> 1) & 15)) * 2 + 1] = (uint16_t)sw[d];
                 const int ti2 = ((lane >> 1) & 15) * GPS + rel + (lane & 1);
                 btab[ti2] = (uint16_t)bw[d];
                 stab[ti2] = (uint16_t)sw[d];
@@ -285,9 +297,15 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
 #pragma unroll
         for (int gi = 0; gi < GPK; ++gi) {
             // scales of rows 4c .. 4c + 3, group gi
-            const uint2 s4 = *reinterpret_cast<const uint2*>(sbuf + gi * 16 + 4 * c);
-            const float sc[4] = {__uint_as_float(s4.x << 16), __uint_as_float(s4.x & 0xFFFF0000u),
-                                 __uint_as_float(s4.y << 16), __uint_as_float(s4.y & 0xFFFF0000u)};
+            float sc[4];
+            if constexpr (SB32) {
+                const float4 s4 = *reinterpret_cast<const float4*>(sbuf + (gi * 16 + 4 * c) * 2);
+                sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
+            } else {
+                const uint2 s4 = *reinterpret_cast<const uint2*>(sbuf + gi * 16 + 4 * c);
+                sc[0] = __uint_as_float(s4.x << 16); sc[1] = __uint_as_float(s4.x & 0xFFFF0000u);
+                sc[2] = __uint_as_float(s4.y << 16); sc[3] = __uint_as_float(s4.y & 0xFFFF0000u);
+            }
             // the group's 16 codes of this lane as the A operands of its two k-steps
             u32x4_t A0, A1, H0, H1;
             if constexpr (BITS == 4) {
@@ -338,18 +356,36 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
             // lane (c, r) holds rows 4c .. 4c + 3 of column 16b + r
             if (nkc == 1) {
                 // whole tile: store now (staging would not coalesce either:
-                // consecutive lanes write different rows of y)
+                // consecutive lanes write different rows of y).  Lane (c, r)
+                // holds 4 consecutive outputs of row m of y: one 8- or
+                // 16-byte buffer store (dropped past the end) when N % 4 == 0
+                // keeps them aligned, else one store per output.
                 const int64_t n0 = c_tile * 16 + 4 * c;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const int m = 16 * b + r;
+                    float v[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float v = fmaf(-AffineMma<BITS>::OFF, accs[b][i], acc[b][i] + accb[b][i]);
-                        if (m < a.M && n0 + i < a.N) {
-                            const size_t o = (size_t)m * a.N + (size_t)(n0 + i);
-                            if (a.out_f32) reinterpret_cast<float*>(a.y)[o] = v;
-                            else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16_rne(v);
+                    for (int i = 0; i < 4; ++i) v[i] = fmaf(-AffineMma<BITS>::OFF, accs[b][i], acc[b][i] + accb[b][i]);
+                    if (vec_store) {
+                        const uint32_t off = (m < a.M && n0 < a.N) ? (uint32_t)(((int64_t)m * a.N + n0) * esz) : kDrop;
+                        if (a.out_f32) {
+                            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                                            __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                                                   ry, off, 0, 0);
+                        } else {
+                            const uint32_t p0 = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+                            const uint32_t p1 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+                            __builtin_amdgcn_raw_buffer_store_b64(u32x2v_t{p0, p1}, ry, off, 0, 0);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if (m < a.M && n0 + i < a.N) {
+                                const size_t o = (size_t)m * a.N + (size_t)(n0 + i);
+                                if (a.out_f32) reinterpret_cast<float*>(a.y)[o] = v[i];
+                                else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16_rne(v[i]);
+                            }
                         }
                     }
                 }
@@ -411,6 +447,8 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
         }
         for (int t = lane; t < 16 * GPS; t += 64)          // both tables, as 32-bit words
             reinterpret_cast<uint32_t*>(btab)[t] = 0u;
+        if constexpr (SB32)                                 // the fp32 scales' low halves
+            for (int t = lane; t < 16 * GPK; t += 64) reinterpret_cast<uint32_t*>(sbuf)[t] = 0u;
     }
     __syncthreads();
     for (int t = threadIdx.x; t < nkc * KSG * NB * LV; t += kAffineMfmaThreads) {
