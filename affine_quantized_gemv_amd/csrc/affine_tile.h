@@ -170,9 +170,12 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
         }
     };
 
-    static_for<0, NBUF>([&](auto Bc) __attribute__((always_inline)) {
-        if (decltype(Bc)::value < ntile) issue(decltype(Bc)::value, Bc);
-    });
+    // The first tile goes out before x is staged; the rest of the ring only
+    // after it: the wait for x (which the compiler places as a wait for every
+    // load in flight) then covers one tile rather than the whole ring, and
+    // the first tile's arithmetic overlaps the others' copies (with few
+    // tiles per workgroup this start is a large part of the call).
+    issue(0, Int<0>{});
 
     // x^T operands of this wavefront's 2 GW k-steps and the group sums
     u32x4_t xr[2 * GW][NB];
@@ -205,7 +208,10 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
         }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    barrier_only();
+    static_for<1, NBUF>([&](auto Bc) __attribute__((always_inline)) {
+        if (decltype(Bc)::value < ntile) issue(decltype(Bc)::value, Bc);
+    });
+    barrier_only();   // tile 0 is in LDS: every wavefront waited for its copies
 
     uint32_t cmask = WD::NATURAL ? WD::MASK : AffineMma<BITS == 2 || BITS == 4 ? BITS : 8>::MASK;
     uint32_t cmaskh = WD::MASK << 16, cbias = 0x43004300u;
@@ -322,19 +328,30 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
             else __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), ry, off, 0, 0);
         }
 
-        // Tile j + 1 must be in LDS before the next step (see mfma_tile.h):
-        // issued after its copies are that step's NSTO stores and, per step
-        // since, one tile's OPT copies (if the tile exists) and NSTO stores.
-        const int64_t nd64 = ntile - 2 - j;
-        const int nd = nd64 < 0 ? 0 : (nd64 > NBUF - 1 ? NBUF - 1 : (int)nd64);
+        // Tile j + 1 must be in LDS before the next step (see mfma_tile.h).
+        // Issued by step j + 1 - NBUF: after its copies came that step's NSTO
+        // stores and, per step since, one tile's OPT copies (if the tile
+        // exists) and NSTO stores.  Issued in the prologue (j = B < NBUF - 1):
+        // after its copies came the prologue's later tiles and, per step 0..B,
+        // one tile's copies (if it exists) and NSTO stores.
         const bool from_step = j + 1 >= NBUF;
-        static_for<0, NBUF>([&](auto Dc) __attribute__((always_inline)) {
-            constexpr int D = decltype(Dc)::value;
-            if (nd == D) {
-                if (from_step) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(D * L::OPT + NBUF * L::NSTO));
-                else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(D * L::OPT + L::NSTO));
-            }
-        });
+        if (from_step) {
+            const int64_t nd64 = ntile - 2 - j;
+            const int nd = nd64 < 0 ? 0 : (nd64 > NBUF - 1 ? NBUF - 1 : (int)nd64);
+            static_for<0, NBUF>([&](auto Dc) __attribute__((always_inline)) {
+                constexpr int D = decltype(Dc)::value;
+                if (nd == D) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(D * L::OPT + NBUF * L::NSTO));
+            });
+        } else {
+            const int64_t lim = ntile < NBUF ? ntile : NBUF;
+            const int64_t np = lim - (B + 2) > 0 ? lim - (B + 2) : 0;                    // later prologue tiles
+            const int64_t ns = ntile - NBUF > 0 ? (ntile - NBUF < B + 1 ? ntile - NBUF : B + 1) : 0;   // tiles issued by steps 0..B
+            const int q = (int)(np + ns);
+            static_for<0, NBUF>([&](auto Qc) __attribute__((always_inline)) {
+                constexpr int Q = decltype(Qc)::value;
+                if (q == Q) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(Q * L::OPT + (B + 1) * L::NSTO));
+            });
+        }
         barrier_only();
     };
 
@@ -348,7 +365,9 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
 
 // Ring depth for (bits, K) with 16-row tiles: about 40-100 KB of tiles in
 // flight, within one CU's LDS at M = 32 (8-bit K = 4096: M <= 16 only);
-// 0 = shape not served.  4-bit K = 1024 is left to the other kernels: its
+// 0 = shape not served.  4-bit K = 4096 keeps 2 tiles (72 KB): 3 measured
+// 13% slower on 14336 x 4096 at M = 8 and 16, where a workgroup has only 3-4
+// tiles; 2-bit K = 4096 keeps 3 (2 measured 10% slower).  4-bit K = 1024 is left to the other kernels: its
 // tiles are 9 KB, and each group's chain (LDS read, code placement, two
 // dependent MFMAs, the fp32 terms) is too short of bytes to keep the copies
 // streaming with 8 wavefronts per CU (measured 38-40 us on the 151936 x 1024
@@ -356,7 +375,7 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
 inline int affine_tile_nbuf(int bits, int K, int MT)
 {
     if (bits == 4 && K == 2048) return 3;
-    if (bits == 4 && K == 4096) return 3;
+    if (bits == 4 && K == 4096) return 2;
     if (bits == 2 && K == 2048) return 5;
     if (bits == 2 && K == 4096) return 3;
     if (bits == 8 && K == 1024) return 3;
@@ -399,7 +418,7 @@ hipError_t launch_affine_tile_mt(const ProjArgs& a, hipStream_t s)
     if constexpr (BITS == 4) {
         switch (a.K) {
             case 2048: return launch_affine_tile_one<4, MT, 2048, 1, 3>(a, s);
-            case 4096: return launch_affine_tile_one<4, MT, 4096, 1, 3>(a, s);
+            case 4096: return launch_affine_tile_one<4, MT, 4096, 1, 2>(a, s);
             default: return hipErrorInvalidValue;
         }
     } else if constexpr (BITS == 2) {

@@ -146,10 +146,11 @@ __global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
         }
     };
 
-    // the first NBUF tiles, then this wavefront's x^T operands
-    static_for<0, NBUF>([&](auto Bc) __attribute__((always_inline)) {
-        if (decltype(Bc)::value < ntile) issue(decltype(Bc)::value, Bc);
-    });
+    // The first tile, then this wavefront's x^T operands, then the rest of
+    // the ring: the wait for x (which the compiler places as a wait for
+    // every load in flight) covers one tile rather than the whole ring, and
+    // the first tile's arithmetic overlaps the others' copies.
+    issue(0, Int<0>{});
     u32x4_t xr[L::KSTEPS][NB];
     const int kw = wave * (L::K / NW);
 #pragma unroll
@@ -162,7 +163,10 @@ __global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
                 xr[s][b] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)m * L::K + kw + 32 * s + 8 * c);
         }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    barrier_only();
+    static_for<1, NBUF>([&](auto Bc) __attribute__((always_inline)) {
+        if (decltype(Bc)::value < ntile) issue(decltype(Bc)::value, Bc);
+    });
+    barrier_only();   // tile 0 is in LDS: every wavefront waited for its copies
 
     // reducer role of this thread: output (m, n) of each tile.  Every lane
     // issues exactly one buffer store per tile (lanes without an output
@@ -214,18 +218,27 @@ __global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
         // step's store, then per step since: the copy of a tile (CPW pieces,
         // if the tile exists) and one store.  Those may stay in flight: nd
         // copies (tiles j+2 .. j+NBUF that exist) and NBUF stores.  When it
-        // was issued before the loop it is complete already (the prologue
-        // waited for everything) and any count is safe.
-        const int64_t nd64 = ntile - 2 - j;
-        const int nd = nd64 < 0 ? 0 : (nd64 > NBUF - 1 ? NBUF - 1 : (int)nd64);
+        // was issued in the prologue (j = B < NBUF - 1), the operations after
+        // its copy are the prologue's later tiles and, per step 0..B, one
+        // tile's copy (if the tile exists) and one store.
         const bool from_step = j + 1 >= NBUF;
-        static_for<0, NBUF>([&](auto Dc) __attribute__((always_inline)) {
-            constexpr int D = decltype(Dc)::value;
-            if (nd == D) {
-                if (from_step) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(D * L::CPW + NBUF));
-                else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(D * L::CPW + 1));
-            }
-        });
+        if (from_step) {
+            const int64_t nd64 = ntile - 2 - j;
+            const int nd = nd64 < 0 ? 0 : (nd64 > NBUF - 1 ? NBUF - 1 : (int)nd64);
+            static_for<0, NBUF>([&](auto Dc) __attribute__((always_inline)) {
+                constexpr int D = decltype(Dc)::value;
+                if (nd == D) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(D * L::CPW + NBUF));
+            });
+        } else {
+            const int64_t lim = ntile < NBUF ? ntile : NBUF;
+            const int64_t np = lim - (B + 2) > 0 ? lim - (B + 2) : 0;                    // later prologue tiles
+            const int64_t ns = ntile - NBUF > 0 ? (ntile - NBUF < B + 1 ? ntile - NBUF : B + 1) : 0;   // tiles issued by steps 0..B
+            const int q = (int)(np + ns);
+            static_for<0, NBUF>([&](auto Qc) __attribute__((always_inline)) {
+                constexpr int Q = decltype(Qc)::value;
+                if (q == Q) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(Q * L::CPW + B + 1));
+            });
+        }
         barrier_only();
     };
 

@@ -445,7 +445,9 @@ def main():
     if args.counter_call:
         calls = [c for c in dense_decode_calls() if label_of(c) == args.counter_call]
         if not calls:
-            print("no dense decode call is labelled %r" % args.counter_call, file=sys.stderr)
+            calls = [c for c in other_calls() if label_of(c) == args.counter_call]
+        if not calls:
+            print("no call is labelled %r" % args.counter_call, file=sys.stderr)
             return 2
         for _ in range(8):
             calls[0]()
