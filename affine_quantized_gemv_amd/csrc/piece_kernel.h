@@ -118,6 +118,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int64
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kBufferFlags);
 }
 
+// s_waitcnt immediate for lgkmcnt(0) alone (vmcnt and expcnt at their
+// maximum, i.e. not waited for): gfx9-family encoding.
+__host__ __device__ constexpr int waitcnt_lgkm0_only() { return 0xF | 0x70 | (3 << 14); }
+
+// A workgroup barrier with no implied wait for loads in flight (the memory
+// clobber keeps the compiler from moving LDS accesses across it).
+__device__ __forceinline__ void piece_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int BITS, int MT, bool SWIGLU, bool XREG, int L, int J, int RD = PieceDepth<BITS, J, MT>::RD>
 __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 {
@@ -155,8 +163,8 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
     }
 
     // ---- x operands: registers or LDS (PRP piece slots per row, zero past PR).
-    // Filled after the first weight loads are issued (see the prologue), so
-    // their latencies overlap.
+    // Their loads go out before the first weight loads and their arithmetic
+    // after them (see the prologue), so the latencies overlap.
     uint4* xp = lds_p4;                                                   // [m][chunk][piece slot]
     float2* xc = reinterpret_cast<float2*>(lds_p4 + (size_t)MT * NCHP * PRP);  // [m][piece slot] (X, T)
     uint32_t xq[XREG ? J : 1][XREG ? MT : 1][NPP];
@@ -166,11 +174,17 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
     // synchronizes.  Affine operands take ~100 VALU instructions per piece,
     // so computing them per lane in every wavefront would delay the first
     // weights by microseconds.
-    auto stage_x = [&]() __attribute__((always_inline)) {
+    // `between` runs after the first round's x loads are issued and before
+    // they are used: the prologue issues the first weight loads there, so the
+    // operand arithmetic waits for x alone and overlaps the weights' latency,
+    // and the closing barrier waits for the LDS writes only.  Without weights
+    // in flight (`between` empty) it is a plain __syncthreads (a bare barrier
+    // there let the compiler keep staged x in registers across the loop on
+    // dense M = 8, 7.5 -> 9.4 us).
+    auto stage_x = [&](auto&& between, auto Early) __attribute__((always_inline)) {
         constexpr int XB = BITS == 0 ? 8 : 2;
         constexpr int KW = KPP / 2;                     // x words per piece
-        for (int t0 = threadIdx.x; t0 < MT * PRP; t0 += XB * kPieceThreads) {
-            uint32_t xw[XB][KW];
+        auto load_round = [&](int t0, uint32_t (&xw)[XB][KW]) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < XB; ++i) {
                 const int t = t0 + i * kPieceThreads;
@@ -184,6 +198,8 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                     xw[i][4 * w] = v.x; xw[i][4 * w + 1] = v.y; xw[i][4 * w + 2] = v.z; xw[i][4 * w + 3] = v.w;
                 }
             }
+        };
+        auto store_round = [&](int t0, uint32_t (&xw)[XB][KW]) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < XB; ++i) {
                 const int t = t0 + i * kPieceThreads;
@@ -197,10 +213,26 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                     xp[(m * NCHP + c) * PRP + p] = make_uint4(q[4 * c], q[4 * c + 1], q[4 * c + 2], q[4 * c + 3]);
                 if constexpr (BITS != 0) xc[m * PRP + p] = make_float2(X, Tc);
             }
+        };
+        if constexpr (decltype(Early)::value) {
+            // one round (the caller checks): every thread, loads predicated
+            uint32_t xw[XB][KW];
+            load_round(threadIdx.x, xw);
+            between();
+            store_round(threadIdx.x, xw);
+            __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_only());
+            piece_barrier();
+        } else {
+            for (int t0 = threadIdx.x; t0 < MT * PRP; t0 += XB * kPieceThreads) {
+                uint32_t xw[XB][KW];
+                load_round(t0, xw);
+                store_round(t0, xw);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     };
-    auto load_x = [&]() __attribute__((always_inline)) {
+    auto load_x = [&](auto&& between, auto EarlyC) __attribute__((always_inline)) {
+        constexpr int Early = decltype(EarlyC)::value;
         if constexpr (XREG && BITS == 0) {
             // dense operands are x itself: each lane loads its own
 #pragma unroll
@@ -213,7 +245,7 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                                   xq[j][m], xX[j][m], xT[j][m]);
                 }
         } else {
-            stage_x();
+            stage_x(between, Int<Early>{});
             if constexpr (XREG) {
                 // affine, registers: each lane copies its own operands
 #pragma unroll
@@ -416,17 +448,27 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 
     // prologue: RD rows, unconditionally (tiles past the wavefront's share --
     // all of them for a wavefront with no tiles -- read as zero or as valid
-    // rows; they are never consumed), and x.  Dense x in registers is loaded
-    // first: the loop reads it, and a load issued after the weights would
-    // make every wait in the loop a wait for all loads in flight.  Staged
-    // operands end in a barrier that waits for everything anyway, so there
-    // the weights go first and their latency overlaps the staging.
+    // rows; they are never consumed), and x.  x is loaded first: dense x in
+    // registers because the loop reads it, and a load issued after the
+    // weights would make every wait in the loop a wait for all loads in
+    // flight; staged operands of one round because their arithmetic then
+    // waits for x only and overlaps the weights' latency (the weights go out
+    // between the x loads and that arithmetic).
+    auto fetch_ring = [&]() __attribute__((always_inline)) {
+        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
+    };
+    // (staged x of more than one round -- dense M = 8 with long rows, ~32 KB
+    // per CU -- goes after the weights instead: loaded first it delayed the
+    // weight stream, 7.5 -> 9.1 us on 1536 x 4096)
+    constexpr bool XFIRST = (int64_t)MT * PRP <= (int64_t)(BITS == 0 ? 8 : 2) * kPieceThreads;
     if constexpr (XREG && BITS == 0) {
-        load_x();
-        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
+        load_x([]() {}, Int<0>{});
+        fetch_ring();
+    } else if constexpr (XFIRST) {
+        load_x(fetch_ring, Int<1>{});
     } else {
-        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
-        load_x();
+        fetch_ring();
+        load_x([]() {}, Int<0>{});
     }
     if (my_tiles == 0) return;
     int64_t bt = 0;
