@@ -608,6 +608,21 @@ def test_affine_tile_path(bits, N, K):
             assert np.array_equal(y, top[:M]), "M=%d" % M
 
 
+@pytest.mark.parametrize("bits,N", [(4, 8000), (2, 8000), (5, 8000), (2, 20000), (4, 20000)])
+def test_affine_tile_path_several_tiles_per_workgroup(bits, N):
+    """Tile path with 1-2 (N = 8000: 500 row tiles) and 4-5 (N = 20000) tiles
+    per workgroup at K = 4096, M = 16.  The ring's first tiles are issued in
+    two parts (tile 0 before x is staged, the rest after), so the waits of
+    the first steps depend on how many tiles a workgroup has; each count is
+    checked against the oracle."""
+    K = 4096
+    x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
+    xs = x[:16]
+    ref, A = oracle.gemv_affine(xs, aw.words, aw.scales, aw.biases, bits)
+    y = run_guarded(gemv_affine_gpu(xd[:16], wq, sd, bd, bits, 16), 16, N)
+    assert_within(y, ref, oracle.tolerance(A), "q%d tile 16x%dx%d" % (bits, N, K))
+
+
 @pytest.mark.parametrize("bits,K", [(2, 4096), (4, 2048), (8, 1024), (8, 4096), (3, 4096), (5, 4096), (6, 2048),
                                     (7, 4096)])
 def test_affine_tile_path_one_hot_exact(bits, K):
