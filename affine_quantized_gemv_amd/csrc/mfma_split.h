@@ -21,25 +21,29 @@ namespace detail {
 
 constexpr int kMfmaSplitMaxWaves = 16;
 
-// CSPLIT (MT = 16 kernel serving 17..32 columns): workgroup b takes column
-// block (b / 8) % 2 of row tile 8 (b / 16) + b % 8, so the two column blocks
-// of a tile run on one XCD (workgroup b runs on XCD b % 8) and the second
-// read of the tile's weights finds them in that XCD's L2.  Twice the
-// workgroups, each with half of the x^T traffic.
-template <int MT, bool SWIGLU, int SPW, bool CSPLIT = false>
+// CW > 0 (the 16-column kernel serving up to 2 CW columns): workgroup b
+// takes column block (b / 8) % 2, columns [CW, 2 CW) for block 1, of row tile
+// 8 (b / 16) + b % 8, so the two column blocks of a tile run on one XCD
+// (workgroup b runs on XCD b % 8) and the second read of the tile's weights
+// finds them in that XCD's L2.  Twice the workgroups, each with half of the
+// x^T traffic.  An output's MFMA chain does not depend on its column, so
+// results are those of the unsplit kernel.
+template <int MT, bool SWIGLU, int SPW, int CW = 0>
 __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(ProjArgs a)
 {
     extern __shared__ float lds_red[];
     int64_t tile = blockIdx.x;
-    if constexpr (CSPLIT) {
-        static_assert(MT == 16, "column blocks of 16");
+    if constexpr (CW > 0) {
+        static_assert(MT == 16 && CW <= 16, "column blocks of a 16-column kernel");
         const int b = blockIdx.x;
         tile = (int64_t)(b >> 4) * 8 + (b & 7);
         if (tile * 16 >= a.N) return;            // whole workgroup, before any barrier
         if ((b >> 3) & 1) {
-            a.x += (size_t)16 * a.K;
-            a.y = static_cast<char*>(a.y) + (size_t)16 * a.N * (a.out_f32 ? 4 : 2);
-            a.M -= 16;
+            a.x += (size_t)CW * a.K;
+            a.y = static_cast<char*>(a.y) + (size_t)CW * a.N * (a.out_f32 ? 4 : 2);
+            a.M -= CW;
+        } else if (a.M > CW) {
+            a.M = CW;
         }
     }
     constexpr int NB = MT / 16;
@@ -160,13 +164,13 @@ hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
 {
     const int nks = (a.K / 32) / SPW;
     const int64_t tiles = ((int64_t)a.N + 15) / 16;
-    if constexpr (MT == 32) {
-        // 17..32 columns with at most half as many row tiles as CUs: the
-        // 16-column kernel once per column block (q/k/v/o 1536 x 1536 at
-        // M = 32: 6.7 -> 5.2 us; down 1536 x 4096: 13.9 -> 9.9 us); with more
-        // tiles the second read of the weights costs more than it saves
-        // (up/gate 4096 x 1536: 7.2 -> 8.0 us), so both blocks stay in one
-        // workgroup
+    // With at most half as many row tiles as CUs, M = 17..32 runs the
+    // 16-column kernel once per 16-column block and M = 9..16 once per
+    // 8-column block (q/k/v/o 1536 x 1536 at M = 32: 6.7 -> 5.2 us; down
+    // 1536 x 4096: 13.9 -> 9.9 us).  With more tiles the second read of the
+    // weights costs more than it saves (up/gate 4096 x 1536 at M = 32: 7.2 ->
+    // 8.0 us), so the columns stay in one workgroup.
+    if (MT == 32 || a.M > 8) {
         int dev = 0, cus = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -174,7 +178,10 @@ hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
         if (2 * tiles <= cus) {
             const size_t lds = (size_t)nks * (SW ? 2 : 1) * 4 * 65 * 4;
             const int64_t blocks = (tiles + 7) / 8 * 16;
-            hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, true>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+            if constexpr (MT == 32)
+                hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 16>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+            else
+                hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 8>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
             return hipGetLastError();
         }
     }
