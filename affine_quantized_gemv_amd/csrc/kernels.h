@@ -26,7 +26,7 @@ struct ProjArgs {
 };
 
 enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6,
-            PATH_MFMA_TILE = 7, PATH_AFFINE_TILE = 8 };
+            PATH_MFMA_TILE = 7, PATH_AFFINE_TILE = 8, PATH_AFFINE_SPLIT = 9 };
 
 // Launch geometry chosen for a call.
 struct LaunchCfg {
@@ -79,6 +79,11 @@ hipError_t launch_mfma_tile(const ProjArgs& a, const LaunchCfg& c, hipStream_t s
 // or 8 (affine_tile_b*.hip).
 template <int BITS>
 hipError_t launch_affine_tile(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+// Affine matrix-core launcher for small N, k split over one workgroup per
+// 16-row tile, BITS = 2, 4 or 8 (affine_split.hip).
+template <int BITS>
+hipError_t launch_affine_split(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // Affine matrix-core launcher, BITS = 2, 4 or 8 (affine_mfma*.hip).
 template <int BITS>

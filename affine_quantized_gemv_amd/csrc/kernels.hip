@@ -3,10 +3,12 @@
 // streaming or tiled VALU kernels (proj_b*.hip); dense matrix-core kernels
 // (mfma_*.hip) for dense and SwiGLU calls with M = 9..32, for large-N dense
 // calls from M = 3 on and for wide small-N ones from M = 5 on; affine
-// matrix-core kernels for 2-, 4- and 8-bit codes (affine_mfma*.hip) and, where
-// a K fits their LDS ring, for every width from M = 5 on (affine_tile_b*.hip);
-// plus the code-unpack kernel.
+// matrix-core kernels for 2-, 4- and 8-bit codes (affine_mfma*.hip; on small
+// matrices from M = 5 on, affine_split.hip) and, where a K fits their LDS
+// ring, for every width from M = 5 on (affine_tile_b*.hip); plus the
+// code-unpack kernel.
 #include "affine_mfma.h"
+#include "affine_split.h"
 #include "affine_tile.h"
 #include "mfma_split.h"
 #include "mfma_tile.h"
@@ -143,6 +145,25 @@ bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)
     c.KT = K;
     c.nwaves = (K / 32) / spw;
     c.blocks = (int)T;
+    c.R = 1;
+    return true;
+}
+
+// Small-N affine matrix-core geometry (2-, 4- and 8-bit codes; affine_split.h):
+// whole 128-byte k-blocks per row split over at most 16 wavefronts; at most
+// 256 row tiles of 16 for M = 5..16 and 128 for M = 17..32, which run in
+// two 16-column workgroups per tile (4096 x 4096 at M = 32: 14.5-25 us that
+// way, twice as many workgroups each staging x^T of K = 4096).  Depends on
+// (bits, N, K) and the column bucket, and every M of a bucket computes each
+// output the same way (both buckets alike with at most 128 tiles).
+bool choose_affine_split(int bits, int M, int N, int K, LaunchCfg& c)
+{
+    c = LaunchCfg{};
+    const int64_t tiles = ((int64_t)N + 15) / 16;
+    if (M < 5 || M > 32 || tiles > (M > 16 ? 128 : 256) || detail::affine_split_kpw(bits, K) == 0) return false;
+    c.path = PATH_AFFINE_SPLIT;
+    c.MT = M <= 16 ? 16 : 32;
+    c.KT = K;
     c.R = 1;
     return true;
 }
@@ -341,6 +362,11 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     // wins.
     // Affine tiles through LDS from M = 5 on where they serve (K = 2048 / 4096
     // and 8-bit K = 1024: 14336 x 4096 at M = 16 54.7 -> 18.4 us at 4 bits).
+    // Small matrices from M = 5 on: one workgroup per tile with every load
+    // issued at once (4-bit 1024 x 3584 at M = 16: 11.8 -> 7.3 us; 1024 x
+    // 1024: 7.4 -> 4.0 us; 8-bit 4096 x 4096: 15.1 -> 14.2 us; 2- and 4-bit
+    // 4096 x 4096 level with the tile kernel).
+    if (!swiglu && choose_affine_split(bits, M, N, K, c)) return c;
     if (!swiglu && M >= 5 && choose_affine_tile(bits, M, N, K, c)) return c;
     if (!swiglu && M >= 3 && choose_affine_mfma(bits, M, N, K, c) &&
         (M > 8 || (bits == 4 && c.ksplit_log2 == 0))) return c;
@@ -362,6 +388,15 @@ hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg
             case 6: return launch_affine_tile<6>(a, c, s);
             case 7: return launch_affine_tile<7>(a, c, s);
             case 8: return launch_affine_tile<8>(a, c, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (c.path == PATH_AFFINE_SPLIT) {
+        if (swiglu) return hipErrorInvalidValue;
+        switch (bits) {
+            case 2: return launch_affine_split<2>(a, c, s);
+            case 4: return launch_affine_split<4>(a, c, s);
+            case 8: return launch_affine_split<8>(a, c, s);
             default: return hipErrorInvalidValue;
         }
     }

@@ -514,9 +514,9 @@ def test_affine4_large_n_one_hot_every_group_position_m16():
         assert np.array_equal(y, codes[:, c].T.astype(np.float64)), "cols %s" % c
 
 
-@pytest.mark.parametrize("N,K", [(1000, 1792), (3000, 512), (700, 3584), (2000, 256), (1024, 1024)])
+@pytest.mark.parametrize("N,K", [(5000, 1792), (6000, 512), (4500, 3584), (7000, 256), (5024, 1024)])
 def test_affine4_matrix_core_k_split(N, K):
-    """4-bit, fewer than 2048 row tiles: the matrix-core path splits K over a
+    """4-bit, 257..2047 row tiles: the matrix-core path splits K over a
     workgroup's wavefronts (chunks of unequal length when the 256-k blocks do
     not divide evenly) and sums the partial tiles in chunk order.  Ragged N;
     M = 9 and 16 against the oracle and bit for bit against each other, M = 32
@@ -540,10 +540,10 @@ def test_affine4_matrix_core_k_split(N, K):
 
 
 def test_affine4_k_split_one_hot_every_group_position_m16():
-    """K split (1000 x 1792: 7 blocks of 256 k in 4 chunks), s = 1, bias = 0,
+    """K split (5000 x 1792: 7 blocks of 256 k in 4 chunks), s = 1, bias = 0,
     one-hot x: y = q exactly at every position of a group, whichever chunk
     holds it (the other chunks add exact zeros)."""
-    N, K = 1000, 1792
+    N, K = 5000, 1792
     words = synth.random_words((N, K // 8), 85, "oh16k")
     codes = oracle.unpack(words, 4, K)
     G = K // 64
@@ -567,7 +567,7 @@ def affine_mma_case(bits, N, K):
 
 
 @pytest.mark.parametrize("bits", [2, 8])
-@pytest.mark.parametrize("N,K", [(40001, 1024), (1000, 1536), (700, 4096), (3000, 512)])
+@pytest.mark.parametrize("N,K", [(40001, 1024), (5000, 1536), (4500, 4096), (6000, 512)])
 def test_affine_matrix_core_2_and_8_bit(bits, N, K):
     """2- and 8-bit codes on the matrix core (8-bit codes as two nibble
     chains): N = 40001 streams whole tiles, the others split K.  M = 9, 16
@@ -586,8 +586,60 @@ def test_affine_matrix_core_2_and_8_bit(bits, N, K):
         assert np.array_equal(y16, y32[:16])
 
 
-@pytest.mark.parametrize("bits,N,K", [(4, 3001, 2048), (4, 2049, 4096), (2, 1000, 4096), (2, 3000, 2048),
-                                      (8, 2000, 1024), (8, 1000, 2048), (8, 999, 4096), (3, 1000, 4096),
+@pytest.mark.parametrize("bits,N,K", [(4, 1000, 1024), (4, 3001, 2048), (4, 700, 3584), (4, 4090, 4096),
+                                      (4, 300, 512), (4, 129, 256), (2, 1000, 4096), (2, 3000, 2048),
+                                      (2, 999, 1536), (8, 2000, 1024), (8, 999, 4096), (8, 1000, 2048)])
+def test_affine_split_path(bits, N, K):
+    """Small matrices (at most 256 row tiles) on the matrix core with one
+    workgroup per tile and K split over its wavefronts (8-bit K = 4096: two
+    k-blocks per wavefront), M = 5..16, and M = 17..32 with at most 128 tiles:
+    M = 9..16 in two 8-column workgroups where the tiles are few, M = 17..32
+    in two 16-column ones.  Ragged last tile; every M against the oracle
+    (bf16 = RNE of fp32, no write outside the output) and bit for bit equal to
+    the first rows of its bucket's widest call (16 or 32 rows), and the two
+    buckets to each other where both take this path."""
+    x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
+    ref, A = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
+    tops = {}
+    for M in (16, 5, 8, 9, 32, 17):
+        y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, M), M, N)
+        assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q%d split %dx%dx%d" % (bits, M, N, K))
+        b = 16 if M <= 16 else 32
+        if b not in tops:
+            tops[b] = y
+        else:
+            assert np.array_equal(y, tops[b][:M]), "M=%d" % M
+    if (N + 15) // 16 <= 128:
+        assert np.array_equal(tops[16], tops[32][:16])
+
+
+@pytest.mark.parametrize("bits,K", [(2, 4096), (4, 1024), (4, 3584), (8, 1024), (8, 4096)])
+def test_affine_split_path_one_hot_exact(bits, K):
+    """Split path (N = 1001: 63 row tiles), s = 1, bias = 0, one-hot x: y = q
+    exactly with the ones at every position of a group, in every wavefront's
+    k-blocks, for M = 16 (8-column workgroups) and 32 (16-column ones); then
+    s = 2, bias = -1 on the same codes: y = 2 q - 1 exactly."""
+    N = 1001
+    words = synth.random_words((N, K * bits // 32), 89, "soh/%d/%d" % (bits, K))
+    codes = oracle.unpack(words, bits, K)
+    G = K // 64
+    cols = np.array([((r * 5 + 3) % G) * 64 + r for r in range(64)])
+    wq = u32_dev(words)
+    for sv, bv in ((0x3F80, 0x0000), (0x4000, 0xBF80)):
+        sd = bf16_dev(np.full((N, G), sv, np.uint16))
+        bd = bf16_dev(np.full((N, G), bv, np.uint16))
+        want_s, want_b = oracle.bf16_to_f64(np.array([sv], np.uint16))[0], oracle.bf16_to_f64(np.array([bv], np.uint16))[0]
+        for MC in (16, 32):
+            for c0 in range(0, 64, MC):
+                c = cols[c0:c0 + MC]
+                x = np.zeros((MC, K), np.uint16)
+                x[np.arange(MC), c] = 0x3F80
+                y = run_guarded(gemv_affine_gpu(bf16_dev(x), wq, sd, bd, bits, MC), MC, N)
+                assert np.array_equal(y, (want_s * codes[:, c] + want_b).T.astype(np.float64)), "M=%d cols %s" % (MC, c)
+
+
+@pytest.mark.parametrize("bits,N,K", [(4, 4201, 2048), (4, 4113, 4096), (2, 4105, 4096), (2, 4300, 2048),
+                                      (8, 4150, 1024), (8, 4111, 2048), (8, 4099, 4096), (3, 1000, 4096),
                                       (5, 1001, 4096), (6, 999, 2048), (6, 500, 4096), (7, 777, 4096)])
 def test_affine_tile_path(bits, N, K):
     """Affine tiles copied into LDS (2/4-bit K = 2048, 4096; 8-bit K = 1024,
@@ -627,9 +679,10 @@ def test_affine_tile_path_several_tiles_per_workgroup(bits, N):
                                     (7, 4096)])
 def test_affine_tile_path_one_hot_exact(bits, K):
     """s = 1, bias = 0, one-hot x: y = q exactly, with the ones at every
-    position of a group, in every wavefront's share of K (M = 16, tile path);
-    then s = 2, bias = -1 on the same codes: y = 2 q - 1 exactly."""
-    N = 1001
+    position of a group, in every wavefront's share of K (M = 16, tile path:
+    more than 256 row tiles); then s = 2, bias = -1 on the same codes: y =
+    2 q - 1 exactly."""
+    N = 4117
     words = synth.random_words((N, K * bits // 32), 88, "toh/%d/%d" % (bits, K))
     codes = oracle.unpack(words, bits, K)
     G = K // 64
@@ -648,7 +701,7 @@ def test_affine_tile_path_one_hot_exact(bits, K):
 
 
 @pytest.mark.parametrize("bits", [2, 8])
-@pytest.mark.parametrize("N,K", [(33000, 1024), (1000, 1536)])
+@pytest.mark.parametrize("N,K", [(33000, 1024), (5000, 1536)])
 def test_affine_matrix_core_2_and_8_bit_one_hot_m16(bits, N, K):
     """s = 1, bias = 0, one-hot x: y = q exactly at all 64 positions of a
     group (each in a different group), on the matrix core, whole tiles and
