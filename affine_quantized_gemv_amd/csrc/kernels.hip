@@ -348,12 +348,17 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     // 4 or 8); M <= 2 stays on the latter (~45 us).
     if (bits == 0 && M >= 3 && choose_mfma_tile(swiglu, M, N, K, c)) return c;
     if (bits == 0 && M > 8 && choose_mfma_stream(swiglu, M, N, K, c)) return c;
-    // Small-N matrix core from M = 5 on for N >= 4096, K <= 2048 (SwiGLU
+    // Small-N matrix core from M = 3 on for N >= 4096, K <= 2048 (SwiGLU
     // 2 x 4096 x 1536: 8.1 us at M = 16 against 10.6 us for the dot-product
-    // kernel at M = 8; up/gate 4096 x 1536: 5.7 against 6.4 us); narrower or
-    // longer matrices keep the dot-product kernel up to M = 8 (q/k/v/o 5.0
-    // against 5.3 us, down 1536 x 4096 7.4 against 10.0 us).
-    if (bits == 0 && (M > 8 || (M >= 5 && N >= 4096 && K <= 2048)) && choose_mfma_split(swiglu, M, N, K, c)) return c;
+    // kernel at M = 8, 7.0 us at M = 8 against 7.8 us for the latter at M =
+    // 4; up/gate 4096 x 1536: 5.7 against 6.4 us) and from M = 5 on for at
+    // most 128 row tiles with K <= 2048 (two 4-column workgroups per tile);
+    // longer matrices keep the dot-product kernel up to M = 8 (down 1536 x
+    // 4096: 7.4 against 10.0 us).
+    if (bits == 0 &&
+        (M > 8 || (M >= 3 && N >= 4096 && K <= 2048) || (M >= 5 && K <= 2048 && ((int64_t)N + 15) / 16 <= 128)) &&
+        choose_mfma_split(swiglu, M, N, K, c))
+        return c;
     // Affine matrix core: its cost does not grow with M (up to 16), the
     // dot-product kernels' does.  4-bit from M = 3 on (measured on the 151936
     // x 1024 LM head: 27.5 us at any M <= 16 against 32 us for the piece

@@ -1,5 +1,6 @@
 // Matrix-core kernel for small-N dense projections and fused SwiGLU at
-// M = 9..32 (from M = 5 on wide matrices; M padded to 16 or 32) on gfx950:
+// M = 9..32 (from M = 3 on wide matrices, from M = 5 on short ones; M padded
+// to 16 or 32) on gfx950:
 // one workgroup per 16-row tile, K split over NKS wavefronts.
 //
 // A small matrix (a few MB) is latency-bound: what matters is how soon every
@@ -170,7 +171,8 @@ hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
     // 1536 x 4096: 13.9 -> 9.9 us).  With more tiles the second read of the
     // weights costs more than it saves (up/gate 4096 x 1536 at M = 32: 7.2 ->
     // 8.0 us), so the columns stay in one workgroup.
-    if (MT == 32 || a.M > 8) {
+    // M = 5..8 likewise once per 4-column block.
+    if (MT == 32 || a.M > 4) {
         int dev = 0, cus = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -180,8 +182,10 @@ hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
             const int64_t blocks = (tiles + 7) / 8 * 16;
             if constexpr (MT == 32)
                 hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 16>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
-            else
+            else if (a.M > 8)
                 hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 8>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+            else
+                hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 4>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
             return hipGetLastError();
         }
     }
