@@ -530,10 +530,11 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
 }
 
 // k-blocks in flight per wavefront and workgroups per CU: on the 151936 x
-// 1024 LM head at M = 16, depth 4 with 2 workgroups (16 wavefronts) per CU
-// measured fastest (3 workgroups, i.e. more bytes in flight, ~20% slower).
+// 1024 LM head at M = 16, depth 4 with one workgroup (8 wavefronts, ~64 KB
+// in flight) per CU measured fastest (25.1 us; 2 workgroups 26.1 us, level
+// at M = 4; 3 workgroups ~20% slower).
 constexpr int kAffineMfmaDepth = 4;
-constexpr int kAffineMfmaWgPerCu = 2;
+constexpr int kAffineMfmaWgPerCu = 1;
 
 // LDS bytes of one workgroup with nkc K-chunks per tile and, for nkc > 1,
 // tmax tiles per slot staged as partials.

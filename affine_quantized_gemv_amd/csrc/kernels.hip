@@ -1,8 +1,9 @@
 // Launch-geometry choice and dispatch: for M <= 8 the 16-byte-piece streaming
 // kernels (piece_b*.hip: dense, SwiGLU, affine b = 2, 4, 8), else the group
 // streaming or tiled VALU kernels (proj_b*.hip); dense matrix-core kernels
-// (mfma_*.hip) for dense and SwiGLU calls with M = 9..32, for large-N dense
-// calls from M = 3 on and for wide small-N ones from M = 5 on; affine
+// (mfma_*.hip) for dense and SwiGLU calls with M = 9..32, for large-N and
+// wide small-N ones from M = 3 on and for short ones with K <= 2048 from
+// M = 5 on; affine
 // matrix-core kernels for 2-, 4- and 8-bit codes (affine_mfma*.hip; on small
 // matrices from M = 5 on, affine_split.hip) and, where a K fits their LDS
 // ring, for every width from M = 5 on (affine_tile_b*.hip); plus the
