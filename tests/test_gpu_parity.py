@@ -218,6 +218,35 @@ def test_dense_rows_independent_of_m(shape):
         assert np.array_equal(yM, want), "M=%d" % M
 
 
+def test_dense_small_n_column_pairs_m5_to_8():
+    """q/k/v/o 1536 x 1536 (96 row tiles) at M = 5..8: two 4-column
+    workgroups per tile, the second with M - 4 = 1..3 columns.  Each M
+    against the oracle and bit for bit equal to the first rows of the 8-row
+    call (an output's chain does not depend on its column block)."""
+    name, N, K = synth.DENSE_DECODE_SHAPES[0]
+    x, W, xd, Wd = dense_case(synth.CFG_DENSE_DECODE, name, N, K)
+    ref, A = dense_ref(synth.CFG_DENSE_DECODE, name, N, K)
+    y8 = None
+    for M in (8, 5, 6, 7):
+        y = run_guarded(lambda out: aqg.gemv_bf16(xd[:M], Wd, out=out), M, N)
+        assert_within(y, ref[:M], oracle.tolerance(A[:M]), "dense %dx%dx%d" % (M, N, K))
+        if y8 is None:
+            y8 = y
+        else:
+            assert np.array_equal(y, y8[:M]), "M=%d" % M
+
+
+@pytest.mark.parametrize("bits,N,K", [(4, 1000, 3584), (8, 999, 4096), (2, 3000, 2048)])
+def test_affine_split_deterministic(bits, N, K):
+    """The split path's partial tiles are summed in a fixed order: repeated
+    calls give the same bits (M = 5, 16 and 32)."""
+    x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
+    for M in (5, 16, 32):
+        a = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
+        b = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
+        assert np.array_equal(a, b), "M=%d" % M
+
+
 def test_swiglu_rows_independent_of_m():
     """2 x 4096 x 1536: the vector ALU path (M <= 2) matches one-row calls bit
     for bit, the matrix-core path (M = 3..32) the 32-row call."""
