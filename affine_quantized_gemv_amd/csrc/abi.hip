@@ -85,7 +85,8 @@ int run_projection(int bits, bool swiglu, const void* x, const void* w0, const v
     if (!w0 || (swiglu && !w1) || (bits && (!scales || !biases))) return AQG_ERR_INVALID_ARG;
     if (bits == 0 ? (K % 8 != 0) : (K % 64 != 0)) return AQG_ERR_UNSUPPORTED;
     if (!aligned(w0, 16) || (w1 && !aligned(w1, 16))) return AQG_ERR_ALIGNMENT;
-    if (bits && (!aligned(scales, 2) || !aligned(biases, 2))) return AQG_ERR_ALIGNMENT;
+    // the matrix-core kernels read scales and biases in 4- to 16-byte pieces
+    if (bits && (!aligned(scales, 4) || !aligned(biases, 4))) return AQG_ERR_ALIGNMENT;
     const int kind = swiglu ? AQG_KIND_SWIGLU : bits;
     if (workspace_bytes < aqg_workspace_bytes(kind, M, N, K)) return AQG_ERR_INVALID_ARG;
     (void)workspace;
@@ -142,8 +143,8 @@ const char* aqg_status_string(int status)
                                          "short workspace or overlapping output";
         case AQG_ERR_UNSUPPORTED: return "AQG_ERR_UNSUPPORTED: M > 32, K not a multiple of 8 (dense) or 64 "
                                          "(affine), or bits outside 2..8";
-        case AQG_ERR_ALIGNMENT: return "AQG_ERR_ALIGNMENT: x and W/Wq must be 16-byte aligned, other arrays "
-                                       "aligned to their element size";
+        case AQG_ERR_ALIGNMENT: return "AQG_ERR_ALIGNMENT: x and W/Wq must be 16-byte aligned, scales and "
+                                       "biases 4-byte aligned, other arrays aligned to their element size";
         case AQG_ERR_LAUNCH: return "AQG_ERR_LAUNCH: the kernel launch failed";
         case AQG_ERR_DEVICE: return "AQG_ERR_DEVICE: no current HIP device, or it is not gfx950";
         default: return "unknown aqg status";

@@ -37,8 +37,9 @@
  *  - Validation happens on the host before any HIP call.  On any status other
  *    than AQG_OK nothing has been enqueued and the outputs are untouched.
  *  - M in [1, 32]; N, K >= 1.  Dense: K % 8 == 0.  Affine: K % 64 == 0.
- *    x and W/Wq must be 16-byte aligned; y, scales, biases, codes naturally
- *    aligned for their element type.  y must not overlap any input.
+ *    x and W/Wq must be 16-byte aligned; scales and biases 4-byte aligned
+ *    (read in 4- to 16-byte pieces); y and codes naturally aligned for their
+ *    element type.  y must not overlap any input.
  *  - out_dtype AQG_OUT_F32 writes the fp32 sums; AQG_OUT_BF16 writes exactly
  *    the round-to-nearest-even bf16 of the values the same call would write
  *    with AQG_OUT_F32 (kernels are deterministic).

@@ -94,6 +94,8 @@ def test_dense_validation(lib, kwargs, status):
     (dict(M=40), aqg.AQG_ERR_UNSUPPORTED),
     (dict(Wq=B16 + 8), aqg.AQG_ERR_ALIGNMENT),
     (dict(s=D16 + 1), aqg.AQG_ERR_ALIGNMENT),
+    (dict(s=D16 + 2), aqg.AQG_ERR_ALIGNMENT),         # scales and biases: 4-byte aligned
+    (dict(b=E16 + 2), aqg.AQG_ERR_ALIGNMENT),
     (dict(y=D16), aqg.AQG_ERR_INVALID_ARG),           # output overlaps scales
 ])
 def test_affine_validation(lib, kwargs, status):
