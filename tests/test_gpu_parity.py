@@ -617,11 +617,12 @@ def test_affine_matrix_core_2_and_8_bit(bits, N, K):
 
 @pytest.mark.parametrize("bits,N,K", [(4, 1000, 1024), (4, 3001, 2048), (4, 700, 3584), (4, 4090, 4096),
                                       (4, 300, 512), (4, 129, 256), (2, 1000, 4096), (2, 3000, 2048),
-                                      (2, 999, 1536), (8, 2000, 1024), (8, 999, 4096), (8, 1000, 2048)])
+                                      (2, 999, 1536), (8, 2000, 1024), (8, 999, 4096), (8, 1000, 2048),
+                                      (4, 1000, 8192), (2, 500, 8192)])
 def test_affine_split_path(bits, N, K):
     """Small matrices (at most 256 row tiles) on the matrix core with one
-    workgroup per tile and K split over its wavefronts (8-bit K = 4096: two
-    k-blocks per wavefront), M = 5..16, and M = 17..32 with at most 128 tiles:
+    workgroup per tile and K split over its wavefronts (8-bit K = 4096 and
+    4-bit K = 8192: two k-blocks per wavefront), M = 5..16, and M = 17..32 with at most 128 tiles:
     M = 9..16 in two 8-column workgroups where the tiles are few, M = 17..32
     in two 16-column ones.  Ragged last tile; every M against the oracle
     (bf16 = RNE of fp32, no write outside the output) and bit for bit equal to
