@@ -38,7 +38,7 @@ _lock = threading.Lock()
 
 __all__ = [
     "build", "bf16_to_f64", "f32_to_bf16", "pack", "unpack", "gemv_bf16",
-    "gemv_affine", "swiglu_bf16", "argmax", "set_threads", "max_threads",
+    "gemv_affine", "swiglu_bf16", "swiglu_affine", "argmax", "set_threads", "max_threads",
     "tolerance", "swiglu_tolerance",
 ]
 
@@ -73,6 +73,8 @@ def bind(path: str):
     lib.oracle_gemv_affine.restype = ctypes.c_int
     lib.oracle_gemv_affine.argtypes = [ctypes.c_int, P, P, P, P, P, P, I64, I64, I64]
     lib.oracle_swiglu_bf16.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64]
+    lib.oracle_swiglu_affine.restype = ctypes.c_int
+    lib.oracle_swiglu_affine.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64]
     lib.oracle_argmax.argtypes = [P, P, I64, I64]
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -187,6 +189,27 @@ def swiglu_bf16(x, Wg, Wu):
     r = {k: np.empty((M, N), np.float64) for k in ("out", "g", "u", "Ag", "Au")}
     _load().oracle_swiglu_bf16(_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(r["out"]), _ptr(r["g"]),
                                _ptr(r["u"]), _ptr(r["Ag"]), _ptr(r["Au"]), M, N, K)
+    return r
+
+
+def swiglu_affine(x, gate, up, bits: int):
+    """Unfused SwiGLU over two affine b-bit matrices.
+
+    gate, up: (words uint32[N, K*bits/32], scales bf16[N, K/64], biases
+    bf16[N, K/64]) each.  Returns dict(out, g, u, Ag, Au), all fp64 [M, N].
+    """
+    x = _c(x, np.uint16)
+    gw, gs, gb = (_c(gate[0], np.uint32), _c(gate[1], np.uint16), _c(gate[2], np.uint16))
+    uw, us, ub = (_c(up[0], np.uint32), _c(up[1], np.uint16), _c(up[2], np.uint16))
+    M, K = x.shape
+    N = gw.shape[0]
+    assert gw.shape == uw.shape == (N, K * bits // 32)
+    assert gs.shape == gb.shape == us.shape == ub.shape == (N, K // 64)
+    r = {k: np.empty((M, N), np.float64) for k in ("out", "g", "u", "Ag", "Au")}
+    if _load().oracle_swiglu_affine(bits, _ptr(x), _ptr(gw), _ptr(gs), _ptr(gb), _ptr(uw), _ptr(us),
+                                    _ptr(ub), _ptr(r["out"]), _ptr(r["g"]), _ptr(r["u"]),
+                                    _ptr(r["Ag"]), _ptr(r["Au"]), M, N, K):
+        raise ValueError("bad bits or K")
     return r
 
 

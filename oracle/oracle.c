@@ -230,6 +230,52 @@ void oracle_swiglu_bf16(const uint16_t *x, const uint16_t *Wg, const uint16_t *W
     }
 }
 
+/* Unfused SwiGLU chain over two affine b-bit matrices (the gate and up
+ * projections of an MLX affine checkpoint's MLP), in double, no intermediate
+ * rounding:
+ *   g[m][n] = sum_k x[m][k] * (sg[n][k/64] * qg[n][k] + bg[n][k/64]),
+ *   u[m][n] = the same with the up matrix,
+ *   out = g / (1 + exp(-g)) * u.
+ * Each matrix has its own codes, scales and biases in the layout of
+ * oracle_gemv_affine; both share the width.  Ag, Au = sum_k |w x|.  g, u,
+ * Ag, Au may be NULL.  Returns 0 on success, 1 on a shape the format does
+ * not allow.  (AstrAI decode_linear_benchmark.md, commit message: the fused
+ * up/gate SwiGLU against the unfused chain; TensorFold PR #849: the affine
+ * format of the MLP modules.) */
+int oracle_swiglu_affine(int bits, const uint16_t *x,
+                         const uint32_t *Wgq, const uint16_t *sg, const uint16_t *bg,
+                         const uint32_t *Wuq, const uint16_t *su, const uint16_t *bu,
+                         double *out, double *g, double *u, double *Ag, double *Au,
+                         int64_t M, int64_t N, int64_t K)
+{
+    if (!bits_ok(bits) || K % 64 != 0)
+        return 1;
+    int64_t wpr = K * bits / 32, gpr = K / 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double ga = 0.0, ua = 0.0, gaa = 0.0, uaa = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double xv = oracle_bf16_to_double(x[m * K + k]);
+                double pg = dequant(bits, Wgq + n * wpr, sg + n * gpr, bg + n * gpr, k) * xv;
+                double pu = dequant(bits, Wuq + n * wpr, su + n * gpr, bu + n * gpr, k) * xv;
+                ga += pg;
+                ua += pu;
+                gaa += fabs(pg);
+                uaa += fabs(pu);
+            }
+            double silu = ga / (1.0 + exp(-ga));
+            int64_t i = m * N + n;
+            out[i] = silu * ua;
+            if (g) g[i] = ga;
+            if (u) u[i] = ua;
+            if (Ag) Ag[i] = gaa;
+            if (Au) Au[i] = uaa;
+        }
+    }
+    return 0;
+}
+
 /* Row-wise argmax over y[M][N]; the lowest index wins on equal values. */
 void oracle_argmax(const double *y, int64_t *idx, int64_t M, int64_t N)
 {

@@ -368,3 +368,166 @@ def test_oracle_is_thread_count_independent():
     finally:
         oracle.set_threads(n0)
     assert np.array_equal(y1, y2)
+
+
+# ------------------------------------------------- SwiGLU abs sums and bound
+
+def test_swiglu_abs_sums_pinned():
+    """Ag, Au (which size the SwiGLU tolerance) are sum_k |w x| of each stream:
+    equal to numpy's |x| |W|^T, unchanged by flipping the sign of x or of W,
+    never below |g|, |u|, and equal to g, u when every product is >= 0."""
+    M, N, K = 3, 24, 512
+    x = synth.normal_bf16((M, K), 1.0, 82, "sa/x")
+    Wg = synth.normal_bf16((N, K), 0.02, 82, "sa/g")
+    Wu = synth.normal_bf16((N, K), 0.02, 82, "sa/u")
+    r = oracle.swiglu_bf16(x, Wg, Wu)
+    ax = np.abs(oracle.bf16_to_f64(x))
+    assert np.allclose(r["Ag"], ax @ np.abs(oracle.bf16_to_f64(Wg)).T, rtol=1e-12, atol=0)
+    assert np.allclose(r["Au"], ax @ np.abs(oracle.bf16_to_f64(Wu)).T, rtol=1e-12, atol=0)
+    assert not np.allclose(r["Ag"], r["Au"], rtol=1e-3)       # each stream has its own sum
+    r2 = oracle.swiglu_bf16(x ^ 0x8000, Wg, Wu ^ 0x8000)
+    assert np.array_equal(r2["Ag"], r["Ag"]) and np.array_equal(r2["Au"], r["Au"])
+    assert np.all(r["Ag"] >= np.abs(r["g"])) and np.all(r["Au"] >= np.abs(r["u"]))
+    pos = oracle.swiglu_bf16(x & 0x7FFF, Wg & 0x7FFF, Wu & 0x7FFF)
+    assert np.array_equal(pos["Ag"], pos["g"]) and np.array_equal(pos["Au"], pos["u"])
+
+
+def _silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def test_silu_slope_constant_of_the_bound():
+    """The bound's 1.1 covers max |silu'| (about 1.0998 near g = 2.4); 1.0 would not."""
+    g = np.linspace(-40.0, 40.0, 800001)
+    e = np.exp(-g)
+    slope = (1.0 + e + g * e) / (1.0 + e) ** 2       # d/dg of g / (1 + e^-g)
+    assert 1.09 < slope.max() <= 1.1
+    h = 1e-6
+    fd = (_silu(g + h) - _silu(g - h)) / (2 * h)      # the derivative itself, by differences
+    assert np.abs(fd - slope).max() < 1e-6
+
+
+def _epilogue_f32(g, u):
+    """silu(g) * u evaluated in fp32 from fp32 inputs, as a kernel epilogue does."""
+    g32 = np.asarray(g, np.float32)
+    u32 = np.asarray(u, np.float32)
+    with np.errstate(over="ignore"):
+        return ((g32 / (np.float32(1.0) + np.exp(-g32))) * u32).astype(np.float64)
+
+
+def _admissible_swiglu_grid():
+    """(g, u, Ag, Au) with Ag >= |g| and Au >= |u| (the only constraints the
+    abs sums obey), over signs, magnitudes and the slope maximum of silu."""
+    gs = np.concatenate([np.linspace(-30, 30, 61), [0.0, 1e-3, 2.3994, -1.2785, 12.0, -12.0]])
+    us = np.array([0.0, 1e-3, -0.01, 1.0, -3.0, 100.0, -250.0])
+    ga = np.array([1.0, 10.0, 100.0, 1000.0])
+    ua = np.array([1.0, 10.0, 1000.0])
+    G, U, GA, UA = np.meshgrid(gs, us, ga, ua, indexing="ij")
+    G, U = G.ravel(), U.ravel()
+    Ag = np.maximum(np.abs(G) * GA.ravel(), 1e-3 * GA.ravel())
+    Au = np.maximum(np.abs(U) * UA.ravel(), 1e-3 * UA.ravel())
+    return G, U, Ag, Au
+
+
+def _worst_perturbed_error(G, U, Ag, Au, tol_fn):
+    """Largest |out' - out| / bound over perturbations |dg| <= tg, |du| <= tu
+    (corners, edges, interior), out' evaluated in fp32 like the kernels."""
+    out = _silu(G) * U
+    bound = tol_fn(G, U, Ag, Au, out)
+    tg = oracle.tolerance(Ag)
+    tu = oracle.tolerance(Au)
+    worst = 0.0
+    for fg in (-1.0, -0.5, 0.0, 0.5, 1.0):
+        for fu in (-1.0, 0.0, 1.0):
+            got = _epilogue_f32(G + fg * tg, U + fu * tu)
+            worst = max(worst, float(np.max(np.abs(got - out) / bound)))
+    return worst
+
+
+def test_swiglu_tolerance_covers_admissible_perturbations():
+    """Sound: whenever g and u are each within their GEMV bounds, the fp32
+    silu(g) * u stays within the propagated SwiGLU bound."""
+    G, U, Ag, Au = _admissible_swiglu_grid()
+    assert _worst_perturbed_error(G, U, Ag, Au, oracle.swiglu_tolerance) <= 1.0
+    # on real GEMV outputs as well
+    M, N, K = 4, 64, 1536
+    x = synth.normal_bf16((M, K), 1.0, 81, "sb/x")
+    r = oracle.swiglu_bf16(x, synth.normal_bf16((N, K), 0.02, 81, "sb/g"),
+                           synth.normal_bf16((N, K), 0.02, 81, "sb/u"))
+    assert _worst_perturbed_error(r["g"], r["u"], r["Ag"], r["Au"], oracle.swiglu_tolerance) <= 1.0
+
+
+def test_swiglu_tolerance_tight_terms_are_needed():
+    """The gate term (with its tu part and slope 1.1) and the up term are each
+    needed: the grid has admissible perturbations that break the bound
+    without them."""
+    G, U, Ag, Au = _admissible_swiglu_grid()
+    tol = oracle.tolerance
+
+    def without_gate(g, u, ag, au, out):
+        return oracle.swiglu_tolerance(g, u, ag, au, out) - 1.1 * tol(ag) * (np.abs(u) + tol(au))
+
+    def slope_one(g, u, ag, au, out):
+        return oracle.swiglu_tolerance(g, u, ag, au, out) - 0.1 * tol(ag) * (np.abs(u) + tol(au))
+
+    def without_tu_in_gate(g, u, ag, au, out):
+        return oracle.swiglu_tolerance(g, u, ag, au, out) - 1.1 * tol(ag) * tol(au)
+
+    def without_up(g, u, ag, au, out):
+        return oracle.swiglu_tolerance(g, u, ag, au, out) - np.abs(_silu(g)) * tol(au)
+
+    for fn in (without_gate, slope_one, without_tu_in_gate, without_up):
+        assert _worst_perturbed_error(G, U, Ag, Au, fn) > 1.0, fn.__name__
+
+
+# ------------------------------------------------------ affine SwiGLU chain
+
+def _exact_affine(bits, N, K, seed, name):
+    """Codes with scale 2^-e and bias -c 2^-e: every w = (q - c) 2^-e is exact in bf16."""
+    g = synth.rng(seed, name)
+    codes = g.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    e = g.integers(6, 10, size=(N, K // 64))
+    c = g.integers(0, 1 << bits, size=(N, K // 64))
+    s = _bf16(2.0 ** -e)
+    b = _bf16(-c * 2.0 ** -e)
+    w = (codes.astype(np.float64) - np.repeat(c, 64, axis=1)) * 2.0 ** -np.repeat(e, 64, axis=1)
+    return oracle.pack(codes, bits), s, b, _bf16(w)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_swiglu_affine_equals_dense_chain_on_exact_weights(bits):
+    """Where every dequantized weight is exact in bf16, the affine SwiGLU is the
+    dense SwiGLU (pinned against numpy) on those weights, bit for bit."""
+    M, N, K = 3, 12, 256
+    x = synth.normal_bf16((M, K), 1.0, 80, "sx/x")
+    gq, gs, gb, Wg = _exact_affine(bits, N, K, 80, "sx/g%d" % bits)
+    uq, us, ub, Wu = _exact_affine(bits, N, K, 80, "sx/u%d" % bits)
+    r = oracle.swiglu_affine(x, (gq, gs, gb), (uq, us, ub), bits)
+    d = oracle.swiglu_bf16(x, Wg, Wu)
+    for k in ("out", "g", "u", "Ag", "Au"):
+        assert np.array_equal(r[k], d[k]), k
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_swiglu_affine_streams_and_special_cases(bits):
+    """g and u are the affine GEMVs of their own matrices (rational brute force on
+    tiny exact inputs); zero codes and biases in either stream give out = 0."""
+    M, N, K = 2, 3, 128
+    g = synth.rng(79, "ss/%d" % bits)
+    x = _bf16(g.integers(-4, 5, size=(M, K)))
+    mats = []
+    for t in ("g", "u"):
+        words = synth.random_words((N, K * bits // 32), 79, "ss/%s%d" % (t, bits))
+        s = _bf16(2.0 ** -g.integers(0, 4, size=(N, K // 64)))
+        b = _bf16(g.integers(-3, 4, size=(N, K // 64)))
+        mats.append((words, s, b))
+    r = oracle.swiglu_affine(x, mats[0], mats[1], bits)
+    for key, (words, s, b) in (("g", mats[0]), ("u", mats[1])):
+        ref = brute.gemv_affine_exact(x.tolist(), words.tolist(), s.tolist(), b.tolist(), bits)
+        for m in range(M):
+            for n in range(N):
+                assert Fraction(r[key][m, n]) == ref[m][n], key
+    assert np.allclose(r["out"], _silu(r["g"]) * r["u"], rtol=1e-15, atol=0)
+    zero = (np.zeros_like(mats[0][0]), mats[0][1], np.zeros_like(mats[0][2]))
+    assert np.all(oracle.swiglu_affine(x, zero, mats[1], bits)["out"] == 0)
+    assert np.all(oracle.swiglu_affine(x, mats[0], zero, bits)["out"] == 0)

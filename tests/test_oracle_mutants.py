@@ -37,6 +37,17 @@ MUTANTS = {
     "argmax_highest_tie": ("if (y[m * N + n] > y[m * N + best])", "if (y[m * N + n] >= y[m * N + best])"),
     "bf16_round_half_up": ("u += 0x7FFFu + lsb;", "u += 0x8000u + 0u * lsb;"),
     "bf16_truncate": ("u += 0x7FFFu + lsb;", "u += 0u * lsb;"),
+    "swiglu_gate_abs_sum_signed": ("gaa += fabs(pg);\n                uaa += fabs(pu);\n            }\n            double silu = ga / (1.0 + exp(-ga));\n            int64_t i = m * N + n;\n            out[i] = silu * ua;\n            if (g) g[i] = ga;\n            if (u) u[i] = ua;\n            if (Ag) Ag[i] = gaa;\n            if (Au) Au[i] = uaa;\n        }\n    }\n}",
+                                   "gaa += pg;\n                uaa += fabs(pu);\n            }\n            double silu = ga / (1.0 + exp(-ga));\n            int64_t i = m * N + n;\n            out[i] = silu * ua;\n            if (g) g[i] = ga;\n            if (u) u[i] = ua;\n            if (Ag) Ag[i] = gaa;\n            if (Au) Au[i] = uaa;\n        }\n    }\n}"),
+    "swiglu_up_abs_sum_from_gate": ("                uaa += fabs(pu);\n            }\n            double silu = ga / (1.0 + exp(-ga));\n            int64_t i = m * N + n;\n            out[i] = silu * ua;\n            if (g) g[i] = ga;\n            if (u) u[i] = ua;\n            if (Ag) Ag[i] = gaa;\n            if (Au) Au[i] = uaa;\n        }\n    }\n}",
+                                    "                uaa += fabs(pg);\n            }\n            double silu = ga / (1.0 + exp(-ga));\n            int64_t i = m * N + n;\n            out[i] = silu * ua;\n            if (g) g[i] = ga;\n            if (u) u[i] = ua;\n            if (Ag) Ag[i] = gaa;\n            if (Au) Au[i] = uaa;\n        }\n    }\n}"),
+    "swiglu_abs_sums_swapped": ("            if (Ag) Ag[i] = gaa;\n            if (Au) Au[i] = uaa;\n        }\n    }\n}\n\n/* Unfused SwiGLU chain over two affine",
+                                "            if (Ag) Ag[i] = uaa;\n            if (Au) Au[i] = gaa;\n        }\n    }\n}\n\n/* Unfused SwiGLU chain over two affine"),
+    "swiglu_affine_up_uses_gate_scales": ("dequant(bits, Wuq + n * wpr, su + n * gpr", "dequant(bits, Wuq + n * wpr, sg + n * gpr"),
+    "swiglu_affine_gate_drops_bias": ("dequant(bits, Wgq + n * wpr, sg + n * gpr, bg + n * gpr, k)",
+                                      "dequant(bits, Wgq + n * wpr, sg + n * gpr, bg + n * gpr, k) - oracle_bf16_to_double(bg[n * gpr + k / 64])"),
+    "swiglu_affine_gate_up_swapped": ("double silu = ga / (1.0 + exp(-ga));\n            int64_t i = m * N + n;\n            out[i] = silu * ua;\n            if (g) g[i] = ga;\n            if (u) u[i] = ua;\n            if (Ag) Ag[i] = gaa;\n            if (Au) Au[i] = uaa;\n        }\n    }\n    return 0;",
+                                      "double silu = ua / (1.0 + exp(-ua));\n            int64_t i = m * N + n;\n            out[i] = silu * ga;\n            if (g) g[i] = ga;\n            if (u) u[i] = ua;\n            if (Ag) Ag[i] = gaa;\n            if (Au) Au[i] = uaa;\n        }\n    }\n    return 0;"),
 }
 
 # Pin tests to run against each mutant (all CPU, seconds in total).
@@ -51,6 +62,8 @@ PINS = [
     (pins.test_argmax_lowest_index_wins_ties_and_matches_numpy, {}),
     (pins.test_affine_scale_and_bias_are_per_group_and_per_row, {}),
     (pins.test_dense_matches_exact_brute_force, {}),
+    (pins.test_swiglu_abs_sums_pinned, {}),
+    (pins.test_swiglu_tolerance_covers_admissible_perturbations, {}),
 ]
 for _b in (2, 3, 4, 5, 6, 7, 8):
     PINS += [
@@ -59,7 +72,10 @@ for _b in (2, 3, 4, 5, 6, 7, 8):
         (pins.test_affine_zero_codes_give_bias_times_group_sums, {"bits": _b}),
         (pins.test_affine_unit_scale_zero_bias_is_integer_dot, {"bits": _b}),
         (pins.test_affine_matches_exact_brute_force_on_tiny_exact_inputs, {"bits": _b}),
+        (pins.test_swiglu_affine_equals_dense_chain_on_exact_weights, {"bits": _b}),
     ]
+for _b in (3, 4, 8):
+    PINS.append((pins.test_swiglu_affine_streams_and_special_cases, {"bits": _b}))
 for _row in pins._golden_rows():
     PINS.append((pins.test_pack_worked_vectors, {"row": _row}))
 
@@ -88,3 +104,27 @@ def test_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
         except AssertionError:
             caught.append(fn.__name__)
     assert caught, "no pin caught mutant %s" % name
+
+
+# Planted mistakes in the propagated SwiGLU bound (oracle/__init__.py): each
+# loosens or drops a term of swiglu_tolerance; the soundness pin must fail.
+TOL_MUTANTS = {
+    "slope_1_0": ("1.1 * tg", "1.0 * tg"),
+    "gate_term_missing_tu": ("(np.abs(u) + tu)", "(np.abs(u))"),
+    "up_term_dropped": ("np.abs(silu) * tu +", ""),
+    "gate_term_dropped": ("1.1 * tg * (np.abs(u) + tu) +", ""),
+    "up_term_uses_g": ("np.abs(silu) * tu", "np.abs(silu) * tg"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TOL_MUTANTS))
+def test_bound_pin_catches_planted_mistake(name, monkeypatch):
+    import inspect
+    old, new = TOL_MUTANTS[name]
+    src = inspect.getsource(oracle.swiglu_tolerance)
+    assert src.count(old) == 1, "mutation anchor not found: %s" % name
+    ns = {"np": oracle.np, "tolerance": oracle.tolerance}
+    exec(src.replace(old, new), ns)
+    monkeypatch.setattr(oracle, "swiglu_tolerance", ns["swiglu_tolerance"])
+    with pytest.raises(AssertionError):
+        pins.test_swiglu_tolerance_covers_admissible_perturbations()
