@@ -21,7 +21,7 @@ import threading
 import torch
 
 __all__ = [
-    "lib_path", "load", "AqgError", "abi_version", "status_string", "workspace_bytes",
+    "lib_path", "load", "AqgError", "abi_version", "status_string", "workspace_bytes", "dispatch_path",
     "gemv_bf16", "gemv_affine", "swiglu_bf16", "unpack_codes",
     "gemv_affine_q2", "gemv_affine_q3", "gemv_affine_q4", "gemv_affine_q5",
     "gemv_affine_q6", "gemv_affine_q7", "gemv_affine_q8",
@@ -75,6 +75,10 @@ def load():
         lib.aqg_swiglu_bf16.argtypes = [P, P, P, P, I, I, I, I, P, Z, P]
         lib.aqg_unpack_codes.restype = I
         lib.aqg_unpack_codes.argtypes = [I, P, P, I, I, P]
+        lib.aqg_dispatch_path.restype = I
+        lib.aqg_dispatch_path.argtypes = [I, I, I, I, ctypes.POINTER(I)]
+        lib.aqg_path_name.restype = ctypes.c_char_p
+        lib.aqg_path_name.argtypes = [I]
         _lib = lib
         return lib
 
@@ -89,6 +93,15 @@ def status_string(status: int) -> str:
 
 def workspace_bytes(kind: int, M: int, N: int, K: int) -> int:
     return int(load().aqg_workspace_bytes(kind, M, N, K))
+
+
+def dispatch_path(kind: int, M: int, N: int, K: int):
+    """(path name, kernel columns) a call would run on (test hook; launches nothing)."""
+    cols = ctypes.c_int(0)
+    p = load().aqg_dispatch_path(kind, M, N, K, ctypes.byref(cols))
+    if p < 0:
+        raise AqgError(-p, "aqg_dispatch_path")
+    return load().aqg_path_name(p).decode(), cols.value
 
 
 # ------------------------------------------------------------ marshalling
@@ -213,10 +226,17 @@ def swiglu_bf16(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, out_dtype=t
 
 def unpack_codes(Wq: torch.Tensor, bits: int, K: int, out=None) -> torch.Tensor:
     """codes[N, K] uint8 through the kernels' own unpack path."""
+    if bits not in range(2, 9):
+        raise ValueError("bits must be in 2..8")
     _dev(Wq, "Wq", (torch.int32, torch.uint32))
     N = Wq.shape[0]
     if Wq.shape[1] * 32 != K * bits:
         raise ValueError("Wq must be [N, K*bits/32]")
-    codes = out if out is not None else torch.empty((N, K), dtype=torch.uint8, device=Wq.device)
+    if out is None:
+        codes = torch.empty((N, K), dtype=torch.uint8, device=Wq.device)
+    else:
+        codes = _dev(out, "out", (torch.uint8,))
+        if tuple(codes.shape) != (N, K) or codes.device != Wq.device:
+            raise ValueError("out must be a uint8 [%d, %d] tensor on %s" % (N, K, Wq.device))
     _check(load().aqg_unpack_codes(bits, _p(Wq), _p(codes), N, K, _stream(Wq)), "aqg_unpack_codes")
     return codes

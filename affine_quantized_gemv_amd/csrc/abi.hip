@@ -3,11 +3,11 @@
 //
 // The refusal rules follow the pages' lessons: unsupported widths, group sizes
 // and shapes are refused rather than silently handled (TensorFold PR #849,
-// "Groups other than 64, and non-affine modes, are still refused"; sizes must
-// be positive, same PR, config-parse fix); a launch is always checked so an
-// output is never left unwritten without an error (FreeToken-Kai
-// docs/turing.md, sgl_kernel section: unchecked launches left torch.empty
-// outputs uninitialised).
+// "What this changes": only the affine mode with groups of 64 is accepted;
+// sizes must be positive, same PR, config-parse fix); a launch is always
+// checked so an output is never left unwritten without an error
+// (FreeToken-Kai docs/turing.md, sgl_kernel section: a launch whose failure
+// went unchecked left its outputs uninitialised).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -187,6 +187,37 @@ AQG_AFFINE_ENTRY(6)
 AQG_AFFINE_ENTRY(7)
 AQG_AFFINE_ENTRY(8)
 #undef AQG_AFFINE_ENTRY
+
+int aqg_dispatch_path(int kind, int M, int N, int K, int* columns)
+{
+    if (M <= 0 || N <= 0 || K <= 0) return -AQG_ERR_INVALID_ARG;
+    const bool swiglu = kind == AQG_KIND_SWIGLU;
+    const int bits = swiglu ? 0 : kind;
+    if (!(kind == AQG_KIND_DENSE || swiglu || (kind >= 2 && kind <= 8))) return -AQG_ERR_INVALID_ARG;
+    if (M > 32) return -AQG_ERR_UNSUPPORTED;
+    if (bits == 0 ? (K % 8 != 0) : (K % 64 != 0)) return -AQG_ERR_UNSUPPORTED;
+    // no device check: without a device the geometry assumes 256 CUs
+    const aqg::LaunchCfg cfg = aqg::choose_config(bits, swiglu, M, N, K);
+    if (columns) *columns = cfg.MT;
+    return cfg.path;
+}
+
+const char* aqg_path_name(int path)
+{
+    switch (path) {
+        case aqg::PATH_VALU: return "valu";
+        case aqg::PATH_MFMA: return "mfma";
+        case aqg::PATH_STREAM: return "stream";
+        case aqg::PATH_PIECE: return "piece";
+        case aqg::PATH_MFMA_STREAM: return "mfma_stream";
+        case aqg::PATH_MFMA_SPLIT: return "mfma_split";
+        case aqg::PATH_AFFINE_MFMA: return "affine_mfma";
+        case aqg::PATH_MFMA_TILE: return "mfma_tile";
+        case aqg::PATH_AFFINE_TILE: return "affine_tile";
+        case aqg::PATH_AFFINE_SPLIT: return "affine_split";
+        default: return "unknown";
+    }
+}
 
 int aqg_unpack_codes(int bits, const uint32_t* Wq, uint8_t* codes, int N, int K, void* stream)
 {

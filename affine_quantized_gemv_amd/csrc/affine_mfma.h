@@ -9,8 +9,12 @@
 // 128 + q (mask placement, no lookup); 8-bit codes go in as two nibbles, the
 // high one in a second MFMA chain weighted 16 in fp32.  So one group's result
 // is D = sum_k (C + q_k) x_k with C = 128 (2176 for 8 bits), and the group
-// contributes scale * D + (bias - C * scale) * X with X = sum_k x_k -- the
-// exact factored form of sum_k x_k (scale * q_k + bias), in fp32.
+// contributes scale * (D - D0) + bias * X with X = sum_k x_k -- the factored
+// form of sum_k x_k (scale * q_k + bias), in fp32.  D0 is the code offset
+// C * X computed by the matrix core itself: the same two (or, for 8 bits,
+// four) MFMAs on the same x^T operands with every code zero, once per group
+// and column in the prologue.  A group whose codes are all zero thus gives
+// D == D0 bit for bit and adds exactly bias * X (no residue of the offset).
 //
 // Operand flow per 128-byte k-block of the tile's 16 rows:
 //   * two buffer loads cover rows 0..7 and 8..15 with whole 128-byte lines,
@@ -23,15 +27,15 @@
 //     four at 8 bits); they become the A operands of two k-steps, and x^T is
 //     staged in LDS with the matching k order, so the products pair up (the
 //     k order inside a group is free: it only has to agree on both sides);
-//   * the two k-steps of a group accumulate into a fresh 16 x 16 tile, which
-//     the group's scale (from a small wavefront-private LDS table filled from
-//     the scale loads) adds into the tile's sum in fp32;
-//   * the bias and the code offset do not depend on the codes: over the tile
-//     they are sum_g bias_g X_g - C sum_g scale_g X_g, two small contractions
-//     over the groups that the matrix core also does at the end of each tile
-//     (A = the tile's biases or scales, bf16, staged per row in LDS; B = the
-//     group sums X split into bf16 high and low parts, X - hi(X) being exact
-//     in bf16 to within 2^-16 of X).
+//   * the two k-steps of a group accumulate into a fresh 16 x 16 tile D; the
+//     group's scale (from a small wavefront-private LDS table filled from the
+//     scale loads) times D - D0 (D0 from an LDS table per group and column)
+//     is added into the tile's sum in fp32;
+//   * the bias term does not depend on the codes: over the tile it is
+//     sum_g bias_g X_g, a small contraction over the groups that the matrix
+//     core also does at the end of each tile (A = the tile's biases, bf16,
+//     staged per row in LDS; B = the group sums X split into bf16 high and
+//     low parts, X - hi(X) being exact in bf16 to within 2^-16 of X).
 // Codes of one group never mix with another group's in an MFMA, and each
 // output is the same chain of MFMAs and fp32 operations for every M of a
 // 16-column bucket.
@@ -140,10 +144,10 @@ __device__ __forceinline__ u32x4_t stage_x_operand(const uint16_t* xr, int S, in
 }
 
 // LDS bytes private to one wavefront: the k-block's scales (bf16, 4 x 16)
-// and its chunk's bias and scale tables (bf16, 16 rows x gps).
+// and its chunk's bias table (bf16, 16 rows x gps).
 __host__ __device__ inline size_t affine_mfma_wave_bytes(int gps)
 {
-    return 256 + (size_t)2 * 16 * gps * 2;
+    return 256 + (size_t)16 * gps * 2;
 }
 
 template <int BITS, int MT, int D, int GPS>
@@ -183,10 +187,10 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
     const int64_t my_tiles = u < T ? (T - 1 - u) / U + 1 : 0;
 
     // LDS: x^T fragments [s][b][lane]; X hi/lo fragments [chunk][ks][b][2][lane];
-    // sums of x per (k-step, column) (prologue only); per wavefront:
-    // scales of the k-block
-    // in use [group][row], its chunk's bias and scale tables [row][GPS] (all
-    // bf16); with a K split, the chunks' partial tiles [slot][tile][chunk].
+    // sums of x per (k-step, column) in the prologue, then the code offsets
+    // D0 per (group, column); per wavefront: scales of the k-block in use
+    // [group][row] and its chunk's bias table [row][GPS] (bf16); with a K
+    // split, the chunks' partial tiles [slot][tile][chunk].
     u32x4_t* xb = lds_a4;
     u32x4_t* xh = xb + (size_t)KS * NB * 64;
     float* xs = reinterpret_cast<float*>(xh + (size_t)nkc * KSG * NB * 2 * LV);
@@ -199,7 +203,6 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
     constexpr bool SB32 = GPK <= 4;
     uint16_t* sbuf = reinterpret_cast<uint16_t*>(wbase);                        // [GPK][16] bf16 / fp32
     uint16_t* btab = reinterpret_cast<uint16_t*>(wbase + 256);                  // [16][GPS]
-    uint16_t* stab = btab + 16 * GPS;                                           // [16][GPS]
     float* pbuf = reinterpret_cast<float*>(wbase0 + (size_t)NW * affine_mfma_wave_bytes(GPS));
 
     // ---- ring of D k-blocks: two whole-line loads + the block's scales and
@@ -237,9 +240,9 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
         f_tile += wrap ? U : 0;
     };
 
-    f32x4_t acc[NB], accb[NB], accs[NB];
+    f32x4_t acc[NB], accb[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = accb[b] = accs[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b) acc[b] = accb[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     int c_b = kb_lo;                     // k-block being consumed
     int64_t c_tile = u;                  // its tile
     int ti = 0;                          // tiles finished (K split: partials staged)
@@ -267,19 +270,16 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
                 sbuf[((lane & 3) * 16 + (lane >> 2)) * 2 + 1] = (uint16_t)sw[d];
                 const int ti2 = (lane >> 2) * GPS + rel + (lane & 3);
                 btab[ti2] = (uint16_t)bw[d];
-                stab[ti2] = (uint16_t)sw[d];
             } else if constexpr (BITS == 2) {
                 sbuf[(2 * (lane & 3)) * 16 + (lane >> 2)] = (uint16_t)sw[d];
                 sbuf[(2 * (lane & 3) + 1) * 16 + (lane >> 2)] = (uint16_t)(sw[d] >> 16);
                 const int ti2 = ((lane >> 2) * GPS + rel + 2 * (lane & 3)) >> 1;   // even group: one 32-bit word
                 reinterpret_cast<uint32_t*>(btab)[ti2] = bw[d];
-                reinterpret_cast<uint32_t*>(stab)[ti2] = sw[d];
             } else {
                 // lanes 32..63 repeat lanes 0..31 (same values, same places)
                 sbuf[((lane & 1) * 16 + ((lane >> 1) & 15)) * 2 + 1] = (uint16_t)sw[d];
                 const int ti2 = ((lane >> 1) & 15) * GPS + rel + (lane & 1);
                 btab[ti2] = (uint16_t)bw[d];
-                stab[ti2] = (uint16_t)sw[d];
             }
         }
         // pieces: s[0] = pieces 0..3 of row j in lane-row g, s[1] = pieces 4..7
@@ -319,6 +319,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
                 codes8_to_bf16(pc[gi][2], pc[gi][3], cmask, cbias, A1, H1);
             }
             const int S0 = 2 * (GPK * c_b + gi);
+            const float* d0g = xs + (size_t)(GPK * c_b + gi) * MT + r;   // code offsets of the group's columns
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const u32x4_t B0 = xb[(S0 * NB + b) * 64 + lane], B1 = xb[((S0 + 1) * NB + b) * 64 + lane];
@@ -330,27 +331,25 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
 #pragma unroll
                     for (int i = 0; i < 4; ++i) dg[i] = fmaf(16.0f, dh[i], dg[i]);
                 }
+                const float z = d0g[16 * b];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(sc[i], dg[i], acc[b][i]);
+                for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(sc[i], dg[i] - z, acc[b][i]);
             }
         }
         if (++c_b == kb_hi) {
-            // end of the tile (or of its K-chunk): bias and code-offset terms
+            // end of the tile (or of its K-chunk): the bias term
             c_b = kb_lo;
             const bool lv = lane < LV;
 #pragma unroll
             for (int ks = 0; ks < KSG; ++ks) {
                 const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
                 const u32x4_t Ab = lv ? *reinterpret_cast<const u32x4_t*>(btab + r * GPS + 32 * ks + 8 * c) : z;
-                const u32x4_t As = lv ? *reinterpret_cast<const u32x4_t*>(stab + r * GPS + 32 * ks + 8 * c) : z;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const u32x4_t Xh = lv ? xhj[((ks * NB + b) * 2 + 0) * LV + lane] : z;
                     const u32x4_t Xl = lv ? xhj[((ks * NB + b) * 2 + 1) * LV + lane] : z;
                     accb[b] = mfma16x16x32(Ab, Xh, accb[b]);
                     accb[b] = mfma16x16x32(Ab, Xl, accb[b]);
-                    accs[b] = mfma16x16x32(As, Xh, accs[b]);
-                    accs[b] = mfma16x16x32(As, Xl, accs[b]);
                 }
             }
             // lane (c, r) holds rows 4c .. 4c + 3 of column 16b + r
@@ -366,7 +365,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
                     const int m = 16 * b + r;
                     float v[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = fmaf(-AffineMma<BITS>::OFF, accs[b][i], acc[b][i] + accb[b][i]);
+                    for (int i = 0; i < 4; ++i) v[i] = acc[b][i] + accb[b][i];
                     if (vec_store) {
                         const uint32_t off = (m < a.M && n0 < a.N) ? (uint32_t)(((int64_t)m * a.N + n0) * esz) : kDrop;
                         if (a.out_f32) {
@@ -395,10 +394,10 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        pt[(4 * c + i) * MT + 16 * b + r] = fmaf(-AffineMma<BITS>::OFF, accs[b][i], acc[b][i] + accb[b][i]);
+                        pt[(4 * c + i) * MT + 16 * b + r] = acc[b][i] + accb[b][i];
             }
 #pragma unroll
-            for (int b = 0; b < NB; ++b) acc[b] = accb[b] = accs[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < NB; ++b) acc[b] = accb[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             c_tile += U;
             ++ti;
         }
@@ -406,8 +405,8 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
 
     // prologue: D k-blocks, then stage x^T (pair order within each 8-k chunk)
     // with the sums of each staged 8 x, then each chunk's group sums X as
-    // bf16 high/low fragments, and clear the bias tables (groups past the
-    // chunk's end stay zero)
+    // bf16 high/low fragments, clear the bias table (groups past the chunk's
+    // end stay zero), and the code offsets D0
     static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(Dd); });
     {
         constexpr int XB = 4;
@@ -445,7 +444,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
                 }
             }
         }
-        for (int t = lane; t < 16 * GPS; t += 64)          // both tables, as 32-bit words
+        for (int t = lane; t < 8 * GPS; t += 64)           // the bias table (16 x GPS bf16) as 32-bit words
             reinterpret_cast<uint32_t*>(btab)[t] = 0u;
         if constexpr (SB32)                                 // the fp32 scales' low halves
             for (int t = lane; t < 16 * GPK; t += 64) reinterpret_cast<uint32_t*>(sbuf)[t] = 0u;
@@ -479,6 +478,21 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
         }
         xh[(kb * 2 + 0) * LV + l] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
         xh[(kb * 2 + 1) * LV + l] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+    }
+    __syncthreads();   // the sums xs are read; their space takes the offsets
+    // code offsets D0[g][column]: the group's MFMA chain on zero codes (every
+    // A row is (128, ..., 128), so every row of the result is the same)
+    {
+        const u32x4_t A0 = u32x4_t{kZeroCodePair, kZeroCodePair, kZeroCodePair, kZeroCodePair};
+        for (int task = wave; task < (KS / 2) * NB; task += NW) {
+            const int g = task / NB, b = task - g * NB;
+            const u32x4_t B0 = xb[((2 * g) * NB + b) * 64 + lane], B1 = xb[((2 * g + 1) * NB + b) * 64 + lane];
+            f32x4_t d0 = mfma16x16x32(A0, B0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            d0 = mfma16x16x32(A0, B1, d0);
+            float z = d0[0];
+            if constexpr (BITS == 8) z = fmaf(16.0f, z, z);   // the high-nibble chain is the same chain
+            if (c == 0) xs[(size_t)g * MT + 16 * b + r] = z;
+        }
     }
     // Every load issued so far is complete (the x loads came after the
     // weights and loads complete in order); saying so keeps a possibly
@@ -565,16 +579,11 @@ hipError_t launch_affine_mfma_one(const ProjArgs& a, int nkc, hipStream_t s)
 {
     const void* fn = reinterpret_cast<const void*>(&affine_mfma_kernel<BITS, MT, kAffineMfmaDepth, GPS>);
     {
-        static std::atomic<int> raised{0};
-        if (!raised.load(std::memory_order_acquire)) {
-            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaStreamLdsMax);
-            if (e != hipSuccess) return e;
-            raised.store(1, std::memory_order_release);
-        }
+        hipError_t e = raise_lds_limit(fn, kMfmaStreamLdsMax);
+        if (e != hipSuccess) return e;
     }
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    hipError_t e = device_cus(cus);
     if (e != hipSuccess) return e;
     const int64_t T = ((int64_t)a.N + 15) / 16;
     int bpc = kAffineMfmaWgPerCu, blocks = 0;
@@ -585,7 +594,7 @@ hipError_t launch_affine_mfma_one(const ProjArgs& a, int nkc, hipStream_t s)
         lds = affine_mfma_lds_bytes(MT, a.K, BITS, nkc, tmax);
         if (lds > kMfmaStreamLdsMax) return hipErrorInvalidValue;
         int occ = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAffineMfmaThreads, lds);
+        e = occupancy(occ, fn, kAffineMfmaThreads, lds);
         if (e != hipSuccess) return e;
         if (occ >= bpc || bpc == 1) break;
         bpc = occ < 1 ? 1 : occ;

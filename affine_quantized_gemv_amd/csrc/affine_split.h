@@ -13,8 +13,10 @@
 // of the codes (no LDS staging, no barrier before the arithmetic).  Per group
 // two MFMA k-steps on the codes placed as bf16 (128 + q; 8-bit codes as two
 // nibble chains, the high one weighted 16) give D = sum_k (C + q_k) x_k, and
-// the group adds scale * D + (bias - C * scale) * X with X = sum_k x_k, in
-// fp32: the factored form of sum_k x_k (scale * q_k + bias).  The partial
+// the group adds scale * (D - D0) + bias * X with X = sum_k x_k, in fp32: the
+// factored form of sum_k x_k (scale * q_k + bias).  D0 is the same MFMA chain
+// on zero codes (C X as the matrix core computes it), formed once per group
+// from the x^T operands, so a group of zero codes adds exactly bias * X.  The partial
 // 16 x 16 tiles of the wavefronts are summed through LDS in wavefront order,
 // so results are deterministic and the same for every M the kernel serves.
 //
@@ -61,7 +63,6 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
     extern __shared__ float lds_red[];
     constexpr int GPK = AffineMma<BITS>::GPK;     // groups per 128-byte k-block
     constexpr int GPW = KPW * GPK;                // groups per wavefront
-    constexpr float OFF = AffineMma<BITS>::OFF;
     constexpr int SDW = GPW / 2;                  // dwords of one row's scales (or biases) per wavefront
     static_assert(GPW % 2 == 0, "groups come in pairs");
 
@@ -113,9 +114,14 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
         load_dwords<SDW>(rb, off, bw[i]);
     }
     // x^T: lane (c, column r) holds the operands of k-steps 2g, 2g + 1 of its
-    // groups and the groups' sums over all four lane quarters (fixed order)
+    // groups, the groups' sums over all four lane quarters (fixed order) and
+    // their code offsets D0 (the group's MFMA chain on zero codes)
     u32x4_t xb[2 * GPW];
     float X[GPW];
+    // D0 lives in LDS (this wavefront's [GPW][16 columns] after the reduction
+    // area): each lane stores the value of its own column and later reads back
+    // the address it wrote (the four lanes of a column write the same value)
+    float* d0w = lds_red + (size_t)(blockDim.x >> 6) * 4 * 65 + (size_t)wave * GPW * 16;
     {
         const bool have = r < a.M;
         const uint16_t* xrow = a.x + (size_t)(have ? r : 0) * a.K + 64 * g0;
@@ -133,6 +139,10 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
             const float p = (c & 1) ? v16 + v : v + v16;
             const float p32 = __shfl_xor(p, 32);
             X[g] = (c & 2) ? p32 + p : p + p32;
+            const u32x4_t Z = u32x4_t{kZeroCodePair, kZeroCodePair, kZeroCodePair, kZeroCodePair};
+            f32x4_t d0 = mfma16x16x32(Z, xb[2 * g], f32x4_t{0.f, 0.f, 0.f, 0.f});
+            d0 = mfma16x16x32(Z, xb[2 * g + 1], d0);
+            d0w[g * 16 + r] = BITS == 8 ? fmaf(16.0f, d0[0], d0[0]) : d0[0];   // 8 bits: the high-nibble chain is the same
         }
     }
 
@@ -177,12 +187,13 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dg[i] = fmaf(16.0f, dh[i], dg[i]);
             }
+            const float z0 = d0w[g * 16 + r];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t sh = sw[i][g >> 1], bh = bw[i][g >> 1];
                 const float s = __uint_as_float((g & 1) ? (sh & 0xFFFF0000u) : (sh << 16));
                 const float bi = __uint_as_float((g & 1) ? (bh & 0xFFFF0000u) : (bh << 16));
-                acc[i] = fmaf(s, dg[i], fmaf(fmaf(-OFF, s, bi), X[g], acc[i]));
+                acc[i] = fmaf(s, dg[i] - z0, fmaf(bi, X[g], acc[i]));
             }
         }
     }
@@ -225,7 +236,8 @@ hipError_t launch_affine_split_one(const ProjArgs& a, hipStream_t s)
     if (a.M > 32) return hipErrorInvalidValue;
     const int nks = (a.K * BITS / 1024) / KPW;
     const int64_t tiles = ((int64_t)a.N + 15) / 16;
-    const size_t lds = (size_t)nks * 4 * 65 * 4;
+    // partial tiles for the reduction, then each wavefront's code offsets
+    const size_t lds = (size_t)nks * 4 * 65 * 4 + (size_t)nks * KPW * AffineMma<BITS>::GPK * 16 * 4;
     // M = 17..32 runs once per 16-column block, and with at most half as many
     // row tiles as CUs M = 9..16 once per 8-column block (the two blocks of a
     // tile on one XCD).
@@ -235,9 +247,8 @@ hipError_t launch_affine_split_one(const ProjArgs& a, hipStream_t s)
         return hipGetLastError();
     }
     if (a.M > 8) {
-        int dev = 0, cus = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        int cus = 0;
+        hipError_t e = device_cus(cus);
         if (e != hipSuccess) return e;
         if (2 * tiles <= cus) {
             const int64_t blocks = (tiles + 7) / 8 * 16;

@@ -20,13 +20,17 @@
 //   * its x^T B operands for that range stay in registers for the whole
 //     launch, in the k order of the width's A operands, with the group sums
 //     X_g = sum_k x_k of each of its columns;
+//   * with them, the code offsets D0_g: the group's MFMA chain run on zero
+//     codes (every A row (128, ..., 128)), i.e. C X_g as the matrix core
+//     computes it (C = 128, or 2176 for 8 bits);
 //   * per tile it turns the group scales and biases into an fp32 table
-//     (s, bias - C s) in its own LDS area;
+//     (s, bias) in its own LDS area;
 //   * per group it reads the lane's code dwords of its row from LDS, places
 //     them in bf16 mantissas (128 + q; 8-bit codes as two nibble operands),
 //     runs the group's two k-steps into a fresh 16 x 16 tile D and adds
-//     s D + (bias - C s) X_g in fp32 -- the factored form of
-//     sum_k x_k (s q_k + bias) (C = 128, or 2176 for 8 bits).
+//     s (D - D0_g) + bias X_g in fp32 -- the factored form of
+//     sum_k x_k (s q_k + bias); a group of zero codes gives D == D0_g bit for
+//     bit and so adds exactly bias X_g.
 // The KS partial blocks of a row block are summed through LDS in k-chunk
 // order (fixed: results do not depend on M); each thread stores 16 RB MT /
 // 512 outputs per tile with one buffer store each.  Larger RB amortizes the
@@ -61,8 +65,9 @@ struct AffineTileLayout {
     static constexpr int PW = NB * 4 * 65;
     static constexpr int PART = NWV * PW * 4;
     static constexpr int NSTO = (16 * RB * MT + NT - 1) / NT;   // stores per thread per tile
-    static constexpr int TAB = NWV * 2 * GW * 16 * 4;   // per-wavefront (s, c) tables
-    static constexpr size_t LDS = (size_t)NBUF * TILE + PART + TAB;
+    static constexpr int TAB = NWV * 2 * GW * 16 * 4;   // per-wavefront (s, bias) tables
+    static constexpr int D0T = NWV * GW * NB * 16 * 4;  // per-wavefront code offsets
+    static constexpr size_t LDS = (size_t)NBUF * TILE + PART + TAB + D0T;
     static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8, "row blocks divide the wavefronts");
     static_assert(K % (64 * KS) == 0, "whole groups per wavefront");
     static_assert(CP % NWV == 0 && CP > 0, "code pieces split evenly over the wavefronts");
@@ -125,7 +130,6 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
     constexpr int NB = L::NB;
     constexpr int GW = L::GW;
     using WD = AffineTileWidth<BITS>;
-    constexpr float OFF = BITS == 8 ? 2176.0f : 128.0f;
     static_assert(NBUF >= 2 && NBUF <= 6, "ring of 2..6 tiles");
 
     const int lane = threadIdx.x & 63;
@@ -177,9 +181,14 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
     // tiles per workgroup this start is a large part of the call).
     issue(0, Int<0>{});
 
-    // x^T operands of this wavefront's 2 GW k-steps and the group sums
+    // x^T operands of this wavefront's 2 GW k-steps, the group sums and the
+    // groups' code offsets
     u32x4_t xr[2 * GW][NB];
     float X[GW][NB];
+    // the offsets live in LDS, this wavefront's [GW][NB][16 columns]: each
+    // lane stores the value of its own column and later reads back the
+    // address it wrote (the four lanes of a column write the same value)
+    float* d0w = reinterpret_cast<float*>(mfma_tile_lds<NBUF + 2, L::D0T>()) + wave * GW * NB * 16;
     const int kw = kc * (K / KS);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -205,6 +214,10 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
             const float p = (c & 1) ? v16 + v : v + v16;
             const float p32 = __shfl_xor(p, 32);
             X[g][b] = (c & 2) ? p32 + p : p + p32;
+            const u32x4_t Z = u32x4_t{kZeroCodePair, kZeroCodePair, kZeroCodePair, kZeroCodePair};
+            f32x4_t d0 = mfma16x16x32(Z, xr[2 * g][b], f32x4_t{0.f, 0.f, 0.f, 0.f});
+            d0 = mfma16x16x32(Z, xr[2 * g + 1][b], d0);
+            d0w[(g * NB + b) * 16 + r] = BITS == 8 ? fmaf(16.0f, d0[0], d0[0]) : d0[0];   // 8 bits: the high-nibble chain is the same
         }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
@@ -230,7 +243,7 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
     auto step = [&](int64_t j, auto Bc) __attribute__((always_inline)) {
         constexpr int B = decltype(Bc)::value;
         const char* tb = mfma_tile_lds<B, L::TILE>();
-        // (s, bias - C s) of this wavefront's groups, rows 0..15: lane e < 16 GW
+        // (s, bias) of this wavefront's groups, rows 0..15: lane e < 16 GW
         // takes row e % 16 of group e / 16
 #pragma unroll
         for (int e0 = 0; e0 < 16 * GW; e0 += 64) {
@@ -242,7 +255,7 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
                 const float s = bf16_to_f32(sp[row * GW + g]);
                 const float bi = bf16_to_f32(bp[row * GW + g]);
                 tab[g * 16 + row] = s;
-                tab[(GW + g) * 16 + row] = fmaf(-OFF, s, bi);
+                tab[(GW + g) * 16 + row] = bi;
             }
         }
         f32x4_t acc[NB];
@@ -294,8 +307,9 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) dg[i] = fmaf(16.0f, dh[i], dg[i]);
                 }
+                const float z0 = d0w[(g * NB + b) * 16 + r];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(sc[i], dg[i], fmaf(cc[i], X[g][b], acc[b][i]));
+                for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(sc[i], dg[i] - z0, fmaf(cc[i], X[g][b], acc[b][i]));
             }
         }
         float* pw = part + wave * L::PW;
@@ -392,10 +406,9 @@ hipError_t launch_affine_tile_one(const ProjArgs& a, hipStream_t s)
 {
     static_assert(AffineTileLayout<BITS, MT, K, RB, NBUF, NWV>::LDS <= 160 * 1024, "fits one CU's LDS");
     const void* fn = reinterpret_cast<const void*>(&affine_tile_kernel<BITS, MT, K, RB, NBUF, NWV>);
-    int dev = 0, cus = 0, bpc = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, 64 * NWV, 0);
+    int cus = 0, bpc = 0;
+    hipError_t e = device_cus(cus);
+    if (e == hipSuccess) e = occupancy(bpc, fn, 64 * NWV, 0);
     if (e != hipSuccess) return e;
     if (bpc < 1) bpc = 1;
     const int64_t T = ((int64_t)a.N + 16 * RB - 1) / (16 * RB);

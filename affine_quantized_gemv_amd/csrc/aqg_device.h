@@ -50,6 +50,9 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// The bf16 pair a zero code field places: (128, 128).
+constexpr uint32_t kZeroCodePair = 0x43004300u;
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // fp32 -> bf16, round to nearest even; NaN becomes a quiet NaN.

@@ -200,9 +200,8 @@ bool choose_affine_mfma(int bits, int M, int N, int K, LaunchCfg& c)
     const int64_t T = ((int64_t)N + 15) / 16;
     const int MT = M <= 16 ? 16 : 32;
     const int kbl = detail::affine_mfma_kbl(K, bits);
-    int cus = 256, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
+    int cus = 256;
+    if (detail::device_cus(cus) != hipSuccess) cus = 256;
     // smallest split that gives ~2048 work items, then more chunks while the
     // LDS does not fit (smaller chunks need smaller bias tables)
     auto fits = [&](int n) {

@@ -173,9 +173,8 @@ hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
     // 8.0 us), so the columns stay in one workgroup.
     // M = 5..8 likewise once per 4-column block.
     if (MT == 32 || a.M > 4) {
-        int dev = 0, cus = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        int cus = 0;
+        hipError_t e = device_cus(cus);
         if (e != hipSuccess) return e;
         if (2 * tiles <= cus) {
             const size_t lds = (size_t)nks * (SW ? 2 : 1) * 4 * 65 * 4;

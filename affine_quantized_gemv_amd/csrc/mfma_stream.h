@@ -244,16 +244,11 @@ hipError_t launch_mfma_stream_one(const ProjArgs& a, hipStream_t s)
 {
     const void* fn = reinterpret_cast<const void*>(&mfma_stream_kernel<MT, SW, kMfmaStreamDepth>);
     {
-        static std::atomic<int> raised{0};
-        if (!raised.load(std::memory_order_acquire)) {
-            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaStreamLdsMax);
-            if (e != hipSuccess) return e;
-            raised.store(1, std::memory_order_release);
-        }
+        hipError_t e = raise_lds_limit(fn, kMfmaStreamLdsMax);
+        if (e != hipSuccess) return e;
     }
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    hipError_t e = device_cus(cus);
     if (e != hipSuccess) return e;
     constexpr int NW = kMfmaStreamThreads / 64;
     const int64_t T = ((int64_t)a.N + 15) / 16;
@@ -266,7 +261,7 @@ hipError_t launch_mfma_stream_one(const ProjArgs& a, hipStream_t s)
         lds = mfma_stream_lds_bytes(MT, a.K, tmax);
         if (lds > kMfmaStreamLdsMax) return hipErrorInvalidValue;
         int bpc = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, kMfmaStreamThreads, lds);
+        e = occupancy(bpc, fn, kMfmaStreamThreads, lds);
         if (e != hipSuccess) return e;
         if (bpc < 1) bpc = 1;
         int64_t w = (int64_t)bpc * cus * NW;

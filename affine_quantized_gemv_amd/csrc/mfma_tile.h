@@ -277,10 +277,9 @@ hipError_t launch_mfma_tile_one(const ProjArgs& a, hipStream_t s)
 {
     static_assert(MfmaTileLayout<MT, KSW, NBUF, NW>::LDS <= 160 * 1024, "fits one CU's LDS");
     const void* fn = reinterpret_cast<const void*>(&mfma_tile_kernel<MT, KSW, NBUF, NW>);
-    int dev = 0, cus = 0, bpc = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, 64 * NW, 0);
+    int cus = 0, bpc = 0;
+    hipError_t e = device_cus(cus);
+    if (e == hipSuccess) e = occupancy(bpc, fn, 64 * NW, 0);
     if (e != hipSuccess) return e;
     if (bpc < 1) bpc = 1;
     const int64_t T = ((int64_t)a.N + 15) / 16;

@@ -535,16 +535,11 @@ hipError_t launch_piece_one(const ProjArgs& a, hipStream_t s)
 {
     const void* fn = reinterpret_cast<const void*>(&piece_kernel<BITS, MT, SW, XREG, L, J>);
     {
-        static std::atomic<int> raised{0};
-        if (!raised.load(std::memory_order_acquire)) {
-            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPieceLdsMax);
-            if (e != hipSuccess) return e;
-            raised.store(1, std::memory_order_release);
-        }
+        hipError_t e = raise_lds_limit(fn, kPieceLdsMax);
+        if (e != hipSuccess) return e;
     }
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    hipError_t e = device_cus(cus);
     if (e != hipSuccess) return e;
     constexpr int64_t G = 64 >> L;
     constexpr int NW = kPieceThreads / 64;
@@ -557,8 +552,7 @@ hipError_t launch_piece_one(const ProjArgs& a, hipStream_t s)
     if (ct < 1) ct = 1;
     {
         int bpc = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &bpc, fn, kPieceThreads, piece_lds_bytes<BITS>(MT, XREG, L, J, a.K, (T + (int64_t)cus * NW - 1) / ((int64_t)cus * NW) + ct));
+        e = occupancy(bpc, fn, kPieceThreads, piece_lds_bytes<BITS>(MT, XREG, L, J, a.K, (T + (int64_t)cus * NW - 1) / ((int64_t)cus * NW) + ct));
         if (e != hipSuccess) return e;
         if (bpc < 1) bpc = 1;
         if (bpc * NW > piece_max_waves_per_cu<BITS, MT>()) bpc = piece_max_waves_per_cu<BITS, MT>() / NW;
@@ -576,7 +570,7 @@ hipError_t launch_piece_one(const ProjArgs& a, hipStream_t s)
         lds = piece_lds_bytes<BITS>(MT, XREG, L, J, a.K, tmax);
         if (lds > kPieceLdsMax) return hipErrorInvalidValue;
         int bpc = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, kPieceThreads, lds);
+        e = occupancy(bpc, fn, kPieceThreads, lds);
         if (e != hipSuccess) return e;
         if (bpc < 1) bpc = 1;
         if (bpc * NW > piece_max_waves_per_cu<BITS, MT>()) bpc = piece_max_waves_per_cu<BITS, MT>() / NW;

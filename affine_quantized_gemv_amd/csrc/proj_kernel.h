@@ -29,6 +29,7 @@
 // docs/turing.md, section 5.
 #pragma once
 #include "aqg_device.h"
+#include "host_query.h"
 #include "kernels.h"
 #include "pair_plans.h"
 
@@ -91,15 +92,21 @@ __device__ __forceinline__ void load_unit(const uint32_t* __restrict__ p, uint32
 // Pre-scaled pair operands and constants of the x values that one plan covers
 // (a 64-k group for PairPlan, a 16-byte piece's 128/b k for PiecePlan), in the
 // plan's order: xq[i] = (x[LO_K] * 2^LO_E) | (x[HI_K] * 2^HI_E) << 16,
-// X = sum of the covered x (each code once: its significance-0 subcode),
-// T = 128 * sum of the pre-scaled halves.  Sums run in pair order, low half
-// first; every caller uses this one routine, so the constants are identical
-// wherever x is kept.
+// X = sum of the covered x (each code once: its significance-0 subcode), and
+// T = the code offset 128 * (sum of the pre-scaled halves) as the consumers'
+// own chain computes it: the same v_dot2 sequence over the same operands
+// (pairs 4c, 4c + 2 into one sum, 4c + 1, 4c + 3 into the other, then their
+// sum) with every code field zero, i.e. the pair 0x43004300 = (128, 128).
+// A unit whose codes are all zero therefore gives d == T bit for bit and
+// contributes exactly bias * X, not a rounding residue of the offset; other
+// codes leave the usual fp32 rounding of d.  Every caller uses this one
+// routine, so the constants are identical wherever x is kept.
 template <class P, int NXW>
 __device__ __forceinline__ void plan_x_operands(const uint32_t (&xw)[NXW], uint32_t (&xq)[P::NP],
                                                 float& X, float& T)
 {
-    float xs = 0.0f, ts = 0.0f;
+    static_assert(P::NP % 4 == 0, "the consumers take pairs four at a time");
+    float xs = 0.0f;
     static_for<0, P::NP>([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         const uint32_t hl = half_of(xw, P::LO_K[i]);
@@ -109,11 +116,17 @@ __device__ __forceinline__ void plan_x_operands(const uint32_t (&xw)[NXW], uint3
         const uint32_t lo = bf16_scale_pow2<P::LO_E[i]>(hl);
         const uint32_t hi = bf16_scale_pow2<P::HI_E[i]>(hh);
         xq[i] = lo | (hi << 16);
-        ts += bf16_to_f32(lo);
-        ts += bf16_to_f32(hi);
+    });
+    float t0 = 0.0f, t1 = 0.0f;
+    static_for<0, P::NP / 4>([&](auto C) __attribute__((always_inline)) {
+        constexpr int c = decltype(C)::value;
+        t0 = dot2(kZeroCodePair, xq[4 * c + 0], t0);
+        t1 = dot2(kZeroCodePair, xq[4 * c + 1], t1);
+        t0 = dot2(kZeroCodePair, xq[4 * c + 2], t0);
+        t1 = dot2(kZeroCodePair, xq[4 * c + 3], t1);
     });
     X = xs;
-    T = 128.0f * ts;
+    T = t0 + t1;
 }
 
 template <int BITS>

@@ -305,16 +305,11 @@ hipError_t launch_stream_one(const ProjArgs& a, const LaunchCfg& c, hipStream_t 
     const void* fn = reinterpret_cast<const void*>(&stream_kernel<BITS, MT, SW, XREG>);
     {
         // allow up to 160 KB of dynamic LDS (gfx950 has 160 KB per CU); once
-        static std::atomic<int> raised{0};
-        if (!raised.load(std::memory_order_acquire)) {
-            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
-            if (e != hipSuccess) return e;
-            raised.store(1, std::memory_order_release);
-        }
+        hipError_t e = raise_lds_limit(fn, kStreamLdsMax);
+        if (e != hipSuccess) return e;
     }
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    hipError_t e = device_cus(cus);
     if (e != hipSuccess) return e;
     const int L = c.lpr_log2;
     const int64_t G = 64 >> L;
@@ -332,7 +327,7 @@ hipError_t launch_stream_one(const ProjArgs& a, const LaunchCfg& c, hipStream_t 
         lds = stream_lds_bytes<BITS, MT, XREG>(c, a.K, tmax);
         if (lds > kStreamLdsMax) return hipErrorInvalidValue;
         int bpc = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, 64 * c.nwaves, lds);
+        e = occupancy(bpc, fn, 64 * c.nwaves, lds);
         if (e != hipSuccess) return e;
         if (bpc < 1) bpc = 1;
         int64_t w = (int64_t)bpc * cus * c.nwaves;

@@ -85,7 +85,11 @@ int aqg_abi_version(void);
 /* Static description of a status code (never NULL). */
 const char* aqg_status_string(int status);
 
-/* Workspace bytes a call of the given kind and shape needs (0 = none). */
+/* Workspace bytes a call of the given kind and shape needs (0 = none).
+ * Asked of the library before a call rather than assumed: a split-K test
+ * that passed a null partials buffer wrote through it (TensorFold PR #849,
+ * the split-K fix in the PR body).  The library checks the size it is given
+ * against this value and refuses a shorter one. */
 size_t aqg_workspace_bytes(int kind, int M, int N, int K);
 
 /*
@@ -140,9 +144,26 @@ int aqg_swiglu_bf16(const void* x, const void* Wg, const void* Wu, void* out, in
 /*
  * Unpack codes: codes[n][k] = q[n,k] as uint8, through the same device code
  * path the affine GEMVs use to read their weights.  Wq: uint32[N][K*b/32];
- * codes: uint8[N][K].  K % 64 == 0.  A test hook for bit-exact checks.
+ * codes: uint8[N][K] (16-byte aligned, not overlapping Wq).  K % 64 == 0,
+ * bits in 2..8.  A test hook for bit-exact checks of the bit-stream reading
+ * above: every code keeps its exact value (TensorFold PR #849, "What this
+ * changes" and the module-width comment).
  */
 int aqg_unpack_codes(int bits, const uint32_t* Wq, uint8_t* codes, int N, int K, void* stream);
+
+/*
+ * Diagnostics (test hook; launches nothing).  The kernel family a call of
+ * `kind` (AQG_KIND_DENSE, 2..8 for affine widths, AQG_KIND_SWIGLU) with
+ * this shape runs on the current device (with no device: on one of 256
+ * CUs, the MI355X's count), as an id >= 0 whose name
+ * aqg_path_name() gives; *columns (if not NULL) receives the kernel's
+ * column count (M padded).  Within one id and column count every output is
+ * computed by the same chain of operations whatever M is, so tests of row
+ * independence and exactness can state which kernel they cover.  Returns
+ * -status (e.g. -AQG_ERR_UNSUPPORTED) for a call the library would refuse.
+ */
+int aqg_dispatch_path(int kind, int M, int N, int K, int* columns);
+const char* aqg_path_name(int path);
 
 #ifdef __cplusplus
 }

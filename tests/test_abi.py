@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     expected = {"aqg_abi_version", "aqg_status_string", "aqg_workspace_bytes", "aqg_gemv_bf16",
-                "aqg_swiglu_bf16", "aqg_unpack_codes"} | {"aqg_gemv_affine_q%d" % b for b in range(2, 9)}
+                "aqg_swiglu_bf16", "aqg_unpack_codes", "aqg_dispatch_path",
+                "aqg_path_name"} | {"aqg_gemv_affine_q%d" % b for b in range(2, 9)}
     assert set(names) == expected
 
 
@@ -135,3 +136,23 @@ def test_python_binding_refuses_host_tensors():
     x = torch.zeros(1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         aqg.gemv_bf16(x, torch.zeros(4, 64, dtype=torch.bfloat16))
+
+
+def test_dispatch_query_names_the_families_the_gpu_tests_cover(lib):
+    """The exactness tests state the kernel family of each case; the library's
+    dispatch query (no launch; 256 CUs without a device) must agree, so a
+    change of thresholds cannot move a case off the kernel it pins unnoticed."""
+    import test_gpu_exact
+    for family, bits, M, N, K in test_gpu_exact.CASES:
+        assert aqg.dispatch_path(bits, M, N, K)[0] == family, (family, bits, M, N, K)
+
+
+def test_dispatch_query_refuses_what_the_calls_refuse(lib):
+    cols = ctypes.c_int(0)
+    assert lib.aqg_dispatch_path(4, 33, 100, 1024, ctypes.byref(cols)) == -aqg.AQG_ERR_UNSUPPORTED
+    assert lib.aqg_dispatch_path(4, 1, 100, 1000, ctypes.byref(cols)) == -aqg.AQG_ERR_UNSUPPORTED
+    assert lib.aqg_dispatch_path(0, 0, 100, 1024, ctypes.byref(cols)) == -aqg.AQG_ERR_INVALID_ARG
+    assert lib.aqg_dispatch_path(1, 1, 100, 1024, None) == -aqg.AQG_ERR_INVALID_ARG
+    assert lib.aqg_path_name(99) == b"unknown"
+    p = lib.aqg_dispatch_path(0, 1, 1536, 1536, ctypes.byref(cols))
+    assert p >= 0 and cols.value == 1 and lib.aqg_path_name(p) == b"piece"
