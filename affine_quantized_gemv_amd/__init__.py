@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "lib_path", "load", "AqgError", "abi_version", "status_string", "workspace_bytes", "dispatch_path",
-    "gemv_bf16", "gemv_affine", "swiglu_bf16", "unpack_codes",
+    "gemv_bf16", "gemv_affine", "swiglu_bf16", "unpack_codes", "gemv_bf16_argmax", "gemv_affine_argmax",
     "gemv_affine_q2", "gemv_affine_q3", "gemv_affine_q4", "gemv_affine_q5",
     "gemv_affine_q6", "gemv_affine_q7", "gemv_affine_q8",
     "AQG_OK", "AQG_ERR_INVALID_ARG", "AQG_ERR_UNSUPPORTED", "AQG_ERR_ALIGNMENT",
@@ -31,7 +31,7 @@ __all__ = [
 
 AQG_OK, AQG_ERR_INVALID_ARG, AQG_ERR_UNSUPPORTED, AQG_ERR_ALIGNMENT, AQG_ERR_LAUNCH, AQG_ERR_DEVICE = range(6)
 AQG_OUT_BF16, AQG_OUT_F32 = 0, 1
-AQG_KIND_DENSE, AQG_KIND_SWIGLU = 0, 9
+AQG_KIND_DENSE, AQG_KIND_SWIGLU, AQG_KIND_ARGMAX_DENSE = 0, 9, 32
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -75,6 +75,12 @@ def load():
         lib.aqg_swiglu_bf16.argtypes = [P, P, P, P, I, I, I, I, P, Z, P]
         lib.aqg_unpack_codes.restype = I
         lib.aqg_unpack_codes.argtypes = [I, P, P, I, I, P]
+        lib.aqg_gemv_bf16_argmax.restype = I
+        lib.aqg_gemv_bf16_argmax.argtypes = [P, P, P, P, I, I, I, P, Z, P]
+        for b in range(2, 9):
+            f = getattr(lib, "aqg_gemv_affine_q%d_argmax" % b)
+            f.restype = I
+            f.argtypes = [P, P, P, P, P, P, I, I, I, P, Z, P]
         lib.aqg_dispatch_path.restype = I
         lib.aqg_dispatch_path.argtypes = [I, I, I, I, ctypes.POINTER(I)]
         lib.aqg_path_name.restype = ctypes.c_char_p
@@ -222,6 +228,66 @@ def swiglu_bf16(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, out_dtype=t
     _check(load().aqg_swiglu_bf16(_p(x), _p(Wg), _p(Wu), _p(y), M, N, K, _odt(y), ws, wsb, _stream(x)),
            "aqg_swiglu_bf16")
     return y
+
+
+def _argmax_out(M: int, like: torch.Tensor, out):
+    if out is None:
+        return (torch.empty(M, dtype=torch.float32, device=like.device),
+                torch.empty(M, dtype=torch.int32, device=like.device))
+    val, idx = out
+    _dev(val, "out[0]", (torch.float32,), ndim=1)
+    _dev(idx, "out[1]", (torch.int32,), ndim=1)
+    if val.shape[0] != M or idx.shape[0] != M:
+        raise ValueError("argmax outputs must have %d rows" % M)
+    return val, idx
+
+
+def _argmax_ws(kind: int, M: int, N: int, K: int, like: torch.Tensor, workspace):
+    need = workspace_bytes(kind, M, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=like.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace needs %d bytes" % need)
+    return workspace
+
+
+def gemv_bf16_argmax(x: torch.Tensor, W: torch.Tensor, out=None, workspace=None):
+    """(max value fp32 [M], index int32 [M]) of each row of x . W^T; the lowest
+    index wins ties; the logits are not written."""
+    _dev(x, "x", (torch.bfloat16,))
+    _dev(W, "W", (torch.bfloat16,))
+    M, K = x.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, %d]" % K)
+    val, idx = _argmax_out(M, x, out)
+    ws = _argmax_ws(AQG_KIND_ARGMAX_DENSE, M, N, K, x, workspace)
+    _check(load().aqg_gemv_bf16_argmax(_p(x), _p(W), _p(val), _p(idx), M, N, K, *_ws(ws), _stream(x)),
+           "aqg_gemv_bf16_argmax")
+    return val, idx
+
+
+def gemv_affine_argmax(x: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+                       bits: int, out=None, workspace=None):
+    """Row argmax of the affine b-bit GEMV (see gemv_affine and gemv_bf16_argmax)."""
+    if bits not in range(2, 9):
+        raise ValueError("bits must be in 2..8")
+    _dev(x, "x", (torch.bfloat16,))
+    _dev(Wq, "Wq", (torch.int32, torch.uint32))
+    _dev(scales, "scales", (torch.bfloat16,))
+    _dev(biases, "biases", (torch.bfloat16,))
+    M, K = x.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] * 32 != K * bits:
+        raise ValueError("Wq must be [N, K*bits/32]")
+    if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
+        raise ValueError("scales and biases must be [N, K/64]")
+    val, idx = _argmax_out(M, x, out)
+    ws = _argmax_ws(AQG_KIND_ARGMAX_DENSE + bits, M, N, K, x, workspace)
+    fn = getattr(load(), "aqg_gemv_affine_q%d_argmax" % bits)
+    _check(fn(_p(x), _p(Wq), _p(scales), _p(biases), _p(val), _p(idx), M, N, K, *_ws(ws), _stream(x)),
+           "aqg_gemv_affine_q%d_argmax" % bits)
+    return val, idx
 
 
 def unpack_codes(Wq: torch.Tensor, bits: int, K: int, out=None) -> torch.Tensor:

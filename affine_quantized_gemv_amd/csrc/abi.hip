@@ -14,6 +14,7 @@
 #include <cstring>
 
 #include "aqgemv.h"
+#include "host_query.h"
 #include "kernels.h"
 
 namespace {
@@ -129,6 +130,110 @@ int run_affine(int bits, const void* x, const uint32_t* Wq, const void* scales, 
                           stream);
 }
 
+// ---------------------------------------------------------- row argmax
+
+constexpr int kArgmaxChunk = 8192;        // columns per partial when the GEMV writes y first
+constexpr int kArgmaxRowsCap = 32;        // partial rows in the workspace (M <= 32)
+constexpr int kArgmaxProducersPerCu = 32; // wavefront slots per CU: no kernel launches more
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// How a row-argmax call runs and the workspace it needs: with a fused
+// epilogue the kernel writes (value, index) partials per producer; otherwise
+// the GEMV writes fp32 y into the workspace and a row reduction makes the
+// partials (one per column chunk).
+struct ArgmaxPlan {
+    bool fused;
+    size_t ybytes;     // fp32 y in front of the partials (0 when fused)
+    int64_t slots;     // partials per row
+    size_t bytes;      // total workspace
+};
+
+ArgmaxPlan argmax_plan(int bits, int M, int N, int K)
+{
+    ArgmaxPlan p{};
+    const aqg::LaunchCfg cfg = aqg::choose_config(bits, false, M, N, K);
+    p.fused = aqg::argmax_fused(cfg);
+    if (p.fused) {
+        int cus = 256;
+        if (aqg::detail::device_cus(cus) != hipSuccess) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        p.ybytes = 0;
+        p.slots = (int64_t)kArgmaxProducersPerCu * cus;
+    } else {
+        p.ybytes = round_up((size_t)M * N * 4, 256);
+        p.slots = ((int64_t)N + kArgmaxChunk - 1) / kArgmaxChunk;
+    }
+    p.bytes = p.ybytes + (size_t)kArgmaxRowsCap * p.slots * 8;
+    return p;
+}
+
+int run_argmax(int bits, const void* x, const void* w0, const void* scales, const void* biases, float* val,
+               int32_t* idx, int M, int N, int K, void* ws, size_t wsb, void* stream)
+{
+    if (!x || !w0 || !val || !idx || (bits && (!scales || !biases))) return AQG_ERR_INVALID_ARG;
+    if (M <= 0 || N <= 0 || K <= 0) return AQG_ERR_INVALID_ARG;
+    if (M > 32) return AQG_ERR_UNSUPPORTED;
+    if (bits == 0 ? (K % 8 != 0) : (K % 64 != 0)) return AQG_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(w0, 16) || !aligned(val, 4) || !aligned(idx, 4)) return AQG_ERR_ALIGNMENT;
+    if (bits && (!aligned(scales, 4) || !aligned(biases, 4))) return AQG_ERR_ALIGNMENT;
+    const ArgmaxPlan plan = argmax_plan(bits, M, N, K);
+    if (!ws || wsb < plan.bytes) return AQG_ERR_INVALID_ARG;
+    if (!aligned(ws, 16)) return AQG_ERR_ALIGNMENT;
+    const size_t xbytes = (size_t)M * K * 2;
+    const size_t wbytes = bits ? (size_t)N * K / 8 * bits : (size_t)N * K * 2;
+    const size_t gbytes = (size_t)N * (K / 64) * 2;
+    const size_t ob = (size_t)M * 4;
+    const void* ins[4] = {x, w0, bits ? scales : nullptr, bits ? biases : nullptr};
+    const size_t insz[4] = {xbytes, wbytes, gbytes, gbytes};
+    const void* outs[3] = {val, idx, ws};
+    const size_t outsz[3] = {ob, ob, plan.bytes};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 4; ++i)
+            if (overlap(outs[o], outsz[o], ins[i], insz[i])) return AQG_ERR_INVALID_ARG;
+        for (int p = o + 1; p < 3; ++p)
+            if (overlap(outs[o], outsz[o], outs[p], outsz[p])) return AQG_ERR_INVALID_ARG;
+    }
+    int st = check_device();
+    if (st != AQG_OK) return st;
+
+    const aqg::LaunchCfg cfg = aqg::choose_config(bits, false, M, N, K);
+    aqg::ProjArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.w0 = w0;
+    a.scales = static_cast<const uint16_t*>(scales);
+    a.biases = static_cast<const uint16_t*>(biases);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.KT = cfg.KT;
+    a.lpr_log2 = cfg.lpr_log2;
+    a.ksplit_log2 = cfg.ksplit_log2;
+    a.tpw = cfg.tpw;
+    a.out_f32 = 1;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char* part = static_cast<char*>(ws) + plan.ybytes;
+    hipError_t e;
+    if (plan.fused) {
+        int64_t producers = 0;
+        a.y = nullptr;
+        a.amx = part;
+        a.amx_slots = plan.slots;
+        a.amx_producers = &producers;
+        e = aqg::launch_proj(bits, false, a, cfg, s);
+        if (e == hipSuccess) e = aqg::launch_argmax_final(part, plan.slots, producers, M, val, idx, s);
+    } else {
+        a.y = ws;
+        e = aqg::launch_proj(bits, false, a, cfg, s);
+        if (e == hipSuccess) e = aqg::launch_argmax_rows(static_cast<const float*>(ws), M, N, kArgmaxChunk, part,
+                                                         plan.slots, s);
+        if (e == hipSuccess) e = aqg::launch_argmax_final(part, plan.slots, plan.slots, M, val, idx, s);
+    }
+    return finish(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,9 +258,34 @@ const char* aqg_status_string(int status)
 
 size_t aqg_workspace_bytes(int kind, int M, int N, int K)
 {
-    (void)kind; (void)M; (void)N; (void)K;
-    return 0;  // no variant uses split-K partials yet
+    if (M <= 0 || N <= 0 || K <= 0 || M > 32) return 0;
+    if (kind == AQG_KIND_ARGMAX_DENSE || (kind >= AQG_KIND_ARGMAX_DENSE + 2 && kind <= AQG_KIND_ARGMAX_DENSE + 8))
+        return argmax_plan(kind - AQG_KIND_ARGMAX_DENSE, M, N, K).bytes;
+    return 0;  // the GEMVs and SwiGLUs keep their partial sums in registers and LDS
 }
+
+int aqg_gemv_bf16_argmax(const void* x, const void* W, float* max_val, int32_t* max_idx, int M, int N, int K,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    return run_argmax(0, x, W, nullptr, nullptr, max_val, max_idx, M, N, K, workspace, workspace_bytes, stream);
+}
+
+#define AQG_AFFINE_ARGMAX_ENTRY(B)                                                                          \
+    int aqg_gemv_affine_q##B##_argmax(const void* x, const uint32_t* Wq, const void* scales,               \
+                                      const void* biases, float* max_val, int32_t* max_idx, int M, int N,  \
+                                      int K, void* workspace, size_t workspace_bytes, void* stream)        \
+    {                                                                                                       \
+        return run_argmax(B, x, Wq, scales, biases, max_val, max_idx, M, N, K, workspace, workspace_bytes,  \
+                          stream);                                                                          \
+    }
+AQG_AFFINE_ARGMAX_ENTRY(2)
+AQG_AFFINE_ARGMAX_ENTRY(3)
+AQG_AFFINE_ARGMAX_ENTRY(4)
+AQG_AFFINE_ARGMAX_ENTRY(5)
+AQG_AFFINE_ARGMAX_ENTRY(6)
+AQG_AFFINE_ARGMAX_ENTRY(7)
+AQG_AFFINE_ARGMAX_ENTRY(8)
+#undef AQG_AFFINE_ARGMAX_ENTRY
 
 int aqg_gemv_bf16(const void* x, const void* W, void* y, int M, int N, int K, int out_dtype,
                   void* workspace, size_t workspace_bytes, void* stream)

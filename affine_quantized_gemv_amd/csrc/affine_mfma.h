@@ -43,6 +43,7 @@
 // Format: TensorFold PR #849, "qwen3_5 cuda: mixed-width MLX checkpoints, 2
 // to 8 bits in groups of 64" (MLX affine mode, groups of 64).
 #pragma once
+#include "argmax.h"
 #include "mfma_stream.h"
 
 namespace aqg {
@@ -257,6 +258,15 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
     const bool vec_store = a.N % 4 == 0 && (int64_t)a.M * a.N * esz < 0x7FFFFFF0;
     const __amdgpu_buffer_rsrc_t ry = tile_rsrc(a.y, (int64_t)a.M * a.N * esz);
     constexpr uint32_t kDrop = 0x80000000u;
+    // row argmax (a.amx, whole tiles only): the lane's running maximum of
+    // its outputs of row 16b + r, per column block b
+    float amx_v[NB];
+    int amx_i[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        amx_v[b] = amx_neutral_value();
+        amx_i[b] = kAmxNoIndex;
+    }
 
     auto consume = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
@@ -366,7 +376,11 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
                     float v[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = acc[b][i] + accb[b][i];
-                    if (vec_store) {
+                    if (a.amx) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (m < a.M && n0 + i < a.N) amx_take(amx_v[b], amx_i[b], v[i], (int)(n0 + i));
+                    } else if (vec_store) {
                         const uint32_t off = (m < a.M && n0 < a.N) ? (uint32_t)(((int64_t)m * a.N + n0) * esz) : kDrop;
                         if (a.out_f32) {
                             __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]),
@@ -500,7 +514,10 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     // without a K split nothing below waits for the other wavefronts
-    if (nkc == 1 && my_tiles == 0) return;
+    if (nkc == 1 && my_tiles == 0) {
+        if (a.amx && lane < kArgmaxRows) amx_store(a.amx, a.amx_slots, u, lane, amx_neutral_value(), kAmxNoIndex);
+        return;
+    }
 
     const int64_t nitems = my_tiles * (kb_hi - kb_lo);
     int64_t base = 0;
@@ -520,7 +537,21 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
             }
         });
     }
-    if (nkc == 1) return;
+    if (nkc == 1) {
+        if (a.amx) {
+            // the four lane quarters hold the same rows: combine, and quarter 0
+            // writes this wavefront's partials of rows 16b + r
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                amx_xor(amx_v[b], amx_i[b], 16);
+                amx_xor(amx_v[b], amx_i[b], 32);
+                if (c == 0) amx_store(a.amx, a.amx_slots, u, 16 * b + r, amx_v[b], amx_i[b]);
+            }
+            if (NB == 1 && lane >= 16 && lane < kArgmaxRows)
+                amx_store(a.amx, a.amx_slots, u, lane, amx_neutral_value(), kAmxNoIndex);
+        }
+        return;
+    }
 
     // K split: sum the chunks' partial tiles in chunk order and store
     __syncthreads();
@@ -599,6 +630,9 @@ hipError_t launch_affine_mfma_one(const ProjArgs& a, int nkc, hipStream_t s)
         if (occ >= bpc || bpc == 1) break;
         bpc = occ < 1 ? 1 : occ;
     }
+    // row argmax: one partial per wavefront, whole tiles only
+    if (a.amx && (nkc != 1 || (int64_t)blocks * (kAffineMfmaThreads / 64) > a.amx_slots)) return hipErrorInvalidValue;
+    if (a.amx_producers) *a.amx_producers = (int64_t)blocks * (kAffineMfmaThreads / 64);
     ProjArgs a2 = a;
     a2.tpw = 1;
     a2.tmax = tmax;

@@ -1,0 +1,84 @@
+// Reductions of row-argmax partials (argmax.h): the final combine over the
+// producers of a fused GEMV epilogue, and the per-chunk maxima of an fp32
+// output for kernels without a fused epilogue.
+#include "argmax.h"
+#include "kernels.h"
+
+namespace aqg {
+namespace detail {
+namespace {
+
+constexpr int kArgmaxThreads = 256;
+
+// Block-wide combine of one (value, index) per thread; thread 0 returns it.
+__device__ __forceinline__ void amx_block(float& bv, int& bi)
+{
+    __shared__ float sv[kArgmaxThreads / 64];
+    __shared__ int si[kArgmaxThreads / 64];
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) amx_xor(bv, bi, s);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        sv[wave] = bv;
+        si[wave] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0)
+        for (int w = 1; w < kArgmaxThreads / 64; ++w) amx_take(bv, bi, sv[w], si[w]);
+}
+
+// One workgroup per row m: the best of the P producers' partials.
+__global__ void __launch_bounds__(kArgmaxThreads) argmax_final_kernel(const int2* __restrict__ part, int64_t slots,
+                                                                      int64_t P, float* __restrict__ val,
+                                                                      int* __restrict__ idx)
+{
+    const int m = blockIdx.x;
+    float bv = amx_neutral_value();
+    int bi = kAmxNoIndex;
+    for (int64_t p = threadIdx.x; p < P; p += kArgmaxThreads) {
+        const int2 e = part[m * slots + p];
+        amx_take(bv, bi, __int_as_float(e.x), e.y);
+    }
+    amx_block(bv, bi);
+    if (threadIdx.x == 0) {
+        val[m] = bv;
+        idx[m] = bi;
+    }
+}
+
+// Workgroup (c, m): the best of y[m][c*chunk .. (c+1)*chunk) as producer c.
+__global__ void __launch_bounds__(kArgmaxThreads) argmax_rows_kernel(const float* __restrict__ y, int N, int chunk,
+                                                                     int2* __restrict__ part, int64_t slots)
+{
+    const int c = blockIdx.x, m = blockIdx.y;
+    const int64_t n0 = (int64_t)c * chunk;
+    const int64_t n1 = n0 + chunk < N ? n0 + chunk : N;
+    float bv = amx_neutral_value();
+    int bi = kAmxNoIndex;
+    for (int64_t n = n0 + threadIdx.x; n < n1; n += kArgmaxThreads) amx_take(bv, bi, y[(int64_t)m * N + n], (int)n);
+    amx_block(bv, bi);
+    if (threadIdx.x == 0) part[m * slots + c] = make_int2(__float_as_int(bv), bi);
+}
+
+}  // namespace
+}  // namespace detail
+
+hipError_t launch_argmax_final(const void* part, int64_t slots, int64_t P, int M, float* val, int* idx,
+                               hipStream_t s)
+{
+    if (P < 1 || P > slots) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(detail::argmax_final_kernel, dim3(M), dim3(detail::kArgmaxThreads), 0, s,
+                       static_cast<const int2*>(part), slots, P, val, idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_argmax_rows(const float* y, int M, int N, int chunk, void* part, int64_t slots, hipStream_t s)
+{
+    const int chunks = (N + chunk - 1) / chunk;
+    if (chunks > slots) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(detail::argmax_rows_kernel, dim3(chunks, M), dim3(detail::kArgmaxThreads), 0, s, y, N, chunk,
+                       static_cast<int2*>(part), slots);
+    return hipGetLastError();
+}
+
+}  // namespace aqg

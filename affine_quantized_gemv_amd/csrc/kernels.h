@@ -23,6 +23,16 @@ struct ProjArgs {
     int out_f32;             // 1: store fp32, 0: store bf16 (RNE)
     int64_t tpw;             // stream path: row tiles per super-tile
     int64_t tmax;            // stream path: most row tiles any wavefront finishes
+    // Row argmax instead of a store (null: store y).  The kernel writes one
+    // (value, index) partial per output row m for each of its producers
+    // (wavefronts or workgroups, per kernel) to amx[m * amx_slots + producer];
+    // a producer with no rows writes (-inf, INT_MAX).  amx_slots: producers
+    // the buffer holds per row (a launch that needs more fails with
+    // hipErrorInvalidValue); the launcher reports the producers it launched
+    // through the host pointer amx_producers.
+    void* amx;
+    int64_t amx_slots;
+    int64_t* amx_producers;
 };
 
 enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6,
@@ -88,6 +98,17 @@ hipError_t launch_affine_split(const ProjArgs& a, const LaunchCfg& c, hipStream_
 // Affine matrix-core launcher, BITS = 2, 4 or 8 (affine_mfma*.hip).
 template <int BITS>
 hipError_t launch_affine_mfma(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+// Row-argmax partials: the reduction over producers (argmax.hip).  part:
+// int2 [M][slots] (value bits, index), producers 0 .. P-1 of each row.
+hipError_t launch_argmax_final(const void* part, int64_t slots, int64_t P, int M, float* val, int* idx,
+                               hipStream_t s);
+// Row-argmax partials of y fp32 [M][N] in chunks of `chunk` columns:
+// producers 0 .. ceil(N / chunk) - 1 of part [M][slots].
+hipError_t launch_argmax_rows(const float* y, int M, int N, int chunk, void* part, int64_t slots, hipStream_t s);
+// Whether the kernel of cfg writes row-argmax partials itself (else the
+// caller runs the GEMV into fp32 and reduces the rows).
+bool argmax_fused(const LaunchCfg& cfg);
 
 // bits: 0 = dense bf16, 2..8 = affine width.
 LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K);

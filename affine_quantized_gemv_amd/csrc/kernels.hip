@@ -381,6 +381,11 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     return choose_valu(bits, swiglu, M, N, K);
 }
 
+bool argmax_fused(const LaunchCfg& c)
+{
+    return c.path == PATH_PIECE || c.path == PATH_MFMA_TILE || (c.path == PATH_AFFINE_MFMA && c.ksplit_log2 == 0);
+}
+
 hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
     if (c.path == PATH_AFFINE_TILE) {

@@ -41,6 +41,7 @@
 // M = 1..32 decode shapes).
 #pragma once
 
+#include "argmax.h"
 #include "mfma_kernel.h"
 #include "piece_kernel.h"
 
@@ -127,7 +128,11 @@ __global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
     const int64_t G8 = gridDim.x / 8;
     const int64_t first = (gridDim.x % 8 == 0) ? (int64_t)(blockIdx.x % 8) * G8 + blockIdx.x / 8 : blockIdx.x;
     const int64_t stride = gridDim.x;
-    if (first >= T) return;
+    if (first >= T) {
+        if (a.amx && threadIdx.x < kArgmaxRows)
+            amx_store(a.amx, a.amx_slots, blockIdx.x, threadIdx.x, amx_neutral_value(), kAmxNoIndex);
+        return;
+    }
     const int64_t ntile = (T - 1 - first) / stride + 1;   // tiles of this workgroup (uniform)
 
     float* part = reinterpret_cast<float*>(mfma_tile_lds<NBUF, L::PART>());
@@ -179,6 +184,11 @@ __global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
     const int esz = a.out_f32 ? 4 : 2;
     const __amdgpu_buffer_rsrc_t ry = tile_rsrc(a.y, (int64_t)a.M * a.N * esz);
     constexpr uint32_t kDrop = 0x80000000u;   // beyond any output range
+    // row argmax (a.amx): the thread's running maximum of its outputs, all of
+    // row om; the store is still issued, out of range, so that every
+    // wavefront's count of memory operations per step stays the same
+    float amx_v = amx_neutral_value();
+    int amx_i = kAmxNoIndex;
 
     auto step = [&](int64_t j, auto Bc) __attribute__((always_inline)) {
         constexpr int B = decltype(Bc)::value;
@@ -209,7 +219,12 @@ __global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
 #pragma unroll
         for (int w = 1; w < NW; ++w) v += p[w * L::PW];
         const int64_t n = (first + j * stride) * 16 + on;
-        const uint32_t off = (red && om < a.M && n < a.N) ? (uint32_t)(((int64_t)om * a.N + n) * esz) : kDrop;
+        const bool live = red && om < a.M && n < a.N;
+        uint32_t off = live ? (uint32_t)(((int64_t)om * a.N + n) * esz) : kDrop;
+        if (a.amx) {
+            if (live) amx_take(amx_v, amx_i, v, (int)n);
+            off = kDrop;
+        }
         if (a.out_f32) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, off, 0, 0);
         else __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), ry, off, 0, 0);
 
@@ -248,6 +263,12 @@ __global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
             if (j < ntile) step(j, Bc);
         });
     }
+    if (a.amx) {
+        // the 16 threads of row om are one 16-lane row of a wavefront
+#pragma unroll
+        for (int sh = 1; sh < 16; sh <<= 1) amx_xor(amx_v, amx_i, sh);
+        if (on == 0 && om < kArgmaxRows) amx_store(a.amx, a.amx_slots, blockIdx.x, om, amx_v, amx_i);
+    }
 }
 
 // Tile buffers for a K: enough that NBUF - 1 tiles (~48 KB or more) are in
@@ -285,6 +306,8 @@ hipError_t launch_mfma_tile_one(const ProjArgs& a, hipStream_t s)
     const int64_t T = ((int64_t)a.N + 15) / 16;
     int64_t blocks = (int64_t)bpc * cus;
     if (blocks > T) blocks = T;
+    if (a.amx && blocks > a.amx_slots) return hipErrorInvalidValue;   // one partial per workgroup
+    if (a.amx_producers) *a.amx_producers = blocks;
     hipLaunchKernelGGL((mfma_tile_kernel<MT, KSW, NBUF, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }

@@ -41,6 +41,7 @@
 #pragma once
 #include <atomic>
 
+#include "argmax.h"
 #include "proj_kernel.h"
 
 namespace aqg {
@@ -470,7 +471,10 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
         fetch_ring();
         load_x([]() {}, Int<0>{});
     }
-    if (my_tiles == 0) return;
+    if (my_tiles == 0) {
+        if (a.amx && lane < MT) amx_store(a.amx, a.amx_slots, wg, lane, amx_neutral_value(), kAmxNoIndex);
+        return;
+    }
     int64_t bt = 0;
     for (; bt + 2 * RD <= my_tiles; bt += RD) {          // steady state
         static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
@@ -500,6 +504,26 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 
     // write out the staged outputs: value v of the wavefront's list is tile
     // v / (G*MT), row slot (v / MT) % G, output row m = v % MT
+    if (a.amx) {
+        // row argmax instead: lane l only sees outputs of row m = l % MT
+        // (64 and G*MT are multiples of MT), so it keeps one running maximum;
+        // the lanes of a row combine theirs and lane m writes the
+        // wavefront's partial of row m
+        float bv = amx_neutral_value();
+        int bi = kAmxNoIndex;
+        for (int v = lane; v < ti * PER_TILE; v += 64) {
+            const int t2 = v / PER_TILE;
+            const int r = v % PER_TILE;
+            const int m = r % MT;
+            const int64_t tile = (wg + (int64_t)(t2 / CT) * W) * CT + t2 % CT;
+            const int64_t n = tile * G + r / MT;
+            if (m < a.M && n < a.N) amx_take(bv, bi, obuf[v], (int)n);
+        }
+#pragma unroll
+        for (int sh = MT; sh < 64; sh <<= 1) amx_xor(bv, bi, sh);
+        if (lane < MT) amx_store(a.amx, a.amx_slots, wg, lane, bv, bi);
+        return;
+    }
     for (int v = lane; v < ti * PER_TILE; v += 64) {
         const int t2 = v / PER_TILE;
         const int r = v % PER_TILE;
@@ -580,6 +604,8 @@ hipError_t launch_piece_one(const ProjArgs& a, hipStream_t s)
         waves = w;
     }
     const int blocks = (int)((waves + NW - 1) / NW);
+    if (a.amx && (int64_t)blocks * NW > a.amx_slots) return hipErrorInvalidValue;   // one partial per wavefront
+    if (a.amx_producers) *a.amx_producers = (int64_t)blocks * NW;
     // the kernel deals super-tiles over all blocks*NW wavefronts
     tmax = ((st + (int64_t)blocks * NW - 1) / ((int64_t)blocks * NW)) * ct;
     lds = piece_lds_bytes<BITS>(MT, XREG, L, J, a.K, tmax);

@@ -43,9 +43,10 @@
  *  - out_dtype AQG_OUT_F32 writes the fp32 sums; AQG_OUT_BF16 writes exactly
  *    the round-to-nearest-even bf16 of the values the same call would write
  *    with AQG_OUT_F32 (kernels are deterministic).
- *  - workspace: scratch for split-K variants.  aqg_workspace_bytes() gives the
- *    size a call needs; NULL / 0 is valid when that size is 0, otherwise a
- *    smaller workspace is AQG_ERR_INVALID_ARG.
+ *  - workspace: scratch of the calls that need one (the row argmax).
+ *    aqg_workspace_bytes() gives the size a call needs; NULL / 0 is valid
+ *    when that size is 0, otherwise a smaller workspace is
+ *    AQG_ERR_INVALID_ARG.
  *  - Accumulation is fp32; the result of each (m, n) does not depend on M
  *    within one code path (rows are independent).
  *  - Thread safety: stateless apart from a per-device architecture check that
@@ -76,8 +77,9 @@ typedef enum {
 typedef enum { AQG_OUT_BF16 = 0, AQG_OUT_F32 = 1 } aqg_out_dtype;
 
 /* Kinds for aqg_workspace_bytes(). */
-#define AQG_KIND_DENSE 0   /* 2..8 = affine of that width */
+#define AQG_KIND_DENSE 0           /* 2..8 = affine GEMV of that width */
 #define AQG_KIND_SWIGLU 9
+#define AQG_KIND_ARGMAX_DENSE 32   /* + b (2..8) = affine row argmax of width b */
 
 /* Returns AQG_ABI_VERSION. */
 int aqg_abi_version(void);
@@ -140,6 +142,51 @@ int aqg_gemv_affine_q8(const void* x, const uint32_t* Wq, const void* scales, co
  */
 int aqg_swiglu_bf16(const void* x, const void* Wg, const void* Wu, void* out, int M, int N, int K,
                     int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Row argmax of a projection (the LM head of greedy decoding), without
+ * writing the logits: for each row m < M,
+ *   max_idx[m] = the lowest n with y[m,n] = max over n' of y[m,n'],
+ *   max_val[m] = y[m, max_idx[m]],
+ * where y is the fp32 result the GEMV of the same arguments writes with
+ * AQG_OUT_F32 (the same kernels and arithmetic; only the epilogue differs).
+ * The lower index wins on equal values (nvfp4-megamoe-kernel commit log,
+ * "Router: full kernel stack", Step 2, topk_select); the draw happens on the
+ * device, as the served decoder does (TensorFold PR #849, the note on the
+ * MLX affine 4-bit checkpoint on the native CUDA server: sample.cu draws on
+ * the device).  NaN values never win; a row of NaNs gives index INT32_MAX.
+ *   max_val: float[M]; max_idx: int32[M] (device, 4-byte aligned, not
+ *   overlapping any input, each other or the workspace).
+ *   workspace: at least aqg_workspace_bytes(AQG_KIND_ARGMAX_DENSE (+ b), M,
+ *   N, K) bytes, 16-byte aligned (required: per-producer partial maxima,
+ *   and for shapes whose kernel has no argmax epilogue the fp32 y; asked of
+ *   the library for the shape, since the kernel choice decides it).  Its
+ *   contents on entry do not matter and are garbage afterwards.
+ * Other arguments and rules as for the GEMVs above.
+ */
+int aqg_gemv_bf16_argmax(const void* x, const void* W, float* max_val, int32_t* max_idx, int M, int N, int K,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q2_argmax(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                              float* max_val, int32_t* max_idx, int M, int N, int K,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q3_argmax(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                              float* max_val, int32_t* max_idx, int M, int N, int K,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q4_argmax(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                              float* max_val, int32_t* max_idx, int M, int N, int K,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q5_argmax(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                              float* max_val, int32_t* max_idx, int M, int N, int K,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q6_argmax(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                              float* max_val, int32_t* max_idx, int M, int N, int K,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q7_argmax(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                              float* max_val, int32_t* max_idx, int M, int N, int K,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q8_argmax(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                              float* max_val, int32_t* max_idx, int M, int N, int K,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Unpack codes: codes[n][k] = q[n,k] as uint8, through the same device code

@@ -35,8 +35,9 @@ def lib():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     expected = {"aqg_abi_version", "aqg_status_string", "aqg_workspace_bytes", "aqg_gemv_bf16",
-                "aqg_swiglu_bf16", "aqg_unpack_codes", "aqg_dispatch_path",
-                "aqg_path_name"} | {"aqg_gemv_affine_q%d" % b for b in range(2, 9)}
+                "aqg_swiglu_bf16", "aqg_unpack_codes", "aqg_dispatch_path", "aqg_path_name",
+                "aqg_gemv_bf16_argmax"} | {"aqg_gemv_affine_q%d" % b for b in range(2, 9)} | \
+               {"aqg_gemv_affine_q%d_argmax" % b for b in range(2, 9)}
     assert set(names) == expected
 
 
@@ -54,6 +55,7 @@ def test_version_and_status_strings(lib):
              "AQG_ERR_LAUNCH", "AQG_ERR_DEVICE"][s])
     assert aqg.status_string(99) == "unknown aqg status"
     assert aqg.workspace_bytes(4, 1, 100, 1024) == 0
+    assert aqg.workspace_bytes(aqg.AQG_KIND_SWIGLU, 4, 4096, 1536) == 0
 
 
 def dense(lib, x=A16, W=B16, y=C16, M=1, N=16, K=64, out=0, ws=None, wsb=0):
@@ -156,3 +158,57 @@ def test_dispatch_query_refuses_what_the_calls_refuse(lib):
     assert lib.aqg_path_name(99) == b"unknown"
     p = lib.aqg_dispatch_path(0, 1, 1536, 1536, ctypes.byref(cols))
     assert p >= 0 and cols.value == 1 and lib.aqg_path_name(p) == b"piece"
+
+
+F16 = 0x60000
+G16 = 0x70000
+WS = 0x1000000
+
+
+def argmax_dense(lib, x=A16, W=B16, val=F16, idx=G16, M=1, N=16, K=64, ws=WS, wsb=None):
+    if wsb is None:
+        wsb = aqg.workspace_bytes(aqg.AQG_KIND_ARGMAX_DENSE, M, N, K) if 0 < M <= 32 and N > 0 and K > 0 else 0
+    return lib.aqg_gemv_bf16_argmax(x, W, val, idx, M, N, K, ws, wsb, None)
+
+
+def test_argmax_workspace_sizes_follow_the_kernel(lib):
+    """Fused epilogue (large N): partials only; otherwise fp32 y plus the
+    chunk partials.  Every size is nonzero (a workspace is always needed)."""
+    K = aqg.AQG_KIND_ARGMAX_DENSE
+    big = aqg.workspace_bytes(K, 16, 100000, 1536)
+    small = aqg.workspace_bytes(K, 16, 1536, 1536)
+    assert big == 32 * 32 * 256 * 8                      # 32 rows x 32 producers per CU x 256 CUs
+    assert small >= 16 * 1536 * 4
+    assert aqg.workspace_bytes(K + 4, 4, 151936, 1024) == big
+    assert aqg.workspace_bytes(K + 3, 4, 50000, 1024) >= 4 * 50000 * 4
+    assert aqg.workspace_bytes(K, 33, 100, 1024) == 0
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(val=None), aqg.AQG_ERR_INVALID_ARG),
+    (dict(idx=None), aqg.AQG_ERR_INVALID_ARG),
+    (dict(ws=None), aqg.AQG_ERR_INVALID_ARG),
+    (dict(wsb=16), aqg.AQG_ERR_INVALID_ARG),             # shorter than the workspace the shape needs
+    (dict(M=33), aqg.AQG_ERR_UNSUPPORTED),
+    (dict(K=12), aqg.AQG_ERR_UNSUPPORTED),
+    (dict(val=F16 + 2), aqg.AQG_ERR_ALIGNMENT),
+    (dict(ws=WS + 8), aqg.AQG_ERR_ALIGNMENT),
+    (dict(idx=F16), aqg.AQG_ERR_INVALID_ARG),            # outputs overlap
+    (dict(val=A16), aqg.AQG_ERR_INVALID_ARG),            # output overlaps x
+    (dict(ws=B16), aqg.AQG_ERR_INVALID_ARG),             # workspace overlaps W
+])
+def test_argmax_validation(lib, kwargs, status):
+    assert argmax_dense(lib, **kwargs) == status
+    f = lib.aqg_gemv_affine_q4_argmax
+    if "W" not in kwargs:
+        kw = dict(kwargs)
+        M = kw.get("M", 1)
+        wsb = kw.get("wsb", aqg.workspace_bytes(aqg.AQG_KIND_ARGMAX_DENSE + 4, M, 16, kw.get("K", 64))
+                     if M <= 32 else 0)
+        assert f(kw.get("x", A16), B16, D16, E16, kw.get("val", F16), kw.get("idx", G16), M, 16, kw.get("K", 64),
+                 kw.get("ws", WS), wsb, None) == status
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="only meaningful where no GPU can be reached")
+def test_valid_argmax_without_gpu_reports_device_error(lib):
+    assert argmax_dense(lib) == aqg.AQG_ERR_DEVICE
