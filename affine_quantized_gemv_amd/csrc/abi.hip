@@ -12,6 +12,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "aqgemv.h"
 #include "host_query.h"
@@ -234,6 +235,39 @@ int run_argmax(int bits, const void* x, const void* w0, const void* scales, cons
     return finish(e);
 }
 
+// ------------------------------------------- argmax without allocation
+
+// Scratch of the allocation-free row argmax: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes its
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// first call on a device looks up that device's address with
+// hipGetSymbolAddress and every later call on it uses that pointer.
+constexpr size_t kScratchBytes = AQG_ARGMAX_NOALLOC_MAX_BYTES;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];      // per device: the array's device address (null until looked up)
+
+int scratch_for_current_device(void** p)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return AQG_ERR_DEVICE;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return AQG_ERR_DEVICE;
+        }
+        g_scratch[dev] = ptr;
+    }
+    *p = g_scratch[dev];
+    return AQG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,6 +296,22 @@ size_t aqg_workspace_bytes(int kind, int M, int N, int K)
     if (kind == AQG_KIND_ARGMAX_DENSE || (kind >= AQG_KIND_ARGMAX_DENSE + 2 && kind <= AQG_KIND_ARGMAX_DENSE + 8))
         return argmax_plan(kind - AQG_KIND_ARGMAX_DENSE, M, N, K).bytes;
     return 0;  // the GEMVs and SwiGLUs keep their partial sums in registers and LDS
+}
+
+int aqg_gemv_argmax_noalloc(int bits, const void* x, const void* W, const void* scales, const void* biases,
+                            float* max_val, int32_t* max_idx, int M, int N, int K, void* stream)
+{
+    if (!(bits == 0 || (bits >= 2 && bits <= 8))) return AQG_ERR_UNSUPPORTED;
+    if (M <= 0 || N <= 0 || K <= 0) return AQG_ERR_INVALID_ARG;
+    if (M > 32) return AQG_ERR_UNSUPPORTED;
+    if (bits == 0 ? (K % 8 != 0) : (K % 64 != 0)) return AQG_ERR_UNSUPPORTED;
+    if (argmax_plan(bits, M, N, K).bytes > kScratchBytes) return AQG_ERR_UNSUPPORTED;
+    int st = check_device();
+    if (st != AQG_OK) return st;
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != AQG_OK) return st;
+    return run_argmax(bits, x, W, scales, biases, max_val, max_idx, M, N, K, ws, kScratchBytes, stream);
 }
 
 int aqg_gemv_bf16_argmax(const void* x, const void* W, float* max_val, int32_t* max_idx, int M, int N, int K,

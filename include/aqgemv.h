@@ -189,6 +189,27 @@ int aqg_gemv_affine_q8_argmax(const void* x, const uint32_t* Wq, const void* sca
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Row argmax that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same result as aqg_gemv_bf16_argmax
+ * (bits = 0) or aqg_gemv_affine_q{bits}_argmax (bits = 2..8) with the same
+ * arguments; W is the dense weight or the affine Wq, and scales and biases
+ * are ignored for bits = 0.  Instead of a caller's workspace it uses a
+ * static device array of AQG_ARGMAX_NOALLOC_MAX_BYTES (8 MiB) that
+ * each GPU the library runs on holds until the process ends; it is looked up
+ * on the first call on each device.  A shape needing more workspace than
+ * that (aqg_workspace_bytes of the matching argmax kind) is
+ * AQG_ERR_UNSUPPORTED; nothing is enqueued then.  The array is shared by
+ * every call on a GPU: calls that may overlap on one GPU (several streams,
+ * several threads) race on it and must be serialized by the caller.  Its
+ * contents need no initialisation (every partial is written before it is
+ * read).  No hipMalloc, hipFree or other allocating call is made.
+ */
+#define AQG_ARGMAX_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+int aqg_gemv_argmax_noalloc(int bits, const void* x, const void* W, const void* scales, const void* biases,
+                            float* max_val, int32_t* max_idx, int M, int N, int K, void* stream);
+
+/*
  * Unpack codes: codes[n][k] = q[n,k] as uint8, through the same device code
  * path the affine GEMVs use to read their weights.  Wq: uint32[N][K*b/32];
  * codes: uint8[N][K] (16-byte aligned, not overlapping Wq).  K % 64 == 0,

@@ -36,7 +36,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     expected = {"aqg_abi_version", "aqg_status_string", "aqg_workspace_bytes", "aqg_gemv_bf16",
                 "aqg_swiglu_bf16", "aqg_unpack_codes", "aqg_dispatch_path", "aqg_path_name",
-                "aqg_gemv_bf16_argmax"} | {"aqg_gemv_affine_q%d" % b for b in range(2, 9)} | \
+                "aqg_gemv_bf16_argmax", "aqg_gemv_argmax_noalloc"} | \
+               {"aqg_gemv_affine_q%d" % b for b in range(2, 9)} | \
                {"aqg_gemv_affine_q%d_argmax" % b for b in range(2, 9)}
     assert set(names) == expected
 
