@@ -22,7 +22,8 @@ import torch
 
 __all__ = [
     "lib_path", "load", "AqgError", "abi_version", "status_string", "workspace_bytes", "dispatch_path",
-    "gemv_bf16", "gemv_affine", "swiglu_bf16", "unpack_codes", "gemv_bf16_argmax", "gemv_affine_argmax",
+    "gemv_bf16", "gemv_affine", "swiglu_bf16", "swiglu_affine", "unpack_codes", "gemv_bf16_argmax",
+    "gemv_affine_argmax",
     "gemv_affine_q2", "gemv_affine_q3", "gemv_affine_q4", "gemv_affine_q5",
     "gemv_affine_q6", "gemv_affine_q7", "gemv_affine_q8",
     "AQG_OK", "AQG_ERR_INVALID_ARG", "AQG_ERR_UNSUPPORTED", "AQG_ERR_ALIGNMENT",
@@ -31,7 +32,7 @@ __all__ = [
 
 AQG_OK, AQG_ERR_INVALID_ARG, AQG_ERR_UNSUPPORTED, AQG_ERR_ALIGNMENT, AQG_ERR_LAUNCH, AQG_ERR_DEVICE = range(6)
 AQG_OUT_BF16, AQG_OUT_F32 = 0, 1
-AQG_KIND_DENSE, AQG_KIND_SWIGLU, AQG_KIND_ARGMAX_DENSE = 0, 9, 32
+AQG_KIND_DENSE, AQG_KIND_SWIGLU, AQG_KIND_SWIGLU_AFFINE, AQG_KIND_ARGMAX_DENSE = 0, 9, 16, 32
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -75,6 +76,10 @@ def load():
         lib.aqg_swiglu_bf16.argtypes = [P, P, P, P, I, I, I, I, P, Z, P]
         lib.aqg_unpack_codes.restype = I
         lib.aqg_unpack_codes.argtypes = [I, P, P, I, I, P]
+        for b in range(2, 9):
+            f = getattr(lib, "aqg_swiglu_affine_q%d" % b)
+            f.restype = I
+            f.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P, Z, P]
         lib.aqg_gemv_bf16_argmax.restype = I
         lib.aqg_gemv_bf16_argmax.argtypes = [P, P, P, P, I, I, I, P, Z, P]
         for b in range(2, 9):
@@ -229,6 +234,39 @@ def swiglu_bf16(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, out_dtype=t
     ws, wsb = _ws(workspace)
     _check(load().aqg_swiglu_bf16(_p(x), _p(Wg), _p(Wu), _p(y), M, N, K, _odt(y), ws, wsb, _stream(x)),
            "aqg_swiglu_bf16")
+    return y
+
+
+def _affine_check(Wq, scales, biases, bits: int, N: int, K: int, name: str):
+    _dev(Wq, name + " Wq", (torch.int32, torch.uint32))
+    _dev(scales, name + " scales", (torch.bfloat16,))
+    _dev(biases, name + " biases", (torch.bfloat16,))
+    if tuple(Wq.shape) != (N, K * bits // 32):
+        raise ValueError("%s Wq must be [%d, %d]" % (name, N, K * bits // 32))
+    if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
+        raise ValueError("%s scales and biases must be [%d, %d]" % (name, N, K // 64))
+
+
+def swiglu_affine(x: torch.Tensor, gate, up, bits: int, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """out[M,N] = silu(x.Wg^T) * (x.Wu^T) with affine b-bit Wg and Wu, fp32 inside.
+
+    gate, up: (Wq int32/uint32 [N, K*bits/32], scales bf16 [N, K/64],
+    biases bf16 [N, K/64]) each.
+    """
+    if bits not in range(2, 9):
+        raise ValueError("bits must be in 2..8")
+    _dev(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    if K % 64:
+        raise ValueError("K must be a multiple of 64")
+    N = gate[0].shape[0]
+    _affine_check(*gate, bits, N, K, "gate")
+    _affine_check(*up, bits, N, K, "up")
+    y = _out(out, M, N, out_dtype, x)
+    ws, wsb = _ws(workspace)
+    fn = getattr(load(), "aqg_swiglu_affine_q%d" % bits)
+    _check(fn(_p(x), _p(gate[0]), _p(gate[1]), _p(gate[2]), _p(up[0]), _p(up[1]), _p(up[2]), _p(y),
+              M, N, K, _odt(y), ws, wsb, _stream(x)), "aqg_swiglu_affine_q%d" % bits)
     return y
 
 

@@ -79,17 +79,20 @@ int finish(hipError_t e)
 }
 
 int run_projection(int bits, bool swiglu, const void* x, const void* w0, const void* w1,
-                   const void* scales, const void* biases, void* y, int M, int N, int K,
-                   int out_dtype, void* workspace, size_t workspace_bytes, void* stream)
+                   const void* scales, const void* biases, const void* scales1, const void* biases1, void* y,
+                   int M, int N, int K, int out_dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
     int st = check_common(x, y, M, N, K, out_dtype);
     if (st != AQG_OK) return st;
-    if (!w0 || (swiglu && !w1) || (bits && (!scales || !biases))) return AQG_ERR_INVALID_ARG;
+    const bool two = swiglu && bits;     // affine SwiGLU: the up matrix has its own scales and biases
+    if (!w0 || (swiglu && !w1) || (bits && (!scales || !biases)) || (two && (!scales1 || !biases1)))
+        return AQG_ERR_INVALID_ARG;
     if (bits == 0 ? (K % 8 != 0) : (K % 64 != 0)) return AQG_ERR_UNSUPPORTED;
     if (!aligned(w0, 16) || (w1 && !aligned(w1, 16))) return AQG_ERR_ALIGNMENT;
     // the matrix-core kernels read scales and biases in 4- to 16-byte pieces
     if (bits && (!aligned(scales, 4) || !aligned(biases, 4))) return AQG_ERR_ALIGNMENT;
-    const int kind = swiglu ? AQG_KIND_SWIGLU : bits;
+    if (two && (!aligned(scales1, 4) || !aligned(biases1, 4))) return AQG_ERR_ALIGNMENT;
+    const int kind = swiglu ? (bits ? AQG_KIND_SWIGLU_AFFINE + bits : AQG_KIND_SWIGLU) : bits;
     if (workspace_bytes < aqg_workspace_bytes(kind, M, N, K)) return AQG_ERR_INVALID_ARG;
     (void)workspace;
 
@@ -99,7 +102,8 @@ int run_projection(int bits, bool swiglu, const void* x, const void* w0, const v
     const size_t gbytes = (size_t)N * (K / 64) * 2;
     if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, w0, wbytes) ||
         (swiglu && overlap(y, ybytes, w1, wbytes)) ||
-        (bits && (overlap(y, ybytes, scales, gbytes) || overlap(y, ybytes, biases, gbytes))))
+        (bits && (overlap(y, ybytes, scales, gbytes) || overlap(y, ybytes, biases, gbytes))) ||
+        (two && (overlap(y, ybytes, scales1, gbytes) || overlap(y, ybytes, biases1, gbytes))))
         return AQG_ERR_INVALID_ARG;
 
     st = check_device();
@@ -112,6 +116,8 @@ int run_projection(int bits, bool swiglu, const void* x, const void* w0, const v
     a.w1 = w1;
     a.scales = static_cast<const uint16_t*>(scales);
     a.biases = static_cast<const uint16_t*>(biases);
+    a.scales1 = static_cast<const uint16_t*>(scales1);
+    a.biases1 = static_cast<const uint16_t*>(biases1);
     a.y = y;
     a.M = M;
     a.N = N;
@@ -127,8 +133,8 @@ int run_projection(int bits, bool swiglu, const void* x, const void* w0, const v
 int run_affine(int bits, const void* x, const uint32_t* Wq, const void* scales, const void* biases,
                void* y, int M, int N, int K, int out_dtype, void* ws, size_t wsb, void* stream)
 {
-    return run_projection(bits, false, x, Wq, nullptr, scales, biases, y, M, N, K, out_dtype, ws, wsb,
-                          stream);
+    return run_projection(bits, false, x, Wq, nullptr, scales, biases, nullptr, nullptr, y, M, N, K, out_dtype,
+                          ws, wsb, stream);
 }
 
 // ---------------------------------------------------------- row argmax
@@ -340,16 +346,34 @@ AQG_AFFINE_ARGMAX_ENTRY(8)
 int aqg_gemv_bf16(const void* x, const void* W, void* y, int M, int N, int K, int out_dtype,
                   void* workspace, size_t workspace_bytes, void* stream)
 {
-    return run_projection(0, false, x, W, nullptr, nullptr, nullptr, y, M, N, K, out_dtype, workspace,
-                          workspace_bytes, stream);
+    return run_projection(0, false, x, W, nullptr, nullptr, nullptr, nullptr, nullptr, y, M, N, K, out_dtype,
+                          workspace, workspace_bytes, stream);
 }
 
 int aqg_swiglu_bf16(const void* x, const void* Wg, const void* Wu, void* out, int M, int N, int K,
                     int out_dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
-    return run_projection(0, true, x, Wg, Wu, nullptr, nullptr, out, M, N, K, out_dtype, workspace,
-                          workspace_bytes, stream);
+    return run_projection(0, true, x, Wg, Wu, nullptr, nullptr, nullptr, nullptr, out, M, N, K, out_dtype,
+                          workspace, workspace_bytes, stream);
 }
+
+#define AQG_SWIGLU_AFFINE_ENTRY(B)                                                                          \
+    int aqg_swiglu_affine_q##B(const void* x, const uint32_t* Wgq, const void* gate_scales,                 \
+                               const void* gate_biases, const uint32_t* Wuq, const void* up_scales,        \
+                               const void* up_biases, void* out, int M, int N, int K, int out_dtype,       \
+                               void* workspace, size_t workspace_bytes, void* stream)                      \
+    {                                                                                                       \
+        return run_projection(B, true, x, Wgq, Wuq, gate_scales, gate_biases, up_scales, up_biases, out, M, \
+                              N, K, out_dtype, workspace, workspace_bytes, stream);                         \
+    }
+AQG_SWIGLU_AFFINE_ENTRY(2)
+AQG_SWIGLU_AFFINE_ENTRY(3)
+AQG_SWIGLU_AFFINE_ENTRY(4)
+AQG_SWIGLU_AFFINE_ENTRY(5)
+AQG_SWIGLU_AFFINE_ENTRY(6)
+AQG_SWIGLU_AFFINE_ENTRY(7)
+AQG_SWIGLU_AFFINE_ENTRY(8)
+#undef AQG_SWIGLU_AFFINE_ENTRY
 
 #define AQG_AFFINE_ENTRY(B)                                                                          \
     int aqg_gemv_affine_q##B(const void* x, const uint32_t* Wq, const void* scales, const void* biases, \
@@ -371,8 +395,9 @@ AQG_AFFINE_ENTRY(8)
 int aqg_dispatch_path(int kind, int M, int N, int K, int* columns)
 {
     if (M <= 0 || N <= 0 || K <= 0) return -AQG_ERR_INVALID_ARG;
-    const bool swiglu = kind == AQG_KIND_SWIGLU;
-    const int bits = swiglu ? 0 : kind;
+    const bool swiglu_affine = kind >= AQG_KIND_SWIGLU_AFFINE + 2 && kind <= AQG_KIND_SWIGLU_AFFINE + 8;
+    const bool swiglu = kind == AQG_KIND_SWIGLU || swiglu_affine;
+    const int bits = swiglu_affine ? kind - AQG_KIND_SWIGLU_AFFINE : (swiglu ? 0 : kind);
     if (!(kind == AQG_KIND_DENSE || swiglu || (kind >= 2 && kind <= 8))) return -AQG_ERR_INVALID_ARG;
     if (M > 32) return -AQG_ERR_UNSUPPORTED;
     if (bits == 0 ? (K % 8 != 0) : (K % 64 != 0)) return -AQG_ERR_UNSUPPORTED;

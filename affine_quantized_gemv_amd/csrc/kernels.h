@@ -13,8 +13,10 @@ struct ProjArgs {
     const uint16_t* x;       // bf16 [M][K]
     const void* w0;          // dense W, affine Wq words, or SwiGLU Wg
     const void* w1;          // SwiGLU Wu (else null)
-    const uint16_t* scales;  // affine: bf16 [N][K/64]
-    const uint16_t* biases;  // affine: bf16 [N][K/64]
+    const uint16_t* scales;  // affine: bf16 [N][K/64] (SwiGLU: of Wg)
+    const uint16_t* biases;  // affine: bf16 [N][K/64] (SwiGLU: of Wg)
+    const uint16_t* scales1; // affine SwiGLU: scales of Wu (else null)
+    const uint16_t* biases1; // affine SwiGLU: biases of Wu (else null)
     void* y;                 // bf16 or f32 [M][N]
     int M, N, K;
     int KT;                  // K elements staged in LDS per tile

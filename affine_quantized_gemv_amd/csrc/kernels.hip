@@ -254,7 +254,7 @@ bool choose_stream(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
     const int G = 64 >> L;
     const int64_t T = ((int64_t)N + G - 1) / G;
     if (T < 2048) return false;
-    c.xreg = (bits != 0 && !swiglu && U <= 64 && (c.MT == 1 || (c.MT == 2 && bits != 8))) ? 1 : 0;
+    c.xreg = (bits != 0 && U <= 64 && (c.MT == 1 || (c.MT == 2 && bits != 8 && !swiglu))) ? 1 : 0;
     const size_t per_unit = bits ? (bits == 8 ? 16 * 16 : 16 * 8) + 8 : 16;
     c.lds = c.xreg ? 0 : (size_t)c.MT * U * per_unit;
     // output staging, bounded with the fewest wavefronts the launch can get
@@ -288,7 +288,6 @@ bool choose_piece(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
 {
     c = LaunchCfg{};
     if (!(bits == 0 || bits == 2 || bits == 4 || bits == 8)) return false;
-    if (swiglu && bits != 0) return false;
     c.path = PATH_PIECE;
     c.MT = 1;
     while (c.MT < M) c.MT <<= 1;
@@ -342,6 +341,13 @@ bool choose_piece(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
 LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 {
     LaunchCfg c;
+    if (swiglu && bits != 0) {
+        // fused SwiGLU over affine gate and up matrices: the dot-product
+        // kernels with both weight streams through the same x operands
+        if (choose_piece(bits, true, M, N, K, c)) return c;
+        if (choose_stream(bits, true, M, N, K, c)) return c;
+        return choose_valu(bits, true, M, N, K);
+    }
     // Large-N dense from M = 3 on: the tile kernel streams the 100000 x 1536
     // LM head at ~48-49 us for any M <= 16 (against ~50 us for the
     // dot-product kernel at M = 3, 4 and ~64 us at M = 5..8, which pads M to
@@ -436,7 +442,15 @@ hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg
         return swiglu ? launch_mfma<true>(a, c, s) : launch_mfma<false>(a, c, s);
     }
     if (c.path == PATH_PIECE) {
-        if (swiglu) return bits == 0 ? launch_piece<0, true>(a, c, s) : hipErrorInvalidValue;
+        if (swiglu) {
+            switch (bits) {
+                case 0: return launch_piece<0, true>(a, c, s);
+                case 2: return launch_piece<2, true>(a, c, s);
+                case 4: return launch_piece<4, true>(a, c, s);
+                case 8: return launch_piece<8, true>(a, c, s);
+                default: return hipErrorInvalidValue;
+            }
+        }
         switch (bits) {
             case 0: return launch_piece<0, false>(a, c, s);
             case 2: return launch_piece<2, false>(a, c, s);
@@ -446,7 +460,19 @@ hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg
         }
     }
     if (c.path == PATH_STREAM) {
-        if (swiglu) return bits == 0 ? launch_stream<0, true>(a, c, s) : hipErrorInvalidValue;
+        if (swiglu) {
+            switch (bits) {
+                case 0: return launch_stream<0, true>(a, c, s);
+                case 2: return launch_stream<2, true>(a, c, s);
+                case 3: return launch_stream<3, true>(a, c, s);
+                case 4: return launch_stream<4, true>(a, c, s);
+                case 5: return launch_stream<5, true>(a, c, s);
+                case 6: return launch_stream<6, true>(a, c, s);
+                case 7: return launch_stream<7, true>(a, c, s);
+                case 8: return launch_stream<8, true>(a, c, s);
+                default: return hipErrorInvalidValue;
+            }
+        }
         switch (bits) {
             case 0: return launch_stream<0, false>(a, c, s);
             case 2: return launch_stream<2, false>(a, c, s);
@@ -460,8 +486,17 @@ hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg
         }
     }
     if (swiglu) {
-        if (bits != 0) return hipErrorInvalidValue;
-        return launch_bits<0, true>(a, c, s);
+        switch (bits) {
+            case 0: return launch_bits<0, true>(a, c, s);
+            case 2: return launch_bits<2, true>(a, c, s);
+            case 3: return launch_bits<3, true>(a, c, s);
+            case 4: return launch_bits<4, true>(a, c, s);
+            case 5: return launch_bits<5, true>(a, c, s);
+            case 6: return launch_bits<6, true>(a, c, s);
+            case 7: return launch_bits<7, true>(a, c, s);
+            case 8: return launch_bits<8, true>(a, c, s);
+            default: return hipErrorInvalidValue;
+        }
     }
     switch (bits) {
         case 0: return launch_bits<0, false>(a, c, s);

@@ -141,7 +141,6 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
     constexpr int G = 64 >> L;                    // rows per tile
     constexpr int PRP = J * P;                    // piece slots per row (>= pieces per row)
     constexpr int PER_TILE = G * MT;              // staged outputs per tile
-    static_assert(!SWIGLU || BITS == 0, "the fused SwiGLU takes dense weights");
     static_assert(L >= 2 && L <= 6, "segment of 4..64 lanes");
 
     const int lane = threadIdx.x & 63;
@@ -289,19 +288,20 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 
     // ---- ring of D = RD*J slots; slot d holds piece j = d % J of a row tile
     uint32_t wb[D][S][4];
-    [[maybe_unused]] uint32_t sw[RD], bw[RD];   // per ring row: the scale / bias of group `lane`
+    [[maybe_unused]] uint32_t sw[S][RD], bw[S][RD];   // per stream and ring row: the scale / bias of group `lane`
     int64_t f_tile = wg * CT;   // tile being fetched (wave-uniform)
     int f_c = 0;                // its index within the super-tile
-    __amdgpu_buffer_rsrc_t rw[S], rs, rb;
+    __amdgpu_buffer_rsrc_t rw[S], rs[S], rb[S];
     auto set_tile = [&]() __attribute__((always_inline)) {
         const int64_t n0 = f_tile * G;
         const int64_t rows = a.N - n0;
 #pragma unroll
-        for (int s = 0; s < S; ++s)
+        for (int s = 0; s < S; ++s) {
             rw[s] = tile_rsrc(static_cast<const char*>(s == 0 ? a.w0 : a.w1) + n0 * row_bytes, rows * row_bytes);
-        if constexpr (BITS != 0) {
-            rs = tile_rsrc(a.scales + n0 * gpr, rows * gpr * 2);
-            rb = tile_rsrc(a.biases + n0 * gpr, rows * gpr * 2);
+            if constexpr (BITS != 0) {
+                rs[s] = tile_rsrc((s == 0 ? a.scales : a.scales1) + n0 * gpr, rows * gpr * 2);
+                rb[s] = tile_rsrc((s == 0 ? a.biases : a.biases1) + n0 * gpr, rows * gpr * 2);
+            }
         }
     };
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -314,8 +314,11 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
             // covers them; consume(d) of the row's first piece has already
             // taken the previous values out (fetch(d) follows consume(d))
             if constexpr (BITS != 0) {
-                sw[d / J] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)lane * 2, 0, kLoadNT);
-                bw[d / J] = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)lane * 2, 0, kLoadNT);
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    sw[s][d / J] = __builtin_amdgcn_raw_buffer_load_b16(rs[s], (uint32_t)lane * 2, 0, kLoadNT);
+                    bw[s][d / J] = __builtin_amdgcn_raw_buffer_load_b16(rb[s], (uint32_t)lane * 2, 0, kLoadNT);
+                }
             }
         }
 #pragma unroll
@@ -335,7 +338,7 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[s][m] = 0.0f;
     int ti = 0;                 // tiles finished by this wavefront
-    [[maybe_unused]] float rsc[J], rbi[J];   // scale and bias of each piece of the row in use
+    [[maybe_unused]] float rsc[S][J], rbi[S][J];   // scale and bias of each piece of the row in use, per stream
 
     auto consume = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
@@ -363,15 +366,23 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
         } else {
             using Plan = PiecePlan<BITS>;
             // pairs 4c+0, 4c+2 into one accumulator, 4c+1, 4c+3 into the other
-            float dd[MT], de[MT];
+            // (per weight stream: the fused SwiGLU runs its gate and up rows
+            // through the same x operands)
+            float dd[S][MT], de[S][MT];
 #pragma unroll
-            for (int m = 0; m < MT; ++m) dd[m] = de[m] = 0.0f;
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) dd[s][m] = de[s][m] = 0.0f;
             static_for<0, NCHP>([&](auto C) __attribute__((always_inline)) {
                 constexpr int c = decltype(C)::value;
-                const uint32_t q0 = Plan::template pair<4 * c + 0>(wb[d][0]);
-                const uint32_t q1 = Plan::template pair<4 * c + 1>(wb[d][0]);
-                const uint32_t q2 = Plan::template pair<4 * c + 2>(wb[d][0]);
-                const uint32_t q3 = Plan::template pair<4 * c + 3>(wb[d][0]);
+                uint32_t q[S][4];
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    q[s][0] = Plan::template pair<4 * c + 0>(wb[d][s]);
+                    q[s][1] = Plan::template pair<4 * c + 1>(wb[d][s]);
+                    q[s][2] = Plan::template pair<4 * c + 2>(wb[d][s]);
+                    q[s][3] = Plan::template pair<4 * c + 3>(wb[d][s]);
+                }
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     uint32_t x0, x1, x2, x3;
@@ -382,28 +393,33 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                         const uint4 v = xp[(m * NCHP + c) * PRP + p];
                         x0 = v.x; x1 = v.y; x2 = v.z; x3 = v.w;
                     }
-                    float v0 = dd[m], v1 = de[m];
-                    v0 = dot2(q0, x0, v0);
-                    v1 = dot2(q1, x1, v1);
-                    v0 = dot2(q2, x2, v0);
-                    v1 = dot2(q3, x3, v1);
-                    dd[m] = v0;
-                    de[m] = v1;
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        float v0 = dd[s][m], v1 = de[s][m];
+                        v0 = dot2(q[s][0], x0, v0);
+                        v1 = dot2(q[s][1], x1, v1);
+                        v0 = dot2(q[s][2], x2, v0);
+                        v1 = dot2(q[s][3], x3, v1);
+                        dd[s][m] = v0;
+                        de[s][m] = v1;
+                    }
                 }
 #pragma unroll
-                for (int m = 0; m < MT; ++m) { pin(dd[m]); pin(de[m]); }
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) { pin(dd[s][m]); pin(de[s][m]); }
                 code_fence();
             });
             if constexpr (j == 0) {
                 // the row's first piece takes every piece's scale and bias
 #pragma unroll
-                for (int jj = 0; jj < J; ++jj) {
-                    rsc[jj] = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(gsrc[jj], (int)sw[d / J]) << 16);
-                    rbi[jj] = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(gsrc[jj], (int)bw[d / J]) << 16);
-                }
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int jj = 0; jj < J; ++jj) {
+                        rsc[s][jj] = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(gsrc[jj], (int)sw[s][d / J]) << 16);
+                        rbi[s][jj] = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(gsrc[jj], (int)bw[s][d / J]) << 16);
+                    }
             }
-            const float sc = rsc[j];
-            const float bi = rbi[j];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 float X, Tc;
@@ -415,7 +431,9 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
                     X = v.x;
                     Tc = v.y;
                 }
-                acc[0][m] = fmaf(sc, (dd[m] + de[m]) - Tc, fmaf(bi, X, acc[0][m]));
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    acc[s][m] = fmaf(rsc[s][j], (dd[s][m] + de[s][m]) - Tc, fmaf(rbi[s][j], X, acc[s][m]));
             }
         }
         if constexpr (j == J - 1) {

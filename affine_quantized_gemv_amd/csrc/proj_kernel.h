@@ -225,14 +225,15 @@ __device__ __forceinline__ float segment_sum64_ct(float v)
 
 // ------------------------------------------------------- per-unit arithmetic
 
-// One unit of R rows (S weight streams) against x from LDS:
+// One unit of R rows (S weight streams, each with its own scales and
+// biases) against x from LDS:
 //   dense:  acc[s][r][m] += sum of 8 products (4 dot2)
 //   affine: d = sum over the group's pairs of dot2(operand, x' pair);
 //           acc += scale*(d - T) + bias*X.
 // xp/xc: the tile's staged x (ut units per m row); u: unit within the tile.
 template <int BITS, int MT, int S, int R>
-__device__ __forceinline__ void unit_mac(const uint32_t (&w)[S][R][Geo<BITS>::NW], const float (&sc)[R],
-                                         const float (&bi)[R], const uint4* xp, const float2* xc, int ut,
+__device__ __forceinline__ void unit_mac(const uint32_t (&w)[S][R][Geo<BITS>::NW], const float (&sc)[S][R],
+                                         const float (&bi)[S][R], const uint4* xp, const float2* xc, int ut,
                                          int u, float (&acc)[S][R][MT])
 {
     if constexpr (BITS == 0) {
@@ -307,7 +308,7 @@ __device__ __forceinline__ void unit_mac(const uint32_t (&w)[S][R][Geo<BITS>::NW
             for (int s = 0; s < S; ++s)
 #pragma unroll
                 for (int r = 0; r < R; ++r)
-                    acc[s][r][m] = fmaf(sc[r], (dd[s][r][m] + de[s][r][m]) - xcv.y, fmaf(bi[r], xcv.x, acc[s][r][m]));
+                    acc[s][r][m] = fmaf(sc[s][r], (dd[s][r][m] + de[s][r][m]) - xcv.y, fmaf(bi[s][r], xcv.x, acc[s][r][m]));
         }
     }
 }
@@ -336,8 +337,8 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
     const int64_t row0 = ((int64_t)blockIdx.x * nwaves + wave) * (int64_t)(G * R) + slot;
     int64_t nrow[R];
     const uint32_t* wrow[S][R];
-    const uint16_t* srow[R];
-    const uint16_t* brow[R];
+    const uint16_t* srow[S][R];
+    const uint16_t* brow[S][R];
     const int64_t row_words = (BITS == 0) ? (int64_t)a.K / 2 : (int64_t)a.K * BITS / 32;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -346,8 +347,11 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
         wrow[0][r] = reinterpret_cast<const uint32_t*>(a.w0) + n * row_words;
         if constexpr (SWIGLU) wrow[1][r] = reinterpret_cast<const uint32_t*>(a.w1) + n * row_words;
         if constexpr (BITS != 0) {
-            srow[r] = a.scales + n * (a.K / 64);
-            brow[r] = a.biases + n * (a.K / 64);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                srow[s][r] = (s == 0 ? a.scales : a.scales1) + n * (a.K / 64);
+                brow[s][r] = (s == 0 ? a.biases : a.biases1) + n * (a.K / 64);
+            }
         }
     }
 
@@ -361,7 +365,7 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
 
     // Ring of D units of weights (and their scale/bias) per lane.
     uint32_t wb[D][S][R][NW];
-    float sb[D][R], bb[D][R];
+    float sb[D][S][R], bb[D][S][R];
 
     for (int kt = 0; kt < a.K; kt += a.KT) {
         const int kw = min(a.KT, a.K - kt);
@@ -379,10 +383,12 @@ __global__ void __launch_bounds__(kMaxThreads) proj_kernel(ProjArgs a)
                     load_unit<BITS>(wrow[s][r] + (int64_t)(ubase + u) * NW, wb[d][s][r]);
             if constexpr (BITS != 0) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    sb[d][r] = bf16_to_f32(srow[r][ubase + u]);
-                    bb[d][r] = bf16_to_f32(brow[r][ubase + u]);
-                }
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        sb[d][s][r] = bf16_to_f32(srow[s][r][ubase + u]);
+                        bb[d][s][r] = bf16_to_f32(brow[s][r][ubase + u]);
+                    }
             }
         };
 

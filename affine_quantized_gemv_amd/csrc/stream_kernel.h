@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
     // never for the D-1 younger ones.  Finished outputs go to a lane-private
     // slice of LDS and are written out after the loop by the same lane.
     uint32_t wb[D][S][1][NW];
-    float sb[D][1], bb[D][1];
+    float sb[D][S][1], bb[D][S][1];
     int64_t f_tile = wg * CT;   // next item to fetch: tile, its index within
     int f_c = 0;                // the super-tile, and the unit slot
     int f_j = 0;
@@ -141,8 +141,11 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
             load_unit<BITS>(base + n * row_words + (int64_t)u * NW, wb[d][s][0]);
         }
         if constexpr (BITS != 0) {
-            sb[d][0] = bf16_to_f32(a.scales[n * gpr + u]);
-            bb[d][0] = bf16_to_f32(a.biases[n * gpr + u]);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                sb[d][s][0] = bf16_to_f32((s == 0 ? a.scales : a.scales1)[n * gpr + u]);
+                bb[d][s][0] = bf16_to_f32((s == 0 ? a.biases : a.biases1)[n * gpr + u]);
+            }
         }
         if (++f_j == upl) { f_j = 0; f_tile = next_tile(f_tile); }
     };
@@ -183,8 +186,11 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
 #pragma unroll
                         for (int i = 0; i < NW; ++i) wb[d][s][0][i] = live ? wb[d][s][0][i] : 0u;
                 } else {
-                    sb[d][0] = live ? sb[d][0] : 0.0f;
-                    bb[d][0] = live ? bb[d][0] : 0.0f;
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        sb[d][s][0] = live ? sb[d][s][0] : 0.0f;
+                        bb[d][s][0] = live ? bb[d][s][0] : 0.0f;
+                    }
                 }
                 {
                     if constexpr (XREG) {
@@ -225,8 +231,8 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
                         for (int m = 0; m < MT; ++m)
 #pragma unroll
                             for (int s = 0; s < S; ++s)
-                                acc[s][0][m] = fmaf(sb[d][0], (dd[s][m] + de[s][m]) - xT[m],
-                                                    fmaf(bb[d][0], xX[m], acc[s][0][m]));
+                                acc[s][0][m] = fmaf(sb[d][s][0], (dd[s][m] + de[s][m]) - xT[m],
+                                                    fmaf(bb[d][s][0], xX[m], acc[s][0][m]));
                     } else {
                         unit_mac<BITS, MT, S, 1>(wb[d], sb[d], bb[d], xp, xc, U, u, acc);
                     }
@@ -348,7 +354,7 @@ hipError_t launch_stream_one(const ProjArgs& a, const LaunchCfg& c, hipStream_t 
 template <int BITS, bool SW>
 hipError_t launch_stream_impl(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
-    if constexpr (BITS != 0 && !SW) {
+    if constexpr (BITS != 0) {
         if (c.xreg) {
             if (c.MT == 1) return launch_stream_one<BITS, 1, SW, true>(a, c, s);
             if constexpr (BITS != 8)

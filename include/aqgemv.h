@@ -4,7 +4,9 @@
  *
  *   y[M,N] = x[M,K] . W^T          W dense bf16            (aqg_gemv_bf16)
  *   y[M,N] = x[M,K] . W^T          W affine b-bit, b=2..8  (aqg_gemv_affine_q2 .. _q8)
- *   out[M,N] = silu(x.Wg^T) * (x.Wu^T)                     (aqg_swiglu_bf16)
+ *   out[M,N] = silu(x.Wg^T) * (x.Wu^T)   Wg, Wu dense      (aqg_swiglu_bf16)
+ *                                        Wg, Wu affine     (aqg_swiglu_affine_q2 .. _q8)
+ *   argmax over n of y[m,n], without writing y             (aqg_gemv_*_argmax)
  *
  * for M = 1..32 rows of activations (single-stream decode, or a window of up
  * to 32 rows).
@@ -79,6 +81,7 @@ typedef enum { AQG_OUT_BF16 = 0, AQG_OUT_F32 = 1 } aqg_out_dtype;
 /* Kinds for aqg_workspace_bytes(). */
 #define AQG_KIND_DENSE 0           /* 2..8 = affine GEMV of that width */
 #define AQG_KIND_SWIGLU 9
+#define AQG_KIND_SWIGLU_AFFINE 16  /* + b (2..8) = affine SwiGLU of width b */
 #define AQG_KIND_ARGMAX_DENSE 32   /* + b (2..8) = affine row argmax of width b */
 
 /* Returns AQG_ABI_VERSION. */
@@ -142,6 +145,41 @@ int aqg_gemv_affine_q8(const void* x, const uint32_t* Wq, const void* scales, co
  */
 int aqg_swiglu_bf16(const void* x, const void* Wg, const void* Wu, void* out, int M, int N, int K,
                     int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused up/gate SwiGLU over two affine b-bit matrices (one symbol per
+ * b = 2..8): g = x . Wg^T and u = x . Wu^T with w = scale * q + bias per
+ * group of 64 (each matrix with its own codes, scales and biases, in the
+ * affine layout above), both in fp32 from the same x; out = g/(1+exp(-g)) * u
+ * in fp32, stored per out_dtype.  Neither g nor u is rounded or written.
+ *   x: bf16[M][K]; Wgq, Wuq: uint32[N][K*b/32]; gate_scales, gate_biases,
+ *   up_scales, up_biases: bf16[N][K/64]; out: bf16 or f32 [M][N].
+ * AstrAI decode_linear_benchmark.md, commit message (the fused up/gate
+ * SwiGLU primitive against the unfused chain) on the affine format of
+ * TensorFold PR #849 (MLX checkpoints quantize the MLP modules at the width
+ * their quantization table names).
+ */
+int aqg_swiglu_affine_q2(const void* x, const uint32_t* Wgq, const void* gate_scales, const void* gate_biases,
+                         const uint32_t* Wuq, const void* up_scales, const void* up_biases, void* out, int M,
+                         int N, int K, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_swiglu_affine_q3(const void* x, const uint32_t* Wgq, const void* gate_scales, const void* gate_biases,
+                         const uint32_t* Wuq, const void* up_scales, const void* up_biases, void* out, int M,
+                         int N, int K, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_swiglu_affine_q4(const void* x, const uint32_t* Wgq, const void* gate_scales, const void* gate_biases,
+                         const uint32_t* Wuq, const void* up_scales, const void* up_biases, void* out, int M,
+                         int N, int K, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_swiglu_affine_q5(const void* x, const uint32_t* Wgq, const void* gate_scales, const void* gate_biases,
+                         const uint32_t* Wuq, const void* up_scales, const void* up_biases, void* out, int M,
+                         int N, int K, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_swiglu_affine_q6(const void* x, const uint32_t* Wgq, const void* gate_scales, const void* gate_biases,
+                         const uint32_t* Wuq, const void* up_scales, const void* up_biases, void* out, int M,
+                         int N, int K, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_swiglu_affine_q7(const void* x, const uint32_t* Wgq, const void* gate_scales, const void* gate_biases,
+                         const uint32_t* Wuq, const void* up_scales, const void* up_biases, void* out, int M,
+                         int N, int K, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_swiglu_affine_q8(const void* x, const uint32_t* Wgq, const void* gate_scales, const void* gate_biases,
+                         const uint32_t* Wuq, const void* up_scales, const void* up_biases, void* out, int M,
+                         int N, int K, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Row argmax of a projection (the LM head of greedy decoding), without
