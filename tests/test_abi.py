@@ -38,7 +38,8 @@ def test_header_declares_expected_entry_points():
                 "aqg_swiglu_bf16", "aqg_unpack_codes", "aqg_dispatch_path", "aqg_path_name",
                 "aqg_gemv_bf16_argmax", "aqg_gemv_argmax_noalloc"} | \
                {"aqg_gemv_affine_q%d" % b for b in range(2, 9)} | \
-               {"aqg_gemv_affine_q%d_argmax" % b for b in range(2, 9)}
+               {"aqg_gemv_affine_q%d_argmax" % b for b in range(2, 9)} | \
+               {"aqg_swiglu_affine_q%d" % b for b in range(2, 9)}
     assert set(names) == expected
 
 
@@ -105,6 +106,21 @@ def test_dense_validation(lib, kwargs, status):
 def test_affine_validation(lib, kwargs, status):
     for bits in range(2, 9):
         assert affine(lib, bits=bits, **kwargs) == status
+
+
+def test_swiglu_affine_validation(lib):
+    for b in range(2, 9):
+        f = getattr(lib, "aqg_swiglu_affine_q%d" % b)
+        ok = (A16, B16, D16, E16, 0x60000, 0x70000, 0x80000, C16, 1, 16, 64, 0, None, 0, None)
+        args = list(ok)
+        assert f(*[None if i == 4 else a for i, a in enumerate(args)]) == aqg.AQG_ERR_INVALID_ARG   # no Wu
+        assert f(*[None if i == 5 else a for i, a in enumerate(args)]) == aqg.AQG_ERR_INVALID_ARG   # no up scales
+        assert f(*[0x70002 if i == 5 else a for i, a in enumerate(args)]) == aqg.AQG_ERR_ALIGNMENT
+        assert f(*[96 if i == 10 else a for i, a in enumerate(args)]) == aqg.AQG_ERR_UNSUPPORTED  # K % 64
+        assert f(*[0x80000 if i == 7 else a for i, a in enumerate(args)]) == aqg.AQG_ERR_INVALID_ARG  # out on up biases
+        if not HAS_GPU_NODE:
+            assert f(*args) == aqg.AQG_ERR_DEVICE
+    assert aqg.workspace_bytes(aqg.AQG_KIND_SWIGLU_AFFINE + 4, 8, 4096, 1536) == 0
 
 
 def test_swiglu_validation(lib):
