@@ -31,6 +31,10 @@ namespace aqg {
 namespace detail {
 
 constexpr int kAffineSplitMaxWaves = 16;
+// With two weight streams (the fused SwiGLU) a wavefront holds twice the
+// codes, scales and biases: at most 8 wavefronts, so each may take 256
+// registers.
+template <int S> constexpr int affine_split_max_waves() { return S == 2 ? 8 : kAffineSplitMaxWaves; }
 
 // NDW consecutive dwords at byte offset off of a buffer (16-, 8- and 4-byte
 // loads).
@@ -57,8 +61,12 @@ __device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t rs, uint32_t 
 // tile's codes finds them in that XCD's L2.  An output's chain of MFMAs and
 // fp32 operations does not depend on its column, so results are those of
 // the unsplit kernel.
-template <int BITS, int KPW, int CW = 0>
-__global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel(ProjArgs a)
+// S = 2: the fused SwiGLU over affine gate (w0, scales, biases) and up (w1,
+// scales1, biases1) matrices: both streams of a tile through the same x^T
+// operands and code offsets, two partial tiles per wavefront, and
+// silu(g) * u in fp32 at the end.
+template <int BITS, int KPW, int CW = 0, int S = 1>
+__global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split_kernel(ProjArgs a)
 {
     extern __shared__ float lds_red[];
     constexpr int GPK = AffineMma<BITS>::GPK;     // groups per 128-byte k-block
@@ -94,24 +102,31 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
     // codes: k-block p as two whole-line loads (rows 0..7 and 8..15)
     const uint32_t voff = (uint32_t)((r & 7) * row_bytes + 16 * ((r < 8 ? 0 : 4) + c));
     const int half_off = (int)(8 * row_bytes);
-    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(static_cast<const char*>(a.w0) + n0 * row_bytes, (a.N - n0) * row_bytes);
-    u32x4_t wa[KPW][2];
+    u32x4_t wa[S][KPW][2];
 #pragma unroll
-    for (int p = 0; p < KPW; ++p) {
-        const int koff = 128 * (kb0 + p);
-        wa[p][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff, kLoadNT));
-        wa[p][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff + half_off, kLoadNT));
+    for (int s = 0; s < S; ++s) {
+        const __amdgpu_buffer_rsrc_t rw =
+            tile_rsrc(static_cast<const char*>(s == 0 ? a.w0 : a.w1) + n0 * row_bytes, (a.N - n0) * row_bytes);
+#pragma unroll
+        for (int p = 0; p < KPW; ++p) {
+            const int koff = 128 * (kb0 + p);
+            wa[s][p][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff, kLoadNT));
+            wa[s][p][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff + half_off, kLoadNT));
+        }
     }
     // scales and biases of groups g0 .. g0 + GPW - 1 for rows 4c .. 4c + 3
     // (the rows of this lane's accumulators); rows past N read as zero
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(a.scales + n0 * gpr, (a.N - n0) * gpr * 2);
-    const __amdgpu_buffer_rsrc_t rb = tile_rsrc(a.biases + n0 * gpr, (a.N - n0) * gpr * 2);
-    uint32_t sw[4][SDW], bw[4][SDW];
+    uint32_t sw[S][4][SDW], bw[S][4][SDW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (uint32_t)(((4 * c + i) * gpr + g0) * 2);
-        load_dwords<SDW>(rs, off, sw[i]);
-        load_dwords<SDW>(rb, off, bw[i]);
+    for (int s = 0; s < S; ++s) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc((s == 0 ? a.scales : a.scales1) + n0 * gpr, (a.N - n0) * gpr * 2);
+        const __amdgpu_buffer_rsrc_t rb = tile_rsrc((s == 0 ? a.biases : a.biases1) + n0 * gpr, (a.N - n0) * gpr * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = (uint32_t)(((4 * c + i) * gpr + g0) * 2);
+            load_dwords<SDW>(rs, off, sw[s][i]);
+            load_dwords<SDW>(rb, off, bw[s][i]);
+        }
     }
     // x^T: lane (c, column r) holds the operands of k-steps 2g, 2g + 1 of its
     // groups, the groups' sums over all four lane quarters (fixed order) and
@@ -121,7 +136,7 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
     // D0 lives in LDS (this wavefront's [GPW][16 columns] after the reduction
     // area): each lane stores the value of its own column and later reads back
     // the address it wrote (the four lanes of a column write the same value)
-    float* d0w = lds_red + (size_t)(blockDim.x >> 6) * 4 * 65 + (size_t)wave * GPW * 16;
+    float* d0w = lds_red + (size_t)S * nks * 4 * 65 + (size_t)wave * GPW * 16;
     {
         const bool have = r < a.M;
         const uint16_t* xrow = a.x + (size_t)(have ? r : 0) * a.K + 64 * g0;
@@ -150,14 +165,18 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
     asm volatile("" : "+s"(cmask));      // no instruction: only hides the constants
     asm volatile("" : "+v"(cbias));
     const bool hi8 = (lane & 8) != 0;
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[S];
 #pragma unroll
-    for (int p = 0; p < KPW; ++p) {
+    for (int s = 0; s < S; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KPW; ++p)
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
         // pc[0][t]: codes of k-step t of the block, pc[1][t]: k-step 4 + t
         uint32_t pc[2][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t l0 = wa[p][0][i], l1 = wa[p][1][i];
+            const uint32_t l0 = wa[s][p][0][i], l1 = wa[s][p][1][i];
             const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l0, 0x128, 0xF, 0xF, false);
             const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l1, 0x128, 0xF, 0xF, false);
             pc[0][i] = hi8 ? r1 : l0;
@@ -190,10 +209,10 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
             const float z0 = d0w[g * 16 + r];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t sh = sw[i][g >> 1], bh = bw[i][g >> 1];
-                const float s = __uint_as_float((g & 1) ? (sh & 0xFFFF0000u) : (sh << 16));
+                const uint32_t sh = sw[s][i][g >> 1], bh = bw[s][i][g >> 1];
+                const float sc = __uint_as_float((g & 1) ? (sh & 0xFFFF0000u) : (sh << 16));
                 const float bi = __uint_as_float((g & 1) ? (bh & 0xFFFF0000u) : (bh << 16));
-                acc[i] = fmaf(s, dg[i] - z0, fmaf(bi, X[g], acc[i]));
+                acc[s][i] = fmaf(sc, dg[i] - z0, fmaf(bi, X[g], acc[s][i]));
             }
         }
     }
@@ -202,7 +221,9 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
     // tile (rows of 65 floats: conflict-free reads below), then every thread
     // adds one output's partials in order 0, 1, ..., nks-1 and stores it
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_red[(size_t)(wave * 4 + i) * 65 + lane] = acc[i];
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_red[(size_t)((s * nks + wave) * 4 + i) * 65 + lane] = acc[s][i];
     __syncthreads();
     // output (m, n0 + n16) lives in lane (n16 / 4) * 16 + m, element n16 % 4
     for (int o = threadIdx.x; o < 256; o += blockDim.x) {
@@ -210,6 +231,12 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
         const int j0 = (n16 & 3) * 65 + (n16 >> 2) * 16 + m;
         float v = lds_red[j0];
         for (int w = 1; w < nks; ++w) v += lds_red[(size_t)(w * 4) * 65 + j0];
+        if constexpr (S == 2) {
+            const float* pu = lds_red + (size_t)nks * 4 * 65 + j0;
+            float u = pu[0];
+            for (int w = 1; w < nks; ++w) u += pu[(size_t)(w * 4) * 65];
+            v = (v / (1.0f + __expf(-v))) * u;
+        }
         const int64_t n = n0 + n16;
         if (m >= a.M || n >= a.N) continue;
         const size_t oi = (size_t)m * a.N + n;
@@ -221,29 +248,29 @@ __global__ void __launch_bounds__(64 * kAffineSplitMaxWaves) affine_split_kernel
 // k-blocks per wavefront: the smallest of 1, 2, 4 that splits the row's
 // 128-byte k-blocks over at most 16 wavefronts, with at most 8 groups per
 // wavefront (their x^T operands take 8 registers each; 0 if none fits).
-inline int affine_split_kpw(int bits, int K)
+inline int affine_split_kpw(int bits, int K, int max_waves = kAffineSplitMaxWaves)
 {
     if (!(bits == 2 || bits == 4 || bits == 8) || K % 64 != 0 || (K * bits) % 1024 != 0) return 0;
     const int kbl = K * bits / 1024;
     for (int kpw : {1, 2, 4})
-        if (kbl % kpw == 0 && kbl / kpw <= kAffineSplitMaxWaves) return kpw * (16 / bits) <= 8 ? kpw : 0;
+        if (kbl % kpw == 0 && kbl / kpw <= max_waves) return kpw * (16 / bits) <= 8 ? kpw : 0;
     return 0;
 }
 
-template <int BITS, int KPW>
+template <int BITS, int KPW, int S>
 hipError_t launch_affine_split_one(const ProjArgs& a, hipStream_t s)
 {
     if (a.M > 32) return hipErrorInvalidValue;
     const int nks = (a.K * BITS / 1024) / KPW;
     const int64_t tiles = ((int64_t)a.N + 15) / 16;
-    // partial tiles for the reduction, then each wavefront's code offsets
-    const size_t lds = (size_t)nks * 4 * 65 * 4 + (size_t)nks * KPW * AffineMma<BITS>::GPK * 16 * 4;
+    // partial tiles for the reduction (per stream), then each wavefront's code offsets
+    const size_t lds = (size_t)S * nks * 4 * 65 * 4 + (size_t)nks * KPW * AffineMma<BITS>::GPK * 16 * 4;
     // M = 17..32 runs once per 16-column block, and with at most half as many
     // row tiles as CUs M = 9..16 once per 8-column block (the two blocks of a
     // tile on one XCD).
     if (a.M > 16) {
         const int64_t blocks = (tiles + 7) / 8 * 16;
-        hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 16>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+        hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 16, S>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
         return hipGetLastError();
     }
     if (a.M > 8) {
@@ -252,26 +279,26 @@ hipError_t launch_affine_split_one(const ProjArgs& a, hipStream_t s)
         if (e != hipSuccess) return e;
         if (2 * tiles <= cus) {
             const int64_t blocks = (tiles + 7) / 8 * 16;
-            hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 8>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+            hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 8, S>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((affine_split_kernel<BITS, KPW>), dim3((unsigned)tiles), dim3(64 * nks), lds, s, a);
+    hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 0, S>), dim3((unsigned)tiles), dim3(64 * nks), lds, s, a);
     return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, int S>
 hipError_t launch_affine_split_impl(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
     (void)c;
     constexpr int GPK = AffineMma<BITS>::GPK;
-    switch (affine_split_kpw(BITS, a.K)) {
-        case 1: return launch_affine_split_one<BITS, 1>(a, s);
+    switch (affine_split_kpw(BITS, a.K, affine_split_max_waves<S>())) {
+        case 1: return launch_affine_split_one<BITS, 1, S>(a, s);
         case 2:
-            if constexpr (2 * GPK <= 8) return launch_affine_split_one<BITS, 2>(a, s);
+            if constexpr (2 * GPK <= 8) return launch_affine_split_one<BITS, 2, S>(a, s);
             else return hipErrorInvalidValue;
         case 4:
-            if constexpr (4 * GPK <= 8) return launch_affine_split_one<BITS, 4>(a, s);
+            if constexpr (4 * GPK <= 8) return launch_affine_split_one<BITS, 4, S>(a, s);
             else return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }

@@ -4,18 +4,18 @@
 
 namespace aqg {
 template <>
-hipError_t launch_affine_split<2>(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+hipError_t launch_affine_split<2, false>(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
-    return detail::launch_affine_split_impl<2>(a, c, s);
+    return detail::launch_affine_split_impl<2, 1>(a, c, s);
 }
 template <>
-hipError_t launch_affine_split<4>(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+hipError_t launch_affine_split<4, false>(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
-    return detail::launch_affine_split_impl<4>(a, c, s);
+    return detail::launch_affine_split_impl<4, 1>(a, c, s);
 }
 template <>
-hipError_t launch_affine_split<8>(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+hipError_t launch_affine_split<8, false>(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
-    return detail::launch_affine_split_impl<8>(a, c, s);
+    return detail::launch_affine_split_impl<8, 1>(a, c, s);
 }
 }  // namespace aqg

@@ -93,8 +93,9 @@ template <int BITS>
 hipError_t launch_affine_tile(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // Affine matrix-core launcher for small N, k split over one workgroup per
-// 16-row tile, BITS = 2, 4 or 8 (affine_split.hip).
-template <int BITS>
+// 16-row tile, BITS = 2, 4 or 8 (affine_split.hip; the fused SwiGLU over
+// affine gate and up matrices in affine_split_swiglu.hip).
+template <int BITS, bool SWIGLU>
 hipError_t launch_affine_split(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // Affine matrix-core launcher, BITS = 2, 4 or 8 (affine_mfma*.hip).

@@ -157,11 +157,13 @@ bool choose_mfma_split(bool swiglu, int M, int N, int K, LaunchCfg& c)
 // way, twice as many workgroups each staging x^T of K = 4096).  Depends on
 // (bits, N, K) and the column bucket, and every M of a bucket computes each
 // output the same way (both buckets alike with at most 128 tiles).
-bool choose_affine_split(int bits, int M, int N, int K, LaunchCfg& c)
+bool choose_affine_split(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
 {
     c = LaunchCfg{};
     const int64_t tiles = ((int64_t)N + 15) / 16;
-    if (M < 5 || M > 32 || tiles > (M > 16 ? 128 : 256) || detail::affine_split_kpw(bits, K) == 0) return false;
+    const int maxw = swiglu ? detail::affine_split_max_waves<2>() : detail::affine_split_max_waves<1>();
+    if (M < 5 || M > 32 || tiles > ((M > 16 && !swiglu) ? 128 : 256) || detail::affine_split_kpw(bits, K, maxw) == 0)
+        return false;
     c.path = PATH_AFFINE_SPLIT;
     c.MT = M <= 16 ? 16 : 32;
     c.KT = K;
@@ -342,8 +344,11 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
 {
     LaunchCfg c;
     if (swiglu && bits != 0) {
-        // fused SwiGLU over affine gate and up matrices: the dot-product
-        // kernels with both weight streams through the same x operands
+        // fused SwiGLU over affine gate and up matrices: both weight streams
+        // through the same x operands, on the small-matrix matrix-core kernel
+        // from M = 5 (2, 4, 8 bits, at most 256 row tiles), else on the
+        // dot-product kernels
+        if (choose_affine_split(bits, true, M, N, K, c)) return c;
         if (choose_piece(bits, true, M, N, K, c)) return c;
         if (choose_stream(bits, true, M, N, K, c)) return c;
         return choose_valu(bits, true, M, N, K);
@@ -377,7 +382,7 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     // issued at once (4-bit 1024 x 3584 at M = 16: 11.8 -> 7.3 us; 1024 x
     // 1024: 7.4 -> 4.0 us; 8-bit 4096 x 4096: 15.1 -> 14.2 us; 2- and 4-bit
     // 4096 x 4096 level with the tile kernel).
-    if (!swiglu && choose_affine_split(bits, M, N, K, c)) return c;
+    if (!swiglu && choose_affine_split(bits, false, M, N, K, c)) return c;
     if (!swiglu && M >= 5 && choose_affine_tile(bits, M, N, K, c)) return c;
     if (!swiglu && M >= 3 && choose_affine_mfma(bits, M, N, K, c) &&
         (M > 8 || (bits == 4 && c.ksplit_log2 == 0))) return c;
@@ -408,11 +413,10 @@ hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg
         }
     }
     if (c.path == PATH_AFFINE_SPLIT) {
-        if (swiglu) return hipErrorInvalidValue;
         switch (bits) {
-            case 2: return launch_affine_split<2>(a, c, s);
-            case 4: return launch_affine_split<4>(a, c, s);
-            case 8: return launch_affine_split<8>(a, c, s);
+            case 2: return swiglu ? launch_affine_split<2, true>(a, c, s) : launch_affine_split<2, false>(a, c, s);
+            case 4: return swiglu ? launch_affine_split<4, true>(a, c, s) : launch_affine_split<4, false>(a, c, s);
+            case 8: return swiglu ? launch_affine_split<8, true>(a, c, s) : launch_affine_split<8, false>(a, c, s);
             default: return hipErrorInvalidValue;
         }
     }
