@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "lib_path", "load", "AqgError", "abi_version", "status_string", "workspace_bytes", "dispatch_path",
     "gemv_bf16", "gemv_affine", "swiglu_bf16", "swiglu_affine", "unpack_codes", "gemv_bf16_argmax",
-    "gemv_affine_argmax",
+    "gemv_affine_argmax", "gemv_bf16_multi", "gemv_affine_multi",
     "gemv_affine_q2", "gemv_affine_q3", "gemv_affine_q4", "gemv_affine_q5",
     "gemv_affine_q6", "gemv_affine_q7", "gemv_affine_q8",
     "AQG_OK", "AQG_ERR_INVALID_ARG", "AQG_ERR_UNSUPPORTED", "AQG_ERR_ALIGNMENT",
@@ -80,6 +80,14 @@ def load():
             f = getattr(lib, "aqg_swiglu_affine_q%d" % b)
             f.restype = I
             f.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P, Z, P]
+        PP = ctypes.POINTER(ctypes.c_void_p)
+        IP = ctypes.POINTER(ctypes.c_int)
+        lib.aqg_gemv_bf16_multi.restype = I
+        lib.aqg_gemv_bf16_multi.argtypes = [P, I, PP, PP, IP, I, I, I, P, Z, P]
+        for b in range(2, 9):
+            f = getattr(lib, "aqg_gemv_affine_q%d_multi" % b)
+            f.restype = I
+            f.argtypes = [P, I, PP, PP, PP, PP, IP, I, I, I, P, Z, P]
         lib.aqg_gemv_bf16_argmax.restype = I
         lib.aqg_gemv_bf16_argmax.argtypes = [P, P, P, P, I, I, I, P, Z, P]
         for b in range(2, 9):
@@ -268,6 +276,56 @@ def swiglu_affine(x: torch.Tensor, gate, up, bits: int, out_dtype=torch.bfloat16
     _check(fn(_p(x), _p(gate[0]), _p(gate[1]), _p(gate[2]), _p(up[0]), _p(up[1]), _p(up[2]), _p(y),
               M, N, K, _odt(y), ws, wsb, _stream(x)), "aqg_swiglu_affine_q%d" % bits)
     return y
+
+
+def _ptrs(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _multi_out(out, M: int, Ns, out_dtype, like):
+    if out is None:
+        return [torch.empty((M, n), dtype=out_dtype, device=like.device) for n in Ns]
+    if len(out) != len(Ns):
+        raise ValueError("one output per projection")
+    return [_out(o, M, n, out_dtype, like) for o, n in zip(out, Ns)]
+
+
+def gemv_bf16_multi(x: torch.Tensor, Ws, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """[x . W_p^T for each W_p] (1..4 dense projections of the same x) in one call."""
+    _dev(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    for i, W in enumerate(Ws):
+        _dev(W, "W[%d]" % i, (torch.bfloat16,))
+        if W.shape[1] != K:
+            raise ValueError("W[%d] must be [N, %d]" % (i, K))
+    Ns = [W.shape[0] for W in Ws]
+    ys = _multi_out(out, M, Ns, out_dtype, x)
+    ws, wsb = _ws(workspace)
+    _check(load().aqg_gemv_bf16_multi(_p(x), len(Ws), _ptrs(Ws), _ptrs(ys), (ctypes.c_int * len(Ns))(*Ns),
+                                      M, K, _odt(ys[0]), ws, wsb, _stream(x)), "aqg_gemv_bf16_multi")
+    return ys
+
+
+def gemv_affine_multi(x: torch.Tensor, mats, bits: int, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """[x . (scale*q + bias)_p^T for each (Wq, scales, biases)_p] of one width, in one call."""
+    if bits not in range(2, 9):
+        raise ValueError("bits must be in 2..8")
+    _dev(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    if K % 64:
+        raise ValueError("K must be a multiple of 64")
+    Ns = []
+    for i, (Wq, sc, bi) in enumerate(mats):
+        N = Wq.shape[0]
+        _affine_check(Wq, sc, bi, bits, N, K, "projection %d" % i)
+        Ns.append(N)
+    ys = _multi_out(out, M, Ns, out_dtype, x)
+    ws, wsb = _ws(workspace)
+    fn = getattr(load(), "aqg_gemv_affine_q%d_multi" % bits)
+    _check(fn(_p(x), len(mats), _ptrs([m[0] for m in mats]), _ptrs([m[1] for m in mats]),
+              _ptrs([m[2] for m in mats]), _ptrs(ys), (ctypes.c_int * len(Ns))(*Ns), M, K, _odt(ys[0]),
+              ws, wsb, _stream(x)), "aqg_gemv_affine_q%d_multi" % bits)
+    return ys
 
 
 def _argmax_out(M: int, like: torch.Tensor, out):

@@ -137,6 +137,106 @@ int run_affine(int bits, const void* x, const uint32_t* Wq, const void* scales, 
                           ws, wsb, stream);
 }
 
+// ------------------------------------------------ multi-projection launch
+
+// The kernels that take a segment table (several projections of one x in
+// one launch): one row tile per workgroup, or a persistent walk over tiles
+// that looks up each tile's projection.
+bool multi_fused(const aqg::LaunchCfg& c)
+{
+    return c.path == aqg::PATH_PIECE || c.path == aqg::PATH_MFMA_SPLIT || c.path == aqg::PATH_AFFINE_SPLIT;
+}
+
+int run_multi(int bits, const void* x, int P, const void* const* W, const void* const* scales,
+              const void* const* biases, void* const* y, const int* N, int M, int K, int out_dtype, void* ws,
+              size_t wsb, void* stream)
+{
+    if (!x || !W || !y || !N || (bits && (!scales || !biases))) return AQG_ERR_INVALID_ARG;
+    if (P < 1 || P > aqg::kMaxSegments) return AQG_ERR_UNSUPPORTED;
+    int64_t total = 0;
+    bool aligned16 = true;
+    for (int p = 0; p < P; ++p) {
+        if (N[p] <= 0) return AQG_ERR_INVALID_ARG;
+        if (p + 1 < P && N[p] % 16 != 0) aligned16 = false;
+        total += N[p];
+    }
+    if (total > 0x7FFFFFFF) return AQG_ERR_UNSUPPORTED;
+    // every projection is a valid call on its own (same checks, in order)
+    for (int p = 0; p < P; ++p) {
+        int st = check_common(x, y[p], M, N[p], K, out_dtype);
+        if (st != AQG_OK) return st;
+        if (!W[p] || (bits && (!scales[p] || !biases[p]))) return AQG_ERR_INVALID_ARG;
+        if (bits == 0 ? (K % 8 != 0) : (K % 64 != 0)) return AQG_ERR_UNSUPPORTED;
+        if (!aligned(W[p], 16) || (bits && (!aligned(scales[p], 4) || !aligned(biases[p], 4))))
+            return AQG_ERR_ALIGNMENT;
+    }
+    if (wsb < aqg_workspace_bytes(bits, M, (int)total, K)) return AQG_ERR_INVALID_ARG;
+    (void)ws;
+    // no output overlaps an input or another output
+    const size_t xbytes = (size_t)M * K * 2;
+    for (int p = 0; p < P; ++p) {
+        const size_t yb = out_bytes(M, N[p], out_dtype);
+        if (overlap(y[p], yb, x, xbytes)) return AQG_ERR_INVALID_ARG;
+        for (int q = 0; q < P; ++q) {
+            const size_t wb = bits ? (size_t)N[q] * K / 8 * bits : (size_t)N[q] * K * 2;
+            const size_t gb = (size_t)N[q] * (K / 64) * 2;
+            if (overlap(y[p], yb, W[q], wb)) return AQG_ERR_INVALID_ARG;
+            if (bits && (overlap(y[p], yb, scales[q], gb) || overlap(y[p], yb, biases[q], gb)))
+                return AQG_ERR_INVALID_ARG;
+            if (q != p && overlap(y[p], yb, y[q], out_bytes(M, N[q], out_dtype))) return AQG_ERR_INVALID_ARG;
+        }
+    }
+    int st = check_device();
+    if (st != AQG_OK) return st;
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    auto base_args = [&](const aqg::LaunchCfg& cfg, int n) {
+        aqg::ProjArgs a{};
+        a.x = static_cast<const uint16_t*>(x);
+        a.M = M;
+        a.N = n;
+        a.K = K;
+        a.KT = cfg.KT;
+        a.lpr_log2 = cfg.lpr_log2;
+        a.ksplit_log2 = cfg.ksplit_log2;
+        a.tpw = cfg.tpw;
+        a.out_f32 = out_dtype == AQG_OUT_F32;
+        return a;
+    };
+    const aqg::LaunchCfg cfg = aqg::choose_config(bits, false, M, (int)total, K);
+    if (aligned16 && multi_fused(cfg)) {
+        aqg::ProjArgs a = base_args(cfg, (int)total);
+        a.nseg = P;
+        int64_t row0 = 0;
+        for (int p = 0; p < P; ++p) {
+            a.seg_row0[p] = row0;
+            a.seg_w[p] = W[p];
+            a.seg_scales[p] = bits ? static_cast<const uint16_t*>(scales[p]) : nullptr;
+            a.seg_biases[p] = bits ? static_cast<const uint16_t*>(biases[p]) : nullptr;
+            a.seg_y[p] = y[p];
+            row0 += N[p];
+        }
+        a.seg_row0[P] = row0;
+        a.w0 = W[0];
+        a.scales = a.seg_scales[0];
+        a.biases = a.seg_biases[0];
+        a.y = y[0];
+        return finish(aqg::launch_proj(bits, false, a, cfg, s));
+    }
+    // otherwise one launch per projection, each on its own kernel
+    for (int p = 0; p < P; ++p) {
+        const aqg::LaunchCfg c = aqg::choose_config(bits, false, M, N[p], K);
+        aqg::ProjArgs a = base_args(c, N[p]);
+        a.w0 = W[p];
+        a.scales = bits ? static_cast<const uint16_t*>(scales[p]) : nullptr;
+        a.biases = bits ? static_cast<const uint16_t*>(biases[p]) : nullptr;
+        a.y = y[p];
+        const int e = finish(aqg::launch_proj(bits, false, a, c, s));
+        if (e != AQG_OK) return e;
+    }
+    return AQG_OK;
+}
+
 // ---------------------------------------------------------- row argmax
 
 constexpr int kArgmaxChunk = 8192;        // columns per partial when the GEMV writes y first
@@ -319,6 +419,30 @@ int aqg_gemv_argmax_noalloc(int bits, const void* x, const void* W, const void* 
     if (st != AQG_OK) return st;
     return run_argmax(bits, x, W, scales, biases, max_val, max_idx, M, N, K, ws, kScratchBytes, stream);
 }
+
+int aqg_gemv_bf16_multi(const void* x, int P, const void* const* W, void* const* y, const int* N, int M, int K,
+                        int out_dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return run_multi(0, x, P, W, nullptr, nullptr, y, N, M, K, out_dtype, workspace, workspace_bytes, stream);
+}
+
+#define AQG_AFFINE_MULTI_ENTRY(B)                                                                            \
+    int aqg_gemv_affine_q##B##_multi(const void* x, int P, const uint32_t* const* Wq,                        \
+                                     const void* const* scales, const void* const* biases, void* const* y,  \
+                                     const int* N, int M, int K, int out_dtype, void* workspace,            \
+                                     size_t workspace_bytes, void* stream)                                  \
+    {                                                                                                        \
+        return run_multi(B, x, P, reinterpret_cast<const void* const*>(Wq), scales, biases, y, N, M, K,      \
+                         out_dtype, workspace, workspace_bytes, stream);                                     \
+    }
+AQG_AFFINE_MULTI_ENTRY(2)
+AQG_AFFINE_MULTI_ENTRY(3)
+AQG_AFFINE_MULTI_ENTRY(4)
+AQG_AFFINE_MULTI_ENTRY(5)
+AQG_AFFINE_MULTI_ENTRY(6)
+AQG_AFFINE_MULTI_ENTRY(7)
+AQG_AFFINE_MULTI_ENTRY(8)
+#undef AQG_AFFINE_MULTI_ENTRY
 
 int aqg_gemv_bf16_argmax(const void* x, const void* W, float* max_val, int32_t* max_idx, int M, int N, int K,
                          void* workspace, size_t workspace_bytes, void* stream)

@@ -77,10 +77,13 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
     int64_t tile = blockIdx.x;
     if constexpr (CW > 0) {
         static_assert(CW <= 16, "column blocks of a 16-column kernel");
-        const int b = blockIdx.x;
-        tile = (int64_t)(b >> 4) * 8 + (b & 7);
+        tile = (int64_t)(blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
         if (tile * 16 >= a.N) return;            // whole workgroup, before any barrier
-        if ((b >> 3) & 1) {
+    }
+    // a multi-projection launch: this tile's projection (matrix, output, N)
+    const int64_t n0 = seg_enter(a, tile * 16);
+    if constexpr (CW > 0) {
+        if ((blockIdx.x >> 3) & 1) {
             a.x += (size_t)CW * a.K;
             a.y = static_cast<char*>(a.y) + (size_t)CW * a.N * (a.out_f32 ? 4 : 2);
             a.M -= CW;
@@ -95,7 +98,6 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
     const int r = lane & 15;
     const int64_t row_bytes = (int64_t)a.K * BITS / 8;
     const int gpr = a.K / 64;
-    const int64_t n0 = tile * 16;
     const int kb0 = wave * KPW;                  // first k-block of this wavefront
     const int g0 = kb0 * GPK;                    // its first group
 

@@ -8,6 +8,8 @@
 
 namespace aqg {
 
+constexpr int kMaxSegments = 4;   // projections of one multi-projection launch
+
 // Arguments of one projection launch.  Pointers are device pointers.
 struct ProjArgs {
     const uint16_t* x;       // bf16 [M][K]
@@ -35,7 +37,40 @@ struct ProjArgs {
     void* amx;
     int64_t amx_slots;
     int64_t* amx_producers;
+    // Several projections of one x in one launch (nseg > 0): the kernel sees
+    // a virtual matrix whose rows are segment 0's rows, then segment 1's, ...
+    // (N = the total); segment s starts at virtual row seg_row0[s] (a
+    // multiple of 16, so no row tile straddles two segments), has its own
+    // weights, scales and biases (affine) and its own output y_s [M][rows_s].
+    int nseg;
+    int64_t seg_row0[kMaxSegments + 1];
+    const void* seg_w[kMaxSegments];
+    const uint16_t* seg_scales[kMaxSegments];
+    const uint16_t* seg_biases[kMaxSegments];
+    void* seg_y[kMaxSegments];
 };
+
+// Segment of virtual row n of a multi-projection launch (0 without).
+__host__ __device__ inline int seg_of(const ProjArgs& a, int64_t n)
+{
+    int s = 0;
+    for (int i = 1; i < a.nseg; ++i) s = n >= a.seg_row0[i] ? i : s;
+    return s;
+}
+
+// Rewrite a's matrix, scales, biases, output and N to those of the segment
+// holding virtual row n0; returns n0 within that segment.
+__host__ __device__ inline int64_t seg_enter(ProjArgs& a, int64_t n0)
+{
+    if (a.nseg == 0) return n0;
+    const int s = seg_of(a, n0);
+    a.w0 = a.seg_w[s];
+    a.scales = a.seg_scales[s];
+    a.biases = a.seg_biases[s];
+    a.y = a.seg_y[s];
+    a.N = (int)(a.seg_row0[s + 1] - a.seg_row0[s]);
+    return n0 - a.seg_row0[s];
+}
 
 enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6,
             PATH_MFMA_TILE = 7, PATH_AFFINE_TILE = 8, PATH_AFFINE_SPLIT = 9 };

@@ -36,10 +36,13 @@ __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(Pro
     int64_t tile = blockIdx.x;
     if constexpr (CW > 0) {
         static_assert(MT == 16 && CW <= 16, "column blocks of a 16-column kernel");
-        const int b = blockIdx.x;
-        tile = (int64_t)(b >> 4) * 8 + (b & 7);
+        tile = (int64_t)(blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
         if (tile * 16 >= a.N) return;            // whole workgroup, before any barrier
-        if ((b >> 3) & 1) {
+    }
+    // a multi-projection launch: this tile's projection (matrix, output, N)
+    const int64_t n0 = seg_enter(a, tile * 16);
+    if constexpr (CW > 0) {
+        if ((blockIdx.x >> 3) & 1) {
             a.x += (size_t)CW * a.K;
             a.y = static_cast<char*>(a.y) + (size_t)CW * a.N * (a.out_f32 ? 4 : 2);
             a.M -= CW;
@@ -59,7 +62,6 @@ __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(Pro
     const int r = lane & 15;
     const int h = lane & 15;
     const int64_t row_bytes = (int64_t)a.K * 2;
-    const int64_t n0 = tile * 16;
     const int s0 = wave * SPW;                   // first k-step of this wavefront
 
     // A: pair p covers k-steps s0 + 2p, s0 + 2p + 1 (64 k, 128 bytes per row)

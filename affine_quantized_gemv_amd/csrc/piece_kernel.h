@@ -293,14 +293,27 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
     int f_c = 0;                // its index within the super-tile
     __amdgpu_buffer_rsrc_t rw[S], rs[S], rb[S];
     auto set_tile = [&]() __attribute__((always_inline)) {
-        const int64_t n0 = f_tile * G;
-        const int64_t rows = a.N - n0;
+        int64_t n0 = f_tile * G;
+        // a multi-projection launch: the projection holding this tile
+        const void* w0 = a.w0;
+        const uint16_t* sc0 = a.scales;
+        const uint16_t* bi0 = a.biases;
+        int64_t nrows = a.N;
+        if (a.nseg) {
+            const int sg = seg_of(a, n0);
+            w0 = a.seg_w[sg];
+            sc0 = a.seg_scales[sg];
+            bi0 = a.seg_biases[sg];
+            nrows = a.seg_row0[sg + 1] - a.seg_row0[sg];
+            n0 -= a.seg_row0[sg];
+        }
+        const int64_t rows = nrows - n0;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            rw[s] = tile_rsrc(static_cast<const char*>(s == 0 ? a.w0 : a.w1) + n0 * row_bytes, rows * row_bytes);
+            rw[s] = tile_rsrc(static_cast<const char*>(s == 0 ? w0 : a.w1) + n0 * row_bytes, rows * row_bytes);
             if constexpr (BITS != 0) {
-                rs[s] = tile_rsrc((s == 0 ? a.scales : a.scales1) + n0 * gpr, rows * gpr * 2);
-                rb[s] = tile_rsrc((s == 0 ? a.biases : a.biases1) + n0 * gpr, rows * gpr * 2);
+                rs[s] = tile_rsrc((s == 0 ? sc0 : a.scales1) + n0 * gpr, rows * gpr * 2);
+                rb[s] = tile_rsrc((s == 0 ? bi0 : a.biases1) + n0 * gpr, rows * gpr * 2);
             }
         }
     };
@@ -550,9 +563,17 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
         const int64_t n = tile * G + r / MT;
         if (m < a.M && n < a.N) {
             const float val = obuf[v];
-            const size_t o = (size_t)m * a.N + n;
-            if (a.out_f32) reinterpret_cast<float*>(a.y)[o] = val;
-            else reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16_rne(val);
+            void* y = a.y;
+            int64_t nl = n, ny = a.N;
+            if (a.nseg) {                        // the projection holding row n
+                const int sg = seg_of(a, n);
+                y = a.seg_y[sg];
+                nl = n - a.seg_row0[sg];
+                ny = a.seg_row0[sg + 1] - a.seg_row0[sg];
+            }
+            const size_t o = (size_t)m * ny + nl;
+            if (a.out_f32) reinterpret_cast<float*>(y)[o] = val;
+            else reinterpret_cast<uint16_t*>(y)[o] = f32_to_bf16_rne(val);
         }
     }
 }

@@ -182,6 +182,53 @@ int aqg_swiglu_affine_q8(const void* x, const uint32_t* Wgq, const void* gate_sc
                          int N, int K, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Several projections of the same x in one launch (e.g. the q, k and v
+ * projections of an attention layer): for p < P,
+ *   y_p[m, n] = sum_k x[m,k] * W_p[n,k]      (n < N[p]),
+ * fp32 accumulation, within the GEMV bound.  When the launch is fused every
+ * output has exactly the bits of the same row of a single call on the
+ * concatenated matrix (rows of W_0, then W_1, ...): the same kernel computes
+ * it.  Small decode
+ * projections cost launch and first-load latency more than bandwidth; a
+ * forward's launches captured once and replayed cut a 2B model's decode
+ * step from 5.3 to 2.8 ms (TensorFold PR #849, the note on captured
+ * forwards), and a decode step can run as one persistent dispatch for the
+ * same reason (luce-megakernel HANDOFF.md, Architecture Summary).
+ *   P in 1..4; W, (scales, biases), y, N: host arrays of P entries (read
+ *   during the call) holding device pointers and row counts; every
+ *   projection must be a valid call on its own, and no output may overlap
+ *   an input or another output.
+ * One kernel serves all P projections when the shape of their concatenation
+ * (N = sum of N[p]) runs on a kernel that takes a projection table (the
+ * 16-byte-piece dot-product kernel or a small-matrix matrix-core kernel)
+ * and N[0..P-2] are multiples of 16; otherwise the projections are launched
+ * one after another on the same stream.
+ */
+int aqg_gemv_bf16_multi(const void* x, int P, const void* const* W, void* const* y, const int* N, int M, int K,
+                        int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q2_multi(const void* x, int P, const uint32_t* const* Wq, const void* const* scales,
+                             const void* const* biases, void* const* y, const int* N, int M, int K,
+                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q3_multi(const void* x, int P, const uint32_t* const* Wq, const void* const* scales,
+                             const void* const* biases, void* const* y, const int* N, int M, int K,
+                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q4_multi(const void* x, int P, const uint32_t* const* Wq, const void* const* scales,
+                             const void* const* biases, void* const* y, const int* N, int M, int K,
+                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q5_multi(const void* x, int P, const uint32_t* const* Wq, const void* const* scales,
+                             const void* const* biases, void* const* y, const int* N, int M, int K,
+                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q6_multi(const void* x, int P, const uint32_t* const* Wq, const void* const* scales,
+                             const void* const* biases, void* const* y, const int* N, int M, int K,
+                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q7_multi(const void* x, int P, const uint32_t* const* Wq, const void* const* scales,
+                             const void* const* biases, void* const* y, const int* N, int M, int K,
+                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemv_affine_q8_multi(const void* x, int P, const uint32_t* const* Wq, const void* const* scales,
+                             const void* const* biases, void* const* y, const int* N, int M, int K,
+                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Row argmax of a projection (the LM head of greedy decoding), without
  * writing the logits: for each row m < M,
  *   max_idx[m] = the lowest n with y[m,n] = max over n' of y[m,n'],

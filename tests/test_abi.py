@@ -39,7 +39,8 @@ def test_header_declares_expected_entry_points():
                 "aqg_gemv_bf16_argmax", "aqg_gemv_argmax_noalloc"} | \
                {"aqg_gemv_affine_q%d" % b for b in range(2, 9)} | \
                {"aqg_gemv_affine_q%d_argmax" % b for b in range(2, 9)} | \
-               {"aqg_swiglu_affine_q%d" % b for b in range(2, 9)}
+               {"aqg_swiglu_affine_q%d" % b for b in range(2, 9)} | \
+               {"aqg_gemv_bf16_multi"} | {"aqg_gemv_affine_q%d_multi" % b for b in range(2, 9)}
     assert set(names) == expected
 
 
@@ -229,3 +230,32 @@ def test_argmax_validation(lib, kwargs, status):
 @pytest.mark.skipif(HAS_GPU_NODE, reason="only meaningful where no GPU can be reached")
 def test_valid_argmax_without_gpu_reports_device_error(lib):
     assert argmax_dense(lib) == aqg.AQG_ERR_DEVICE
+
+
+def test_multi_validation(lib):
+    P = ctypes.c_void_p
+    f = lib.aqg_gemv_bf16_multi
+
+    def call(Ws, ys, Ns, M=1, K=64):
+        return f(A16, len(Ns), (P * len(Ws))(*Ws), (P * len(ys))(*ys), (ctypes.c_int * len(Ns))(*Ns), M, K, 0,
+                 None, 0, None)
+    W = [0x100000, 0x200000, 0x300000]
+    Y = [0x400000, 0x500000, 0x600000]
+    assert f(A16, 0, None, None, None, 1, 64, 0, None, 0, None) == aqg.AQG_ERR_INVALID_ARG
+    assert call([], [], []) == aqg.AQG_ERR_UNSUPPORTED                       # P = 0
+    assert call(W + W[:2], Y + Y[:2], [16] * 5) == aqg.AQG_ERR_UNSUPPORTED   # P = 5
+    assert call(W, Y, [16, 0, 16]) == aqg.AQG_ERR_INVALID_ARG                # an empty projection
+    assert call(W, Y, [16, 16, 16], M=33) == aqg.AQG_ERR_UNSUPPORTED
+    assert call(W, Y, [16, 16, 16], K=12) == aqg.AQG_ERR_UNSUPPORTED
+    assert call([W[0], W[1] + 8, W[2]], Y, [16, 16, 16]) == aqg.AQG_ERR_ALIGNMENT
+    assert call(W, [Y[0], Y[0] + 4, Y[2]], [16, 16, 16]) == aqg.AQG_ERR_INVALID_ARG   # outputs overlap
+    assert call(W, [Y[0], W[2], Y[2]], [16, 16, 16]) == aqg.AQG_ERR_INVALID_ARG      # output on a weight
+    if not HAS_GPU_NODE:
+        assert call(W, Y, [16, 16, 16]) == aqg.AQG_ERR_DEVICE
+    g = lib.aqg_gemv_affine_q4_multi
+    S = [0x700000, 0x710000, 0x720000]
+    B = [0x800000, 0x810000, 0x820000]
+    args = lambda s: (A16, 3, (P * 3)(*W), (P * 3)(*s), (P * 3)(*B), (P * 3)(*Y), (ctypes.c_int * 3)(16, 16, 16),
+                      1, 64, 0, None, 0, None)
+    assert g(*args([S[0], 0, S[2]])) == aqg.AQG_ERR_INVALID_ARG           # a null scale array entry
+    assert g(*args([S[0], S[1] + 2, S[2]])) == aqg.AQG_ERR_ALIGNMENT
