@@ -96,6 +96,8 @@ def load():
             f.argtypes = [P, P, P, P, P, P, I, I, I, P, Z, P]
         lib.aqg_gemv_argmax_noalloc.restype = I
         lib.aqg_gemv_argmax_noalloc.argtypes = [I, P, P, P, P, P, P, I, I, I, P]
+        lib.aqg_stream_read.restype = I
+        lib.aqg_stream_read.argtypes = [P, Z, P, P]
         lib.aqg_dispatch_path.restype = I
         lib.aqg_dispatch_path.argtypes = [I, I, I, I, ctypes.POINTER(I)]
         lib.aqg_path_name.restype = ctypes.c_char_p

@@ -65,7 +65,10 @@ __device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t rs, uint32_t 
 // scales1, biases1) matrices: both streams of a tile through the same x^T
 // operands and code offsets, two partial tiles per wavefront, and
 // silu(g) * u in fp32 at the end.
-template <int BITS, int KPW, int CW = 0, int S = 1>
+// SEG: a multi-projection launch (the tile's projection looked up in the
+// table at entry); a separate instantiation, so single projections load no
+// table before their first weight loads.
+template <int BITS, int KPW, int CW = 0, int S = 1, bool SEG = false>
 __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split_kernel(ProjArgs a)
 {
     extern __shared__ float lds_red[];
@@ -80,15 +83,26 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
         tile = (int64_t)(blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
         if (tile * 16 >= a.N) return;            // whole workgroup, before any barrier
     }
-    // a multi-projection launch: this tile's projection (matrix, output, N)
-    const int64_t n0 = seg_enter(a, tile * 16);
+    // this tile's matrix, scales, biases, output and row count: those of its
+    // projection in a multi-projection launch (locals: the kernel never
+    // writes its argument block)
+    SegView sv{a.w0, a.scales, a.biases, a.y, a.N, tile * 16};
+    if constexpr (SEG) sv = seg_view(a, tile * 16);
+    const int64_t n0 = sv.n0;
+    const int N_ = sv.N;
+    const void* const w0_ = sv.w;
+    const uint16_t* const sc_ = sv.sc;
+    const uint16_t* const bi_ = sv.bi;
+    const uint16_t* x_ = a.x;
+    void* y_ = sv.y;
+    int M_ = a.M;
     if constexpr (CW > 0) {
         if ((blockIdx.x >> 3) & 1) {
-            a.x += (size_t)CW * a.K;
-            a.y = static_cast<char*>(a.y) + (size_t)CW * a.N * (a.out_f32 ? 4 : 2);
-            a.M -= CW;
-        } else if (a.M > CW) {
-            a.M = CW;
+            x_ += (size_t)CW * a.K;
+            y_ = static_cast<char*>(y_) + (size_t)CW * N_ * (a.out_f32 ? 4 : 2);
+            M_ -= CW;
+        } else if (M_ > CW) {
+            M_ = CW;
         }
     }
     const int lane = threadIdx.x & 63;
@@ -108,7 +122,7 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const __amdgpu_buffer_rsrc_t rw =
-            tile_rsrc(static_cast<const char*>(s == 0 ? a.w0 : a.w1) + n0 * row_bytes, (a.N - n0) * row_bytes);
+            tile_rsrc(static_cast<const char*>(s == 0 ? w0_ : a.w1) + n0 * row_bytes, (N_ - n0) * row_bytes);
 #pragma unroll
         for (int p = 0; p < KPW; ++p) {
             const int koff = 128 * (kb0 + p);
@@ -121,8 +135,8 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
     uint32_t sw[S][4][SDW], bw[S][4][SDW];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc((s == 0 ? a.scales : a.scales1) + n0 * gpr, (a.N - n0) * gpr * 2);
-        const __amdgpu_buffer_rsrc_t rb = tile_rsrc((s == 0 ? a.biases : a.biases1) + n0 * gpr, (a.N - n0) * gpr * 2);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc((s == 0 ? sc_ : a.scales1) + n0 * gpr, (N_ - n0) * gpr * 2);
+        const __amdgpu_buffer_rsrc_t rb = tile_rsrc((s == 0 ? bi_ : a.biases1) + n0 * gpr, (N_ - n0) * gpr * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t off = (uint32_t)(((4 * c + i) * gpr + g0) * 2);
@@ -140,8 +154,8 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
     // the address it wrote (the four lanes of a column write the same value)
     float* d0w = lds_red + (size_t)S * nks * 4 * 65 + (size_t)wave * GPW * 16;
     {
-        const bool have = r < a.M;
-        const uint16_t* xrow = a.x + (size_t)(have ? r : 0) * a.K + 64 * g0;
+        const bool have = r < M_;
+        const uint16_t* xrow = x_ + (size_t)(have ? r : 0) * a.K + 64 * g0;
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
             float s0 = 0.f, s1 = 0.f;
@@ -240,10 +254,10 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
             v = (v / (1.0f + __expf(-v))) * u;
         }
         const int64_t n = n0 + n16;
-        if (m >= a.M || n >= a.N) continue;
-        const size_t oi = (size_t)m * a.N + n;
-        if (a.out_f32) reinterpret_cast<float*>(a.y)[oi] = v;
-        else reinterpret_cast<uint16_t*>(a.y)[oi] = f32_to_bf16_rne(v);
+        if (m >= M_ || n >= N_) continue;
+        const size_t oi = (size_t)m * N_ + n;
+        if (a.out_f32) reinterpret_cast<float*>(y_)[oi] = v;
+        else reinterpret_cast<uint16_t*>(y_)[oi] = f32_to_bf16_rne(v);
     }
 }
 
@@ -259,8 +273,8 @@ inline int affine_split_kpw(int bits, int K, int max_waves = kAffineSplitMaxWave
     return 0;
 }
 
-template <int BITS, int KPW, int S>
-hipError_t launch_affine_split_one(const ProjArgs& a, hipStream_t s)
+template <int BITS, int KPW, int S, bool SEG>
+hipError_t launch_affine_split_seg(const ProjArgs& a, hipStream_t s)
 {
     if (a.M > 32) return hipErrorInvalidValue;
     const int nks = (a.K * BITS / 1024) / KPW;
@@ -272,7 +286,7 @@ hipError_t launch_affine_split_one(const ProjArgs& a, hipStream_t s)
     // tile on one XCD).
     if (a.M > 16) {
         const int64_t blocks = (tiles + 7) / 8 * 16;
-        hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 16, S>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+        hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 16, S, SEG>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
         return hipGetLastError();
     }
     if (a.M > 8) {
@@ -281,12 +295,21 @@ hipError_t launch_affine_split_one(const ProjArgs& a, hipStream_t s)
         if (e != hipSuccess) return e;
         if (2 * tiles <= cus) {
             const int64_t blocks = (tiles + 7) / 8 * 16;
-            hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 8, S>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+            hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 8, S, SEG>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 0, S>), dim3((unsigned)tiles), dim3(64 * nks), lds, s, a);
+    hipLaunchKernelGGL((affine_split_kernel<BITS, KPW, 0, S, SEG>), dim3((unsigned)tiles), dim3(64 * nks), lds, s, a);
     return hipGetLastError();
+}
+
+template <int BITS, int KPW, int S>
+hipError_t launch_affine_split_one(const ProjArgs& a, hipStream_t s)
+{
+    if constexpr (S == 1) {
+        if (a.nseg > 1) return launch_affine_split_seg<BITS, KPW, S, true>(a, s);
+    }
+    return launch_affine_split_seg<BITS, KPW, S, false>(a, s);
 }
 
 template <int BITS, int S>

@@ -37,11 +37,13 @@ struct ProjArgs {
     void* amx;
     int64_t amx_slots;
     int64_t* amx_producers;
-    // Several projections of one x in one launch (nseg > 0): the kernel sees
+    // Several projections of one x in one launch (nseg > 1): the kernel sees
     // a virtual matrix whose rows are segment 0's rows, then segment 1's, ...
     // (N = the total); segment s starts at virtual row seg_row0[s] (a
     // multiple of 16, so no row tile straddles two segments), has its own
     // weights, scales and biases (affine) and its own output y_s [M][rows_s].
+    // launch_proj fills a one-segment table (w0, scales, biases, y, N) when
+    // nseg is 0, so the kernels read the table without a branch.
     int nseg;
     int64_t seg_row0[kMaxSegments + 1];
     const void* seg_w[kMaxSegments];
@@ -50,26 +52,60 @@ struct ProjArgs {
     void* seg_y[kMaxSegments];
 };
 
+// The segment table is read with constant indices only: a variable index
+// into the kernel-argument arrays would make the compiler copy the whole
+// argument block to private memory.
+
 // Segment of virtual row n of a multi-projection launch (0 without).
 __host__ __device__ inline int seg_of(const ProjArgs& a, int64_t n)
 {
     int s = 0;
-    for (int i = 1; i < a.nseg; ++i) s = n >= a.seg_row0[i] ? i : s;
+#pragma unroll
+    for (int i = 1; i < kMaxSegments; ++i) s = ((i < a.nseg) & (n >= a.seg_row0[i])) ? i : s;
     return s;
 }
 
-// Rewrite a's matrix, scales, biases, output and N to those of the segment
-// holding virtual row n0; returns n0 within that segment.
-__host__ __device__ inline int64_t seg_enter(ProjArgs& a, int64_t n0)
+// One field of segment s (a constant-index select).
+template <class T>
+__host__ __device__ inline T seg_pick(const T (&v)[kMaxSegments], int s)
 {
-    if (a.nseg == 0) return n0;
+    T r = v[0];
+#pragma unroll
+    for (int i = 1; i < kMaxSegments; ++i) r = s == i ? v[i] : r;
+    return r;
+}
+
+// First row and row count of segment s.
+__host__ __device__ inline int64_t seg_start(const ProjArgs& a, int s)
+{
+    int64_t r = a.seg_row0[0];
+#pragma unroll
+    for (int i = 1; i < kMaxSegments; ++i) r = s == i ? a.seg_row0[i] : r;
+    return r;
+}
+__host__ __device__ inline int64_t seg_rows(const ProjArgs& a, int s)
+{
+    int64_t r = a.seg_row0[1] - a.seg_row0[0];
+#pragma unroll
+    for (int i = 1; i < kMaxSegments; ++i) r = s == i ? a.seg_row0[i + 1] - a.seg_row0[i] : r;
+    return r;
+}
+
+// The matrix, scales, biases, output and row count of the projection holding
+// virtual row n0 (a's own without segments), and n0 within that projection.
+struct SegView {
+    const void* w;
+    const uint16_t* sc;
+    const uint16_t* bi;
+    void* y;
+    int N;
+    int64_t n0;
+};
+__host__ __device__ inline SegView seg_view(const ProjArgs& a, int64_t n0)
+{
     const int s = seg_of(a, n0);
-    a.w0 = a.seg_w[s];
-    a.scales = a.seg_scales[s];
-    a.biases = a.seg_biases[s];
-    a.y = a.seg_y[s];
-    a.N = (int)(a.seg_row0[s + 1] - a.seg_row0[s]);
-    return n0 - a.seg_row0[s];
+    return SegView{seg_pick(a.seg_w, s), seg_pick(a.seg_scales, s), seg_pick(a.seg_biases, s),
+                   seg_pick(a.seg_y, s), (int)seg_rows(a, s), n0 - seg_start(a, s)};
 }
 
 enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6,

@@ -397,7 +397,26 @@ bool argmax_fused(const LaunchCfg& c)
     return c.path == PATH_PIECE || c.path == PATH_MFMA_TILE || (c.path == PATH_AFFINE_MFMA && c.ksplit_log2 == 0);
 }
 
-hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
+hipError_t launch_proj_table(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+hipError_t launch_proj(int bits, bool swiglu, const ProjArgs& a0, const LaunchCfg& c, hipStream_t s)
+{
+    if (a0.nseg > 0) return launch_proj_table(bits, swiglu, a0, c, s);
+    // one projection: a one-segment table
+    ProjArgs a = a0;
+    a.nseg = 1;
+    a.seg_row0[0] = 0;
+    for (int i = 1; i <= kMaxSegments; ++i) a.seg_row0[i] = a.N;
+    for (int i = 0; i < kMaxSegments; ++i) {
+        a.seg_w[i] = a.w0;
+        a.seg_scales[i] = a.scales;
+        a.seg_biases[i] = a.biases;
+        a.seg_y[i] = a.y;
+    }
+    return launch_proj_table(bits, swiglu, a, c, s);
+}
+
+hipError_t launch_proj_table(int bits, bool swiglu, const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
     if (c.path == PATH_AFFINE_TILE) {
         if (swiglu) return hipErrorInvalidValue;

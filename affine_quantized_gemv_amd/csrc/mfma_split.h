@@ -29,7 +29,10 @@ constexpr int kMfmaSplitMaxWaves = 16;
 // finds them in that XCD's L2.  Twice the workgroups, each with half of the
 // x^T traffic.  An output's MFMA chain does not depend on its column, so
 // results are those of the unsplit kernel.
-template <int MT, bool SWIGLU, int SPW, int CW = 0>
+// SEG: a multi-projection launch (the tile's projection looked up in the
+// table at entry); a separate instantiation, so single projections load no
+// table before their first weight loads.
+template <int MT, bool SWIGLU, int SPW, int CW = 0, bool SEG = false>
 __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(ProjArgs a)
 {
     extern __shared__ float lds_red[];
@@ -39,15 +42,24 @@ __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(Pro
         tile = (int64_t)(blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
         if (tile * 16 >= a.N) return;            // whole workgroup, before any barrier
     }
-    // a multi-projection launch: this tile's projection (matrix, output, N)
-    const int64_t n0 = seg_enter(a, tile * 16);
+    // this tile's matrix, scales, biases, output and row count: those of its
+    // projection in a multi-projection launch (locals: the kernel never
+    // writes its argument block)
+    SegView sv{a.w0, a.scales, a.biases, a.y, a.N, tile * 16};
+    if constexpr (SEG) sv = seg_view(a, tile * 16);
+    const int64_t n0 = sv.n0;
+    const int N_ = sv.N;
+    const void* const w0_ = sv.w;
+    const uint16_t* x_ = a.x;
+    void* y_ = sv.y;
+    int M_ = a.M;
     if constexpr (CW > 0) {
         if ((blockIdx.x >> 3) & 1) {
-            a.x += (size_t)CW * a.K;
-            a.y = static_cast<char*>(a.y) + (size_t)CW * a.N * (a.out_f32 ? 4 : 2);
-            a.M -= CW;
-        } else if (a.M > CW) {
-            a.M = CW;
+            x_ += (size_t)CW * a.K;
+            y_ = static_cast<char*>(y_) + (size_t)CW * N_ * (a.out_f32 ? 4 : 2);
+            M_ -= CW;
+        } else if (M_ > CW) {
+            M_ = CW;
         }
     }
     constexpr int NB = MT / 16;
@@ -71,7 +83,7 @@ __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(Pro
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const __amdgpu_buffer_rsrc_t rs =
-            tile_rsrc(static_cast<const char*>(s == 0 ? a.w0 : a.w1) + n0 * row_bytes, (a.N - n0) * row_bytes);
+            tile_rsrc(static_cast<const char*>(s == 0 ? w0_ : a.w1) + n0 * row_bytes, (N_ - n0) * row_bytes);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int koff = 64 * (s0 + 2 * p);  // bytes: 32 k per step, 2 bytes each
@@ -87,8 +99,8 @@ __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(Pro
         for (int b = 0; b < NB; ++b) {
             const int m = 16 * b + r;
             xb[t][b] = u32x4_t{0u, 0u, 0u, 0u};
-            if (m < a.M)
-                xb[t][b] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)m * a.K + 32 * (s0 + t) + 8 * c);
+            if (m < M_)
+                xb[t][b] = *reinterpret_cast<const u32x4_t*>(x_ + (size_t)m * a.K + 32 * (s0 + t) + 8 * c);
         }
 
     const bool hi8 = (lane & 8) != 0;
@@ -142,11 +154,11 @@ __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(Pro
             if constexpr (SWIGLU) u += lds_red[(size_t)(w * PER + NB * 4) * 65 + j0];
         }
         const int64_t n = n0 + n16;
-        if (m >= a.M || n >= a.N) continue;
+        if (m >= M_ || n >= N_) continue;
         if constexpr (SWIGLU) v = (v / (1.0f + __expf(-v))) * u;
-        const size_t oi = (size_t)m * a.N + n;
-        if (a.out_f32) reinterpret_cast<float*>(a.y)[oi] = v;
-        else reinterpret_cast<uint16_t*>(a.y)[oi] = f32_to_bf16_rne(v);
+        const size_t oi = (size_t)m * N_ + n;
+        if (a.out_f32) reinterpret_cast<float*>(y_)[oi] = v;
+        else reinterpret_cast<uint16_t*>(y_)[oi] = f32_to_bf16_rne(v);
     }
 }
 
@@ -162,8 +174,8 @@ inline int mfma_split_spw(int K, bool swiglu)
     return 0;
 }
 
-template <int MT, bool SW, int SPW>
-hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
+template <int MT, bool SW, int SPW, bool SEG>
+hipError_t launch_mfma_split_seg(const ProjArgs& a, hipStream_t s)
 {
     const int nks = (a.K / 32) / SPW;
     const int64_t tiles = ((int64_t)a.N + 15) / 16;
@@ -182,17 +194,26 @@ hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
             const size_t lds = (size_t)nks * (SW ? 2 : 1) * 4 * 65 * 4;
             const int64_t blocks = (tiles + 7) / 8 * 16;
             if constexpr (MT == 32)
-                hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 16>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+                hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 16, SEG>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
             else if (a.M > 8)
-                hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 8>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+                hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 8, SEG>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
             else
-                hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 4>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
+                hipLaunchKernelGGL((mfma_split_kernel<16, SW, SPW, 4, SEG>), dim3((unsigned)blocks), dim3(64 * nks), lds, s, a);
             return hipGetLastError();
         }
     }
     const size_t lds = (size_t)nks * (SW ? 2 : 1) * (MT / 16) * 4 * 65 * 4;
-    hipLaunchKernelGGL((mfma_split_kernel<MT, SW, SPW>), dim3((unsigned)tiles), dim3(64 * nks), lds, s, a);
+    hipLaunchKernelGGL((mfma_split_kernel<MT, SW, SPW, 0, SEG>), dim3((unsigned)tiles), dim3(64 * nks), lds, s, a);
     return hipGetLastError();
+}
+
+template <int MT, bool SW, int SPW>
+hipError_t launch_mfma_split_one(const ProjArgs& a, hipStream_t s)
+{
+    if constexpr (!SW) {
+        if (a.nseg > 1) return launch_mfma_split_seg<MT, SW, SPW, true>(a, s);
+    }
+    return launch_mfma_split_seg<MT, SW, SPW, false>(a, s);
 }
 
 template <int MT, bool SW>

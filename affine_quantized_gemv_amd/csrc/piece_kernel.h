@@ -127,7 +127,11 @@ __host__ __device__ constexpr int waitcnt_lgkm0_only() { return 0xF | 0x70 | (3 
 // clobber keeps the compiler from moving LDS accesses across it).
 __device__ __forceinline__ void piece_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BITS, int MT, bool SWIGLU, bool XREG, int L, int J, int RD = PieceDepth<BITS, J, MT>::RD>
+// SEG: a multi-projection launch (row tiles looked up in the projection
+// table); a separate instantiation, since the per-tile lookup's scalar work
+// inside the stream loop measured ~15% slower on the 4-bit LM head.
+template <int BITS, int MT, bool SWIGLU, bool XREG, int L, int J, bool SEG = false,
+          int RD = PieceDepth<BITS, J, MT>::RD>
 __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
 {
     extern __shared__ uint4 lds_p4[];
@@ -293,19 +297,19 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
     int f_c = 0;                // its index within the super-tile
     __amdgpu_buffer_rsrc_t rw[S], rs[S], rb[S];
     auto set_tile = [&]() __attribute__((always_inline)) {
-        int64_t n0 = f_tile * G;
-        // a multi-projection launch: the projection holding this tile
         const void* w0 = a.w0;
         const uint16_t* sc0 = a.scales;
         const uint16_t* bi0 = a.biases;
+        int64_t n0 = f_tile * G;
         int64_t nrows = a.N;
-        if (a.nseg) {
+        if constexpr (SEG) {
+            // the projection holding this tile: scalar selects, no branch
             const int sg = seg_of(a, n0);
-            w0 = a.seg_w[sg];
-            sc0 = a.seg_scales[sg];
-            bi0 = a.seg_biases[sg];
-            nrows = a.seg_row0[sg + 1] - a.seg_row0[sg];
-            n0 -= a.seg_row0[sg];
+            w0 = seg_pick(a.seg_w, sg);
+            sc0 = seg_pick(a.seg_scales, sg);
+            bi0 = seg_pick(a.seg_biases, sg);
+            nrows = seg_rows(a, sg);
+            n0 -= seg_start(a, sg);
         }
         const int64_t rows = nrows - n0;
 #pragma unroll
@@ -565,11 +569,11 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
             const float val = obuf[v];
             void* y = a.y;
             int64_t nl = n, ny = a.N;
-            if (a.nseg) {                        // the projection holding row n
+            if constexpr (SEG) {                 // the projection holding row n
                 const int sg = seg_of(a, n);
-                y = a.seg_y[sg];
-                nl = n - a.seg_row0[sg];
-                ny = a.seg_row0[sg + 1] - a.seg_row0[sg];
+                y = seg_pick(a.seg_y, sg);
+                nl = n - seg_start(a, sg);
+                ny = seg_rows(a, sg);
             }
             const size_t o = (size_t)m * ny + nl;
             if (a.out_f32) reinterpret_cast<float*>(y)[o] = val;
@@ -593,10 +597,10 @@ size_t piece_lds_bytes(int MT, bool xreg, int L, int J, int K, int64_t tmax)
     return x16 * 16 + out;
 }
 
-template <int BITS, int MT, bool SW, bool XREG, int L, int J>
+template <int BITS, int MT, bool SW, bool XREG, int L, int J, bool SEG>
 hipError_t launch_piece_one(const ProjArgs& a, hipStream_t s)
 {
-    const void* fn = reinterpret_cast<const void*>(&piece_kernel<BITS, MT, SW, XREG, L, J>);
+    const void* fn = reinterpret_cast<const void*>(&piece_kernel<BITS, MT, SW, XREG, L, J, SEG>);
     {
         hipError_t e = raise_lds_limit(fn, kPieceLdsMax);
         if (e != hipSuccess) return e;
@@ -652,7 +656,7 @@ hipError_t launch_piece_one(const ProjArgs& a, hipStream_t s)
     ProjArgs a2 = a;
     a2.tpw = ct;
     a2.tmax = tmax;
-    hipLaunchKernelGGL((piece_kernel<BITS, MT, SW, XREG, L, J>), dim3(blocks), dim3(kPieceThreads), lds, s, a2);
+    hipLaunchKernelGGL((piece_kernel<BITS, MT, SW, XREG, L, J, SEG>), dim3(blocks), dim3(kPieceThreads), lds, s, a2);
     return hipGetLastError();
 }
 
@@ -661,7 +665,10 @@ hipError_t launch_piece_mt(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
     constexpr bool XR = piece_xreg_ok<BITS, MT, J>();
     if ((c.xreg != 0) != XR) return hipErrorInvalidValue;
-    return launch_piece_one<BITS, MT, SW, XR, L, J>(a, s);
+    if constexpr (!SW) {
+        if (a.nseg > 1) return launch_piece_one<BITS, MT, SW, XR, L, J, true>(a, s);
+    }
+    return launch_piece_one<BITS, MT, SW, XR, L, J, false>(a, s);
 }
 
 template <int BITS, bool SW, int L, int J>

@@ -318,6 +318,18 @@ int aqg_unpack_codes(int bits, const uint32_t* Wq, uint8_t* codes, int N, int K,
 int aqg_dispatch_path(int kind, int M, int N, int K, int* columns);
 const char* aqg_path_name(int path);
 
+/*
+ * Measurement probe (launches one kernel, computes nothing): reads bytes
+ * bytes from src (device, 16-byte aligned, bytes >= 16) with the weight
+ * streams' access pattern (16-byte buffer loads, whole 128-byte lines per
+ * instruction, eight 4-wavefront workgroups per CU) and no arithmetic.  Its
+ * time over sizes gives the machine's read ceiling t0 + bytes/BW, the curve
+ * the projections are reported against (the benchmark section of AstrAI
+ * decode_linear_benchmark.md reports estimated effective IO bandwidth).
+ * sink: a float per workgroup (8 per CU), almost never written.
+ */
+int aqg_stream_read(const void* src, size_t bytes, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

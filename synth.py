@@ -54,6 +54,11 @@ AFFINE4_M = [1, 4, 16]
 MIXED_BITS = [2, 3, 4, 5, 6, 8]
 MIXED_SHAPES = [("sq_4096", 4096, 4096), ("wide_14336", 14336, 4096)]
 MIXED_M = [1, 8, 16]
+# fused SwiGLU over affine gate and up matrices: the hidden-1536 MLP and the
+# ~0.8B decoder MLP
+SWIGLU_AFFINE_SHAPES = [("mlp_1536", 4096, 1536), ("mlp_1024", 3584, 1024)]
+SWIGLU_AFFINE_BITS = [2, 3, 4, 5, 6, 8]
+SWIGLU_AFFINE_M = [1, 4, 16, 32]
 
 
 def rng(config_id: int, name: str) -> np.random.Generator:

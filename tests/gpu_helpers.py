@@ -1,6 +1,13 @@
 """Helpers for the GPU parity tests: host<->device transfer of bf16 bit
-patterns, canary-guarded output buffers and the parity checks themselves."""
+patterns, canary-guarded output buffers and the parity checks themselves.
+
+With AQG_PARITY_LOG=FILE every tolerance check appends its diagnostics (max
+abs error, relative L2 error, max err/bound) to FILE as a JSON line;
+`bench.py --summarize-parity FILE` tabulates them."""
 from __future__ import annotations
+
+import json
+import os
 
 import numpy as np
 import torch
@@ -63,6 +70,13 @@ def run_guarded(fn, M: int, N: int):
 
 def assert_within(y: np.ndarray, ref: np.ndarray, bound: np.ndarray, what: str = ""):
     err = np.abs(y - ref)
+    log = os.environ.get("AQG_PARITY_LOG")
+    if log and err.size:
+        rec = {"what": what, "n": int(err.size), "max_abs": float(err.max()),
+               "rel_l2": float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300)),
+               "max_err_over_bound": float((err / bound).max())}
+        with open(log, "a") as f:
+            f.write(json.dumps(rec) + "\n")
     bad = ~(err <= bound)
     if bad.any():
         i = np.argwhere(bad)[0]

@@ -40,7 +40,8 @@ def test_header_declares_expected_entry_points():
                {"aqg_gemv_affine_q%d" % b for b in range(2, 9)} | \
                {"aqg_gemv_affine_q%d_argmax" % b for b in range(2, 9)} | \
                {"aqg_swiglu_affine_q%d" % b for b in range(2, 9)} | \
-               {"aqg_gemv_bf16_multi"} | {"aqg_gemv_affine_q%d_multi" % b for b in range(2, 9)}
+               {"aqg_gemv_bf16_multi"} | {"aqg_gemv_affine_q%d_multi" % b for b in range(2, 9)} | \
+               {"aqg_stream_read"}
     assert set(names) == expected
 
 

@@ -21,8 +21,8 @@ from gpu_helpers import assert_within, bf16_dev, run_guarded, u32_dev
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [("mlp_1536", 4096, 1536), ("mlp_1024", 3584, 1024)]
-BITS = [2, 3, 4, 5, 6, 8]
+SHAPES = synth.SWIGLU_AFFINE_SHAPES
+BITS = synth.SWIGLU_AFFINE_BITS
 MS = [1, 2, 4, 8, 16, 32]
 
 
