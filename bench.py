@@ -270,6 +270,42 @@ def other_calls():
     del w
 
 
+def make_call(label):
+    """The call a label names (see label_of), with seeded synthetic inputs of
+    its shape and two weight copies: for counter runs, which need only the
+    kernel's own behaviour, not the full set of configurations."""
+    import synth
+    parts = label.split()
+    bits = 0
+    if parts[0].startswith("q") and parts[0][1:].isdigit():
+        bits = int(parts[0][1:])
+        parts = parts[1:]
+    kind, name = parts[0], parts[1]
+    M = int(parts[2].split("=")[1])
+    N, K = (int(v) for v in parts[3].split("x"))
+    cfg = 9
+    x = dev_bf16(synth.normal_bf16((32, K), 1.0, cfg, "cc/x/%d" % K))
+
+    def affine_w(tag, n):
+        aw = synth.affine_weight(cfg, tag, bits, n, K)
+        return [dev_u32(aw.words), dev_bf16(aw.scales), dev_bf16(aw.biases)]
+
+    def dense_w(tag, n):
+        return [dev_bf16(synth.normal_bf16((n, K), 0.02, cfg, "cc/W/%s/%dx%d" % (tag, n, K)))]
+    parts_n = None
+    if kind == "multi":
+        parts_n = [N // 3] * 3
+        ts = []
+        for i, n in enumerate(parts_n):
+            ts += affine_w("m%d" % i, n) if bits else dense_w("m%d" % i, n)
+    elif kind in ("swiglu", "swiglu_affine"):
+        ts = (affine_w("g", N) + affine_w("u", N)) if bits else (dense_w("g", N) + dense_w("u", N))
+    else:
+        ts = affine_w(name, N) if bits else dense_w(name, N)
+    w = Weights(ts, 1, copies=2)
+    return Call("counters", name, kind, M, N, K, x, w, bits=bits, parts=parts_n)
+
+
 # ------------------------------------------------------------------ timing
 
 def time_call(call, n, reps=5):
@@ -700,14 +736,10 @@ def main():
         copy_probe(args.copy_probe)
         return 0
     if args.counter_call:
-        calls = [c for c in dense_decode_calls() if label_of(c) == args.counter_call]
-        if not calls:
-            for c in other_calls():
-                if label_of(c) == args.counter_call:
-                    calls = [c]
-                    break
-        if not calls:
-            print("no call is labelled %r" % args.counter_call, file=sys.stderr)
+        try:
+            calls = [make_call(args.counter_call)]
+        except (ValueError, IndexError):
+            print("not a call label: %r" % args.counter_call, file=sys.stderr)
             return 2
         for _ in range(8):
             calls[0]()
