@@ -614,15 +614,30 @@ def summarize_counters(d, labels):
              "busy % waiting | LDS bank conflicts / KiB |", "|---|---|---|---|---|---|---|---|"]
     for label in labels:
         name = slug(label)
-        vals = {}
-        kern = None
+        # a call may run several kernels (the row argmax: the GEMV, then the
+        # reduction of its partials): bytes are summed over them, the other
+        # counters are those of the kernel that moves the most bytes
+        per = {}
         for ctr in ("FETCH_SIZE", "WRITE_SIZE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_WAVES", "SQ_WAVE_CYCLES",
                     "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE",
                     "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES"):
-            rs = [r for r in rows(ctr, name) if "aqg" in r["Kernel_Name"]]
-            if rs:
-                kern = rs[0]["Kernel_Name"].replace("void aqg::detail::", "").replace("(aqg::ProjArgs)", "")
-                vals[ctr] = statistics.fmean(float(r["Counter_Value"]) for r in rs)
+            by_kernel = {}
+            for r in rows(ctr, name):
+                if "aqg" in r["Kernel_Name"]:
+                    by_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            for kname, v in by_kernel.items():
+                per.setdefault(kname, {})[ctr] = statistics.fmean(v)
+        kern = None
+        vals = {}
+        if per:
+            main = max(per, key=lambda k: per[k].get("FETCH_SIZE", 0.0))
+            kern = main.replace("void aqg::detail::", "").replace("(aqg::ProjArgs)", "")
+            if len(per) > 1:
+                kern += " (+ %d more)" % (len(per) - 1)
+            vals = dict(per[main])
+            for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                if all(ctr in v for v in per.values()):
+                    vals[ctr] = sum(v[ctr] for v in per.values())
         alg = label_bytes(label)
         kib = alg / 1024.0
         rec = {"kernel": kern, "algorithmic_bytes_per_launch": alg, "raw": {k: round(v, 1) for k, v in vals.items()}}
@@ -634,7 +649,9 @@ def summarize_counters(d, labels):
 
         def f(v, fmt="%.1f"):
             return fmt % v if v is not None else "-"
-        waves_cu = vals.get("SQ_WAVE_CYCLES", 0) / max(vals.get("GRBM_GUI_ACTIVE", 0), 1) / 256 \
+        # SQ_WAVE_CYCLES counts in units of 4 cycles; GRBM_GUI_ACTIVE is the
+        # sum over the 8 XCDs of each one's busy cycles
+        waves_cu = 4 * vals["SQ_WAVE_CYCLES"] / max(vals["GRBM_GUI_ACTIVE"] / 8, 1) / 256 \
             if "SQ_WAVE_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals else None
         wait = 100 * vals["SQ_WAIT_INST_ANY"] / vals["SQ_WAVE_CYCLES"] \
             if "SQ_WAIT_INST_ANY" in vals and vals.get("SQ_WAVE_CYCLES") else None
