@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "lib_path", "load", "AqgError", "abi_version", "status_string", "workspace_bytes", "dispatch_path",
     "gemv_bf16", "gemv_affine", "swiglu_bf16", "swiglu_affine", "unpack_codes", "gemv_bf16_argmax",
-    "gemv_affine_argmax", "gemv_bf16_multi", "gemv_affine_multi",
+    "gemv_affine_argmax", "gemv_bf16_multi", "gemv_affine_multi", "gemm_affine",
     "gemv_affine_q2", "gemv_affine_q3", "gemv_affine_q4", "gemv_affine_q5",
     "gemv_affine_q6", "gemv_affine_q7", "gemv_affine_q8",
     "AQG_OK", "AQG_ERR_INVALID_ARG", "AQG_ERR_UNSUPPORTED", "AQG_ERR_ALIGNMENT",
@@ -33,6 +33,8 @@ __all__ = [
 AQG_OK, AQG_ERR_INVALID_ARG, AQG_ERR_UNSUPPORTED, AQG_ERR_ALIGNMENT, AQG_ERR_LAUNCH, AQG_ERR_DEVICE = range(6)
 AQG_OUT_BF16, AQG_OUT_F32 = 0, 1
 AQG_KIND_DENSE, AQG_KIND_SWIGLU, AQG_KIND_SWIGLU_AFFINE, AQG_KIND_ARGMAX_DENSE = 0, 9, 16, 32
+AQG_KIND_GEMM_AFFINE = 48      # + bits: affine prompt GEMM (any M)
+GEMM_MAX_M = 65536             # AQG_GEMM_MAX_M
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -94,6 +96,10 @@ def load():
             f = getattr(lib, "aqg_gemv_affine_q%d_argmax" % b)
             f.restype = I
             f.argtypes = [P, P, P, P, P, P, I, I, I, P, Z, P]
+        for b in range(2, 9):
+            f = getattr(lib, "aqg_gemm_affine_q%d" % b)
+            f.restype = I
+            f.argtypes = [P, P, P, P, P, I, I, I, I, P, Z, P]
         lib.aqg_gemv_argmax_noalloc.restype = I
         lib.aqg_gemv_argmax_noalloc.argtypes = [I, P, P, P, P, P, P, I, I, I, P]
         lib.aqg_stream_read.restype = I
@@ -349,6 +355,28 @@ def _argmax_ws(kind: int, M: int, N: int, K: int, like: torch.Tensor, workspace)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace needs %d bytes" % need)
     return workspace
+
+
+def gemm_affine(x: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+                bits: int, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """Affine b-bit prompt GEMM: the product of gemv_affine for any M (up to
+    GEMM_MAX_M rows of x).  workspace: a device tensor of at least
+    workspace_bytes(AQG_KIND_GEMM_AFFINE + bits, M, N, K) bytes (allocated
+    here when None)."""
+    if bits not in range(2, 9):
+        raise ValueError("bits must be in 2..8")
+    _dev(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    if K % 64:
+        raise ValueError("K must be a multiple of 64")
+    N = Wq.shape[0]
+    _affine_check(Wq, scales, biases, bits, N, K, "W")
+    y = _out(out, M, N, out_dtype, x)
+    ws = _argmax_ws(AQG_KIND_GEMM_AFFINE + bits, M, N, K, x, workspace)
+    fn = getattr(load(), "aqg_gemm_affine_q%d" % bits)
+    _check(fn(_p(x), _p(Wq), _p(scales), _p(biases), _p(y), M, N, K, _odt(y), _p(ws),
+              ws.numel() * ws.element_size(), _stream(x)), "aqg_gemm_affine_q%d" % bits)
+    return y
 
 
 def gemv_bf16_argmax(x: torch.Tensor, W: torch.Tensor, out=None, workspace=None):

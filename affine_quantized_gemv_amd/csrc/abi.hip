@@ -137,6 +137,64 @@ int run_affine(int bits, const void* x, const uint32_t* Wq, const void* scales, 
                           ws, wsb, stream);
 }
 
+// ------------------------------------------------ prompt GEMM
+
+hipError_t launch_gemm_bits(int bits, const aqg::GemmArgs& a, hipStream_t s)
+{
+    switch (bits) {
+        case 2: return aqg::launch_affine_gemm<2>(a, s);
+        case 3: return aqg::launch_affine_gemm<3>(a, s);
+        case 4: return aqg::launch_affine_gemm<4>(a, s);
+        case 5: return aqg::launch_affine_gemm<5>(a, s);
+        case 6: return aqg::launch_affine_gemm<6>(a, s);
+        case 7: return aqg::launch_affine_gemm<7>(a, s);
+        case 8: return aqg::launch_affine_gemm<8>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+int run_gemm(int bits, const void* x, const uint32_t* Wq, const void* scales, const void* biases, void* y,
+             int M, int N, int K, int out_dtype, void* ws, size_t wsb, void* stream)
+{
+    if (!x || !y || !Wq || !scales || !biases) return AQG_ERR_INVALID_ARG;
+    if (M <= 0 || N <= 0 || K <= 0) return AQG_ERR_INVALID_ARG;
+    if (out_dtype != AQG_OUT_BF16 && out_dtype != AQG_OUT_F32) return AQG_ERR_INVALID_ARG;
+    if (M > AQG_GEMM_MAX_M || K % 64 != 0) return AQG_ERR_UNSUPPORTED;
+    const size_t need = aqg::gemm_workspace_bytes(bits, M, K);
+    if (!ws || wsb < need) return AQG_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(Wq, 16) || !aligned(ws, 16)) return AQG_ERR_ALIGNMENT;
+    if (!aligned(scales, 4) || !aligned(biases, 4)) return AQG_ERR_ALIGNMENT;
+    if (!aligned(y, out_dtype == AQG_OUT_F32 ? 4 : 2)) return AQG_ERR_ALIGNMENT;
+    const size_t ybytes = out_bytes(M, N, out_dtype);
+    const size_t xbytes = (size_t)M * K * 2;
+    const size_t wbytes = (size_t)N * K / 8 * bits;
+    const size_t gbytes = (size_t)N * (K / 64) * 2;
+    const void* in[4] = {x, Wq, scales, biases};
+    const size_t inb[4] = {xbytes, wbytes, gbytes, gbytes};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(y, ybytes, in[i], inb[i]) || overlap(ws, need, in[i], inb[i])) return AQG_ERR_INVALID_ARG;
+    if (overlap(ws, need, y, ybytes)) return AQG_ERR_INVALID_ARG;
+    int st = check_device();
+    if (st != AQG_OK) return st;
+
+    aqg::GemmArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.wq = Wq;
+    a.scales = static_cast<const uint16_t*>(scales);
+    a.biases = static_cast<const uint16_t*>(biases);
+    a.y = y;
+    a.xp = static_cast<uint16_t*>(ws);
+    a.pieces = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + aqg::gemm_pieces_offset(M, K));
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.G = K / 64;
+    a.Gp = (a.G + 31) / 32 * 32;
+    a.Mp = (M + aqg::kGemmTileM - 1) / aqg::kGemmTileM * aqg::kGemmTileM;
+    a.out_f32 = out_dtype == AQG_OUT_F32;
+    return finish(launch_gemm_bits(bits, a, static_cast<hipStream_t>(stream)));
+}
+
 // ------------------------------------------------ multi-projection launch
 
 // The kernels that take a segment table (several projections of one x in
@@ -386,8 +444,9 @@ const char* aqg_status_string(int status)
         case AQG_OK: return "AQG_OK: success";
         case AQG_ERR_INVALID_ARG: return "AQG_ERR_INVALID_ARG: null pointer, non-positive size, bad out_dtype, "
                                          "short workspace or overlapping output";
-        case AQG_ERR_UNSUPPORTED: return "AQG_ERR_UNSUPPORTED: M > 32, K not a multiple of 8 (dense) or 64 "
-                                         "(affine), or bits outside 2..8";
+        case AQG_ERR_UNSUPPORTED: return "AQG_ERR_UNSUPPORTED: M > 32 (M > AQG_GEMM_MAX_M for the prompt "
+                                         "GEMMs), K not a multiple of 8 (dense) or 64 (affine), or bits "
+                                         "outside 2..8";
         case AQG_ERR_ALIGNMENT: return "AQG_ERR_ALIGNMENT: x and W/Wq must be 16-byte aligned, scales and "
                                        "biases 4-byte aligned, other arrays aligned to their element size";
         case AQG_ERR_LAUNCH: return "AQG_ERR_LAUNCH: the kernel launch failed";
@@ -398,7 +457,10 @@ const char* aqg_status_string(int status)
 
 size_t aqg_workspace_bytes(int kind, int M, int N, int K)
 {
-    if (M <= 0 || N <= 0 || K <= 0 || M > 32) return 0;
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    if (kind >= AQG_KIND_GEMM_AFFINE + 2 && kind <= AQG_KIND_GEMM_AFFINE + 8)
+        return M > AQG_GEMM_MAX_M || K % 64 != 0 ? 0 : aqg::gemm_workspace_bytes(kind - AQG_KIND_GEMM_AFFINE, M, K);
+    if (M > 32) return 0;
     if (kind == AQG_KIND_ARGMAX_DENSE || (kind >= AQG_KIND_ARGMAX_DENSE + 2 && kind <= AQG_KIND_ARGMAX_DENSE + 8))
         return argmax_plan(kind - AQG_KIND_ARGMAX_DENSE, M, N, K).bytes;
     return 0;  // the GEMVs and SwiGLUs keep their partial sums in registers and LDS
@@ -516,9 +578,31 @@ AQG_AFFINE_ENTRY(7)
 AQG_AFFINE_ENTRY(8)
 #undef AQG_AFFINE_ENTRY
 
+#define AQG_GEMM_ENTRY(B)                                                                            \
+    int aqg_gemm_affine_q##B(const void* x, const uint32_t* Wq, const void* scales, const void* biases, \
+                             void* y, int M, int N, int K, int out_dtype, void* workspace,          \
+                             size_t workspace_bytes, void* stream)                                  \
+    {                                                                                                \
+        return run_gemm(B, x, Wq, scales, biases, y, M, N, K, out_dtype, workspace, workspace_bytes, \
+                        stream);                                                                     \
+    }
+AQG_GEMM_ENTRY(2)
+AQG_GEMM_ENTRY(3)
+AQG_GEMM_ENTRY(4)
+AQG_GEMM_ENTRY(5)
+AQG_GEMM_ENTRY(6)
+AQG_GEMM_ENTRY(7)
+AQG_GEMM_ENTRY(8)
+#undef AQG_GEMM_ENTRY
+
 int aqg_dispatch_path(int kind, int M, int N, int K, int* columns)
 {
     if (M <= 0 || N <= 0 || K <= 0) return -AQG_ERR_INVALID_ARG;
+    if (kind >= AQG_KIND_GEMM_AFFINE + 2 && kind <= AQG_KIND_GEMM_AFFINE + 8) {
+        if (M > AQG_GEMM_MAX_M || K % 64 != 0) return -AQG_ERR_UNSUPPORTED;
+        if (columns) *columns = aqg::kGemmTileM;
+        return aqg::PATH_AFFINE_GEMM;
+    }
     const bool swiglu_affine = kind >= AQG_KIND_SWIGLU_AFFINE + 2 && kind <= AQG_KIND_SWIGLU_AFFINE + 8;
     const bool swiglu = kind == AQG_KIND_SWIGLU || swiglu_affine;
     const int bits = swiglu_affine ? kind - AQG_KIND_SWIGLU_AFFINE : (swiglu ? 0 : kind);
@@ -544,6 +628,7 @@ const char* aqg_path_name(int path)
         case aqg::PATH_MFMA_TILE: return "mfma_tile";
         case aqg::PATH_AFFINE_TILE: return "affine_tile";
         case aqg::PATH_AFFINE_SPLIT: return "affine_split";
+        case aqg::PATH_AFFINE_GEMM: return "affine_gemm";
         default: return "unknown";
     }
 }

@@ -1,0 +1,555 @@
+// Matrix-core GEMM for affine codes of 2 to 8 bits at any M (prompt chunks:
+// M > 32 rows of activations), on gfx950.
+//
+//   y[m, n] = sum_k x[m, k] (s[n, g] q[n, k] + b[n, g]),   g = k / 64
+//
+// in the factored form sum_g s[n,g] D[m,n,g] + sum_g (b[n,g] X[m,g] -
+// s[n,g] D0[m,g]) with X the group sums of x, evaluated in fp32:
+//
+//   * D is the group's dot product of x with the codes as the matrix core
+//     computes it (v_mfma_f32_16x16x32_bf16, two k-steps per group).  For 2
+//     to 7 bits a code goes into a bf16 mantissa as 128 + q (mask placement,
+//     no lookup, as in the decode kernels); 8-bit codes are converted to bf16
+//     exactly (every integer up to 256 is a bf16), so D carries no offset.
+//   * D0 is that offset, 128 X, as the matrix core computes it for all-zero
+//     codes (the same two MFMAs on the same x operands), so a group of zero
+//     codes gives D == D0 bit for bit.  No offset for 8 bits.
+//   * Per group and output the wavefront adds s D into its fp32 tile: one FMA.
+//   * The code-independent terms sum_g b X and - sum_g s D0 are a contraction
+//     over the groups that the matrix core does once per tile, 32 groups per
+//     MFMA: A = the rows' biases (bf16, exact) or negated scales, B = X or D0
+//     split into three bf16 pieces (hi, mid, lo: X = hi + mid + lo exactly for
+//     a normal fp32 X), products exact in fp32.
+//
+// A pre-pass over x (gemm_prep_kernel) writes, into the caller's workspace,
+// the x^T B operands of every (16-row block, group, k-step) in the width's k
+// order (1 KB each, laid out exactly as the main kernel keeps them in LDS)
+// and the six pieces per (row, group).
+//
+// Main kernel (affine_gemm_kernel): a workgroup of 8 wavefronts owns a tile
+// of 64 WN rows of W by 64 rows of x and walks K in stages of one group;
+// with WK > 1 the K range is split into WK chunks, one per wavefront slice.
+// Wavefront (wn, kc) owns rows 64 wn .. + 63 of the tile and chunk kc: a
+// 64 x 64 output tile = 4 x 4 MFMA tiles of 16 x 16.  Each stage is copied
+// straight into LDS by buffer loads with an LDS destination, spread evenly
+// over the wavefronts: the chunks' code bytes of the tile's rows (16 bytes
+// per lane for even widths, 4 for odd ones), the x operands (1 KB per
+// instruction) and the scales (one dword per row holding the group's bf16
+// scale).  NBUF stage buffers form a ring; copies run NBUF - 1 stages ahead
+// of the arithmetic, with one barrier per stage and explicit waits that
+// leave exactly the younger stages' copies in flight.  Per stage a
+// wavefront turns its 64 rows' scales to fp32 through a private LDS table,
+// reads its 8 x operands, and per 16-row block its lanes' code windows
+// (lane quarter c: codes 16c .. 16c + 15 of the group), builds the two A
+// operands, runs 8 MFMAs and 16 FMAs.  The chunk partials of a tile are
+// summed through LDS in chunk order (fixed: no result depends on M or on
+// the other rows), then stored as fp32 or RNE bf16.
+//
+// Format: TensorFold PR #849, "qwen3_5 cuda: mixed-width MLX checkpoints, 2
+// to 8 bits in groups of 64" (MLX affine mode, groups of 64); the same page
+// notes that its 8-bit modules have no prompt GEMM and run prompt chunks on
+// the decode tiles, 16 rows at a time.
+#pragma once
+
+#include "affine_tile.h"
+#include "host_query.h"
+#include "kernels.h"
+
+namespace aqg {
+
+namespace detail {
+
+constexpr int kGemmWaves = 8;   // wavefronts per workgroup
+
+// ------------------------------------------------------------ k orders
+
+// Element e (0..15) of a lane's 16-value x window held as 8 bf16 pairs.
+template <int E>
+__device__ __forceinline__ uint32_t win_elem(const uint32_t (&v)[8])
+{
+    return (E & 1) ? (v[E >> 1] >> 16) : (v[E >> 1] & 0xFFFFu);
+}
+
+// x^T operand of k-step H from a lane's window (x at 16c .. 16c + 15 of the
+// group), in the k order of the width's A operands:
+//   2 bits: 4H + {0, 8, 1, 9, 2, 10, 3, 11}   (codes2_to_bf16)
+//   4 bits: 8H + {0, 4, 1, 5, 2, 6, 3, 7}     (codes4_to_bf16)
+//   other widths: 8H + {0 .. 7}, natural
+template <int BITS, int H>
+__device__ __forceinline__ u32x4_t gemm_x_operand(const uint32_t (&v)[8])
+{
+    u32x4_t o;
+    static_for<0, 4>([&](auto Tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(Tc)::value;
+        if constexpr (BITS == 2) {
+            o[t] = win_elem<4 * H + t>(v) | (win_elem<4 * H + t + 8>(v) << 16);
+        } else if constexpr (BITS == 4) {
+            o[t] = win_elem<8 * H + t>(v) | (win_elem<8 * H + t + 4>(v) << 16);
+        } else {
+            o[t] = v[4 * H + t];
+        }
+    });
+    return o;
+}
+
+// Eight 8-bit codes (dwords a, b; byte i = code i) as exact bf16 pairs in
+// natural order (q0, q1), (q2, q3), (b0, b1), (b2, b3).
+__device__ __forceinline__ u32x4_t codes8_exact_bf16(uint32_t a, uint32_t b)
+{
+    auto pair = [](uint32_t w, int sh) __attribute__((always_inline)) {
+        const float lo = (float)((w >> sh) & 0xFFu);
+        const float hi = (float)((w >> (sh + 8)) & 0xFFu);
+        return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    };
+    return u32x4_t{pair(a, 0), pair(a, 16), pair(b, 0), pair(b, 16)};
+}
+
+// ------------------------------------------------------------ pre-pass
+
+// Truncation of an fp32 to its top 8 significant bits (a bf16 value).
+__device__ __forceinline__ float bf16_trunc(float f) { return __uint_as_float(__float_as_uint(f) & 0xFFFF0000u); }
+
+// One wavefront per (16-row block mt of x, group g < Gp): lane (c, r) takes
+// row 16 mt + r and x[64 g + 16 c .. + 15].  Writes the two x operands of
+// the group (g < G), and with c == 0 the six (three) pieces of (row, g);
+// rows past M and groups past G give zeros.
+template <int BITS>
+__global__ void __launch_bounds__(256) gemm_prep_kernel(GemmArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int c = lane >> 4, r = lane & 15;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t units = (int64_t)(a.Mp / 16) * a.Gp;
+    if (w >= units) return;   // wave-uniform
+    const int mt = (int)(w / a.Gp), g = (int)(w % a.Gp);
+    const int m = 16 * mt + r;
+    const bool have = m < a.M && g < a.G;
+
+    uint32_t v[8];
+    if (have) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + 64 * g + 16 * c);
+        const uint4 p = src[0], q = src[1];
+        v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+        v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0u;
+    }
+    const u32x4_t b0 = gemm_x_operand<BITS, 0>(v);
+    const u32x4_t b1 = gemm_x_operand<BITS, 1>(v);
+    if (g < a.G) {
+        uint4* dst = reinterpret_cast<uint4*>(a.xp) + (((int64_t)mt * a.G + g) * 2) * 64 + lane;
+        dst[0] = make_uint4(b0[0], b0[1], b0[2], b0[3]);
+        dst[64] = make_uint4(b1[0], b1[1], b1[2], b1[3]);
+    }
+
+    // X: the window summed in a fixed order, then over the lane quarters
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = bf16_to_f32(v[i] & 0xFFFFu) + bf16_to_f32(v[i] >> 16);
+    float part = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+    const float p16 = __shfl_xor(part, 16);
+    const float h = (c & 1) ? p16 + part : part + p16;
+    const float h32 = __shfl_xor(h, 32);
+    const float X = (c & 2) ? h32 + h : h + h32;
+
+    float vals[6];
+    vals[0] = bf16_trunc(X);
+    const float rx = X - vals[0];
+    vals[1] = bf16_trunc(rx);
+    vals[2] = rx - vals[1];
+    if constexpr (BITS != 8) {
+        const u32x4_t Z = u32x4_t{kZeroCodePair, kZeroCodePair, kZeroCodePair, kZeroCodePair};
+        f32x4_t d = mfma16x16x32(Z, b0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        d = mfma16x16x32(Z, b1, d);
+        const float D0 = d[0];   // every row of the all-128 A operand is the same
+        vals[3] = bf16_trunc(D0);
+        const float rd = D0 - vals[3];
+        vals[4] = bf16_trunc(rd);
+        vals[5] = rd - vals[4];
+    }
+    if (c == 0) {
+#pragma unroll
+        for (int p = 0; p < gemm_pieces(BITS); ++p)
+            a.pieces[((int64_t)p * a.Mp + m) * a.Gp + g] = f32_to_bf16_rne(vals[p]);
+    }
+}
+
+// ------------------------------------------------------------ main kernel
+
+template <int BITS, int WN, int WK, int NBUF>
+struct GemmLayout {
+    static constexpr int NW = WN * WK;                    // wavefronts
+    static constexpr int MB = kGemmTileM / 16;            // 16-column blocks of a tile
+    static constexpr int ROWS = 64 * WN;                  // rows of W per tile
+    static constexpr int GB = 8 * BITS;                   // code bytes per row and group
+    static constexpr int CB = (GB % 16 == 0) ? 16 : 4;    // bytes per lane of a code copy
+    static constexpr int CODE = WK * ROWS * GB;           // LDS bytes of codes per stage
+    static constexpr int CODE_CPW = CODE / (64 * CB) / NW;   // code copies per wavefront per stage
+    static constexpr int XOP = WK * MB * 2 * 1024;        // x operand bytes per stage
+    static constexpr int XOP_CPW = XOP / 1024 / NW;       // 1 KB copies per wavefront per stage
+    static constexpr int SCL = WK * ROWS * 4;             // scale dwords per stage
+    static constexpr int STAGE = CODE + XOP + SCL;
+    static constexpr int CPS = CODE_CPW + XOP_CPW + 1;    // copies per wavefront per stage
+    static constexpr int TAB = NW * 64 * 4;               // per-wavefront fp32 scale tables
+    static constexpr int RED = (WK - 1) * WN * 64 * 64 * 4;   // chunk partials (over the ring)
+    static constexpr int RING = NBUF * STAGE > RED ? NBUF * STAGE : RED;
+    static constexpr size_t LDS = (size_t)RING + TAB;
+    static_assert(NW == kGemmWaves, "eight wavefronts per workgroup");
+    static_assert(CODE % (64 * CB * NW) == 0, "code copies split evenly over the wavefronts");
+    static_assert(XOP % (1024 * NW) == 0, "x copies split evenly over the wavefronts");
+    static_assert(SCL == NW * 256, "one scale copy per wavefront");
+    static_assert(NBUF >= 2 && (NBUF - 2) * CPS <= 63, "vmcnt counts at most 63");
+    static_assert(LDS <= 160 * 1024, "LDS of one CU");
+};
+
+// Code window of lane quarter c (codes 16c .. 16c + 15 of a group) from the
+// row's group bytes in LDS, as the A operands of the group's two k-steps.
+// m = field mask, mh = m << 16, cb = 0x43004300, opaque registers.
+template <int BITS>
+__device__ __forceinline__ void gemm_a_operands(const char* rowp, int c, uint32_t m, uint32_t mh, uint32_t cb,
+                                                u32x4_t& a0, u32x4_t& a1)
+{
+    if constexpr (BITS == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(rowp + 4 * c);
+        a0 = codes2_to_bf16(w, 0, m, cb);
+        a1 = codes2_to_bf16(w, 1, m, cb);
+    } else if constexpr (BITS == 4) {
+        const uint2 w = *reinterpret_cast<const uint2*>(rowp + 8 * c);
+        a0 = codes4_to_bf16(w.x, m, cb);
+        a1 = codes4_to_bf16(w.y, m, cb);
+    } else if constexpr (BITS == 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(rowp + 16 * c);
+        a0 = codes8_exact_bf16(w.x, w.y);
+        a1 = codes8_exact_bf16(w.z, w.w);
+    } else {
+        using WD = AffineTileWidth<BITS>;
+        constexpr int NWN = WD::NWN;
+        const int bit0 = 16 * BITS * c;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(rowp) + (bit0 >> 5);
+        const uint32_t sh = (uint32_t)(bit0 & 31);   // 0 or 16
+        uint32_t raw[NWN], wn[NWN];
+#pragma unroll
+        for (int i = 0; i < NWN; ++i) raw[i] = src[i];
+#pragma unroll
+        for (int i = 0; i + 1 < NWN; ++i) wn[i] = __builtin_amdgcn_alignbit(raw[i + 1], raw[i], sh);
+        wn[NWN - 1] = raw[NWN - 1] >> sh;   // only its low 16 bits belong to the window when sh = 16
+        a0 = codes_window_to_bf16<BITS, 0>(wn, m, mh, cb);
+        a1 = codes_window_to_bf16<BITS, 1>(wn, m, mh, cb);
+    }
+}
+
+// Eight consecutive bf16 of a row of an [N][G] array, groups g0 .. g0 + 7,
+// zero past the row's end (G) or for a row past N.  even: G is even (dword
+// loads are aligned).
+__device__ __forceinline__ u32x4_t load8_groups(const uint16_t* arr, int64_t n, int N, int G, int g0, bool even)
+{
+    u32x4_t o = u32x4_t{0u, 0u, 0u, 0u};
+    if (n >= N || g0 >= G) return o;
+    const uint16_t* p = arr + n * G + g0;
+    if (even && g0 + 8 <= G) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+        o = u32x4_t{q[0], q[1], q[2], q[3]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = g0 + i < G ? (uint32_t)p[i] : 0u;
+            o[i >> 1] |= (i & 1) ? (v << 16) : v;
+        }
+    }
+    return o;
+}
+
+template <int BITS, int WN, int WK, int NBUF>
+__global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a)
+{
+    using L = GemmLayout<BITS, WN, WK, NBUF>;
+    constexpr int MB = L::MB;
+    constexpr int NP = gemm_pieces(BITS);
+    extern __shared__ __attribute__((aligned(16))) char gemm_lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane >> 4, r = lane & 15;
+    const int wn = wave % WN, kc = wave / WN;
+
+    // tile of this workgroup: consecutive tiles (same rows of W, successive
+    // 64-row blocks of x) go to the workgroups of one XCD
+    const int TM = a.Mp / kGemmTileM;
+    const int64_t T = (((int64_t)a.N + L::ROWS - 1) / L::ROWS) * TM;
+    const int64_t bid = blockIdx.x;
+    const int64_t tile = (gridDim.x % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    const int64_t n0 = (tile / TM) * L::ROWS;
+    const int m0 = (int)(tile % TM) * kGemmTileM;
+    const int GC = a.G / WK;            // groups (stages) per chunk
+    const int64_t row_bytes = (int64_t)a.K * BITS / 8;
+    const int64_t rows_here = (int64_t)a.N - n0 < L::ROWS ? (int64_t)a.N - n0 : L::ROWS;
+
+    const u32x4v_t rw = buffer_words(reinterpret_cast<const char*>(a.wq) + n0 * row_bytes, rows_here * row_bytes);
+    const int64_t xp0 = (int64_t)(m0 / 16) * a.G * 2048;   // bytes
+    const u32x4v_t rx = buffer_words(reinterpret_cast<const char*>(a.xp) + xp0, (int64_t)MB * a.G * 2048);
+    const u32x4v_t rs = buffer_words(a.scales + n0 * a.G, (rows_here * a.G * 2 + 3) & ~(int64_t)3);
+
+    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)gemm_lds;
+
+    // this wavefront's copies of a stage (the same for every stage but for
+    // the group offset): code copy j covers LDS bytes [j 64 CB, (j+1) 64 CB)
+    // of the stage's [WK][ROWS][GB] codes
+    uint32_t code_voff[L::CODE_CPW];
+#pragma unroll
+    for (int q = 0; q < L::CODE_CPW; ++q) {
+        const int f = (wave * L::CODE_CPW + q) * 64 * L::CB + lane * L::CB;
+        const int ck = f / (L::ROWS * L::GB);
+        const int rem = f % (L::ROWS * L::GB);
+        const int row = rem / L::GB, off = rem % L::GB;
+        code_voff[q] = (uint32_t)(row * row_bytes + (int64_t)ck * a.G / WK * L::GB + off);
+    }
+    // scales: wavefront (wn, kc) copies the dwords of its own rows and chunk
+    const int64_t my_row = n0 + 64 * wn + lane;   // row of this lane's scale copy
+    const int64_t srow = my_row - n0;
+
+    auto issue = [&](int i, int buf) __attribute__((always_inline)) {
+        const uint32_t base = lds0 + (uint32_t)buf * L::STAGE;
+#pragma unroll
+        for (int q = 0; q < L::CODE_CPW; ++q) {
+            const uint32_t dst = base + (uint32_t)((wave * L::CODE_CPW + q) * 64 * L::CB);
+            if constexpr (L::CB == 16) copy_1k_to_lds(rw, dst, code_voff[q], (uint32_t)(i * L::GB));
+            else copy_dword_to_lds(rw, dst, code_voff[q], (uint32_t)(i * L::GB));
+        }
+#pragma unroll
+        for (int q = 0; q < L::XOP_CPW; ++q) {
+            const int j = wave * L::XOP_CPW + q;          // [chunk][mb][H]
+            const int ck = j / (MB * 2), mb = (j / 2) % MB, hh = j % 2;
+            const uint32_t dst = base + L::CODE + (uint32_t)j * 1024;
+            const uint32_t soff = (uint32_t)(((mb * a.G + ck * GC + i) * 2 + hh) * 1024);
+            copy_1k_to_lds(rx, dst, (uint32_t)lane * 16, soff);
+        }
+        {
+            const uint32_t dst = base + L::CODE + L::XOP + (uint32_t)wave * 256;
+            const uint32_t voff = (uint32_t)(((srow * a.G + kc * GC + i) * 2) & ~(int64_t)3);
+            copy_dword_to_lds(rs, dst, voff, 0u);
+        }
+    };
+
+    f32x4_t acc[4][MB];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[t][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint32_t cmask = BITS == 2 ? 0x00030003u : BITS == 4 ? 0x000F000Fu : AffineTileWidth<BITS>::MASK;
+    uint32_t cmaskh = AffineTileWidth<BITS>::MASK << 16, cbias = kZeroCodePair;
+    asm volatile("" : "+s"(cmask));      // no instruction: only hides the constants
+    asm volatile("" : "+s"(cmaskh));
+    asm volatile("" : "+v"(cbias));
+
+    float* tab = reinterpret_cast<float*>(gemm_lds + L::RING) + wave * 64;
+
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i)
+        if (i < GC) issue(i, i);
+
+    for (int i = 0; i < GC; ++i) {
+        if (i + NBUF - 2 < GC) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NBUF - 2) * L::CPS));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        barrier_only();   // stage i is in LDS; every wavefront is done with stage i - 1
+        if (i + NBUF - 1 < GC) issue(i + NBUF - 1, (i + NBUF - 1) % NBUF);
+
+        const char* st = gemm_lds + (i % NBUF) * L::STAGE;
+        // scales of this wavefront's rows for group g, to fp32 (the dword
+        // holds the pair of bf16 that contains it)
+        {
+            const uint32_t sw = reinterpret_cast<const uint32_t*>(st + L::CODE + L::XOP)[wave * 64 + lane];
+            const bool odd = ((my_row * a.G + kc * GC + i) & 1) != 0;
+            tab[lane] = __uint_as_float(odd ? (sw & 0xFFFF0000u) : (sw << 16));
+        }
+        u32x4_t xb[MB][2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                xb[mb][hh] = reinterpret_cast<const u32x4_t*>(st + L::CODE + ((kc * MB + mb) * 2 + hh) * 1024)[lane];
+        f32x4_t S[4];   // read through the same float pointer, after the write above
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) S[t][v] = tab[16 * t + 4 * c + v];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const char* rowp = st + (kc * L::ROWS + 64 * wn + 16 * t + r) * L::GB;
+            u32x4_t a0, a1;
+            gemm_a_operands<BITS>(rowp, c, cmask, cmaskh, cbias, a0, a1);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                f32x4_t d = mfma16x16x32(a0, xb[mb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                d = mfma16x16x32(a1, xb[mb][1], d);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[t][mb][v] = fmaf(S[t][v], d[v], acc[t][mb][v]);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+
+    // sum_g (b X - s D0): units (32-group block j, piece p), chunk kc taking
+    // p = kc, kc + WK, ...
+    {
+        const bool even = (a.G & 1) == 0;
+        const int NJ = a.Gp / 32;
+        for (int j = 0; j < NJ; ++j) {
+            const int g0 = 32 * j + 8 * c;
+            u32x4_t ab[4], as[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int64_t n = n0 + 64 * wn + 16 * t + r;
+                ab[t] = load8_groups(a.biases, n, a.N, a.G, g0, even);
+                as[t] = load8_groups(a.scales, n, a.N, a.G, g0, even);
+                as[t] ^= u32x4_t{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+            }
+            for (int p = kc; p < NP; p += WK) {
+                u32x4_t bp[MB];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    bp[mb] = *reinterpret_cast<const u32x4_t*>(
+                        a.pieces + ((int64_t)p * a.Mp + m0 + 16 * mb + r) * a.Gp + g0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[t][mb] = mfma16x16x32(p < 3 ? ab[t] : as[t], bp[mb], acc[t][mb]);
+            }
+        }
+    }
+
+    // chunk partials, summed in chunk order
+    if constexpr (WK > 1) {
+        barrier_only();   // every wavefront is done with the stage ring
+        f32x4_t* red = reinterpret_cast<f32x4_t*>(gemm_lds);
+        if (kc > 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    red[(((kc - 1) * WN + wn) * 16 + t * MB + mb) * 64 + lane] = acc[t][mb];
+        }
+        __syncthreads();
+        if (kc > 0) return;
+#pragma unroll
+        for (int k2 = 1; k2 < WK; ++k2)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[t][mb] += red[(((k2 - 1) * WN + wn) * 16 + t * MB + mb) * 64 + lane];
+    }
+
+    // store: lane (c, r) holds rows n .. n + 3 of column m of each 16 x 16 tile
+    const bool vec = (a.N & 3) == 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int64_t n = n0 + 64 * wn + 16 * t + 4 * c;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = m0 + 16 * mb + r;
+            if (m >= a.M || n >= a.N) continue;
+            const int64_t o = (int64_t)m * a.N + n;
+            const f32x4_t v = acc[t][mb];
+            if (a.out_f32) {
+                float* y = static_cast<float*>(a.y) + o;
+                if (vec) {
+                    *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < a.N) y[e] = v[e];
+                }
+            } else {
+                uint16_t* y = static_cast<uint16_t*>(a.y) + o;
+                const uint16_t h0 = f32_to_bf16_rne(v[0]), h1 = f32_to_bf16_rne(v[1]);
+                const uint16_t h2 = f32_to_bf16_rne(v[2]), h3 = f32_to_bf16_rne(v[3]);
+                if (vec) {
+                    *reinterpret_cast<uint2*>(y) = make_uint2(h0 | ((uint32_t)h1 << 16), h2 | ((uint32_t)h3 << 16));
+                } else {
+                    const uint16_t h[4] = {h0, h1, h2, h3};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < a.N) y[e] = h[e];
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ host side
+
+struct GemmCfg {
+    int wn, wk, nbuf;
+};
+
+// Stage buffers: as many as fit in 160 KB (at most 4), with the vmcnt wait
+// count (NBUF - 2) * copies per stage within its 6 bits.
+template <int BITS, int WN, int WK>
+constexpr int gemm_nbuf()
+{
+    constexpr int rows = 64 * WN, gb = 8 * BITS, cb = (gb % 16 == 0) ? 16 : 4;
+    constexpr int stage = WK * rows * gb + WK * (kGemmTileM / 16) * 2 * 1024 + WK * rows * 4;
+    constexpr int cps = WK * rows * gb / (64 * cb) / kGemmWaves + (kGemmTileM / 16) * 2 / WN + 1;
+    constexpr int tab = kGemmWaves * 256;
+    int n = (160 * 1024 - tab) / stage;
+    n = n > 4 ? 4 : n;
+    while (n > 2 && (n - 2) * cps > 63) --n;
+    return n;
+}
+
+template <int BITS, int WN, int WK>
+hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t s)
+{
+    constexpr int NBUF = gemm_nbuf<BITS, WN, WK>();
+    using L = GemmLayout<BITS, WN, WK, NBUF>;
+    auto fn = affine_gemm_kernel<BITS, WN, WK, NBUF>;
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(fn), L::LDS);
+    if (e != hipSuccess) return e;
+    const int64_t T = (((int64_t)a.N + L::ROWS - 1) / L::ROWS) * (a.Mp / kGemmTileM);
+    if (T > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3((unsigned)T), dim3(64 * kGemmWaves), L::LDS, s, a);
+    return hipGetLastError();
+}
+
+// Split of the 8 wavefronts: (WN, WK) = (8, 1), (4, 2) or (2, 4).  The widest
+// tile that still gives every CU a workgroup, else the one with the most
+// workgroups (WK must divide the groups per row).
+inline GemmCfg choose_gemm(int M, int N, int K, int cus)
+{
+    const int G = K / 64;
+    const int64_t tm = ((int64_t)M + kGemmTileM - 1) / kGemmTileM;
+    const int opts[3][2] = {{8, 1}, {4, 2}, {2, 4}};
+    GemmCfg best{8, 1, 0};
+    int64_t best_t = -1;
+    for (const auto& o : opts) {
+        if (G % o[1] != 0) continue;
+        const int64_t t = (((int64_t)N + 64 * o[0] - 1) / (64 * o[0])) * tm;
+        if (t >= cus) return GemmCfg{o[0], o[1], 0};
+        if (t > best_t) {
+            best_t = t;
+            best = GemmCfg{o[0], o[1], 0};
+        }
+    }
+    return best;
+}
+
+template <int BITS>
+hipError_t launch_affine_gemm_impl(const GemmArgs& a, hipStream_t s)
+{
+    const int64_t units = (int64_t)(a.Mp / 16) * a.Gp;
+    hipLaunchKernelGGL(gemm_prep_kernel<BITS>, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int cus = 256;
+    if (device_cus(cus) != hipSuccess) cus = 256;
+    const GemmCfg g = choose_gemm(a.M, a.N, a.K, cus);
+    if (g.wn == 8) return launch_gemm_cfg<BITS, 8, 1>(a, s);
+    if (g.wn == 4) return launch_gemm_cfg<BITS, 4, 2>(a, s);
+    return launch_gemm_cfg<BITS, 2, 4>(a, s);
+}
+
+}  // namespace detail
+}  // namespace aqg

@@ -109,7 +109,7 @@ __host__ __device__ inline SegView seg_view(const ProjArgs& a, int64_t n0)
 }
 
 enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6,
-            PATH_MFMA_TILE = 7, PATH_AFFINE_TILE = 8, PATH_AFFINE_SPLIT = 9 };
+            PATH_MFMA_TILE = 7, PATH_AFFINE_TILE = 8, PATH_AFFINE_SPLIT = 9, PATH_AFFINE_GEMM = 10 };
 
 // Launch geometry chosen for a call.
 struct LaunchCfg {
@@ -183,6 +183,48 @@ hipError_t launch_argmax_rows(const float* y, int M, int N, int chunk, void* par
 // Whether the kernel of cfg writes row-argmax partials itself (else the
 // caller runs the GEMV into fp32 and reduces the rows).
 bool argmax_fused(const LaunchCfg& cfg);
+
+// Arguments of one prompt GEMM (device pointers).  xp and pieces live in the
+// caller's workspace and are written by the pre-pass.
+struct GemmArgs {
+    const uint16_t* x;        // bf16 [M][K]
+    const uint32_t* wq;       // codes [N][K b / 32]
+    const uint16_t* scales;   // bf16 [N][G]
+    const uint16_t* biases;   // bf16 [N][G]
+    void* y;                  // bf16 or f32 [M][N]
+    uint16_t* xp;             // x operands [Mp / 16][G][2][64 lanes][8] bf16
+    uint16_t* pieces;         // [NP][Mp][Gp] bf16: X hi, mid, lo, then D0 hi, mid, lo
+    int M, N, K;
+    int G;                    // groups per row, K / 64
+    int Gp;                   // G rounded up to 32
+    int Mp;                   // M rounded up to 64
+    int out_f32;
+};
+
+constexpr int kGemmTileM = 64;      // rows of x per tile
+
+// Pieces per (row, group): X (3) and, with a code offset, D0 (3).
+__host__ __device__ constexpr int gemm_pieces(int bits) { return bits == 8 ? 3 : 6; }
+
+// Workspace of a prompt GEMM: the x operands (Mp K bf16), then, from the
+// next 256-byte boundary, the pieces.
+inline size_t gemm_workspace_bytes(int bits, int M, int K)
+{
+    const size_t Mp = ((size_t)M + kGemmTileM - 1) / kGemmTileM * kGemmTileM;
+    const size_t G = (size_t)K / 64, Gp = (G + 31) / 32 * 32;
+    const size_t xp = (Mp * K * 2 + 255) / 256 * 256;
+    return xp + ((size_t)gemm_pieces(bits) * Mp * Gp * 2 + 255) / 256 * 256;
+}
+inline size_t gemm_pieces_offset(int M, int K)
+{
+    const size_t Mp = ((size_t)M + kGemmTileM - 1) / kGemmTileM * kGemmTileM;
+    return (Mp * K * 2 + 255) / 256 * 256;
+}
+
+// Affine prompt GEMM, BITS = 2..8 (affine_gemm_b*.hip): the pre-pass over x,
+// then the main kernel.
+template <int BITS>
+hipError_t launch_affine_gemm(const GemmArgs& a, hipStream_t s);
 
 // bits: 0 = dense bf16, 2..8 = affine width.
 LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K);

@@ -9,7 +9,8 @@
  *   argmax over n of y[m,n], without writing y             (aqg_gemv_*_argmax)
  *
  * for M = 1..32 rows of activations (single-stream decode, or a window of up
- * to 32 rows).
+ * to 32 rows), and the affine product for any M (prompt chunks):
+ *   y[M,N] = x[M,K] . W^T          W affine b-bit, M >= 1  (aqg_gemm_affine_q2 .. _q8)
  *
  * Sources (web pages, cited by title and section):
  *  - AstrAI decode_linear_benchmark.md -- the commit message: a BF16 GEMV for
@@ -38,14 +39,16 @@
  *    synchronization.
  *  - Validation happens on the host before any HIP call.  On any status other
  *    than AQG_OK nothing has been enqueued and the outputs are untouched.
- *  - M in [1, 32]; N, K >= 1.  Dense: K % 8 == 0.  Affine: K % 64 == 0.
+ *  - M in [1, 32] (the prompt GEMMs: [1, AQG_GEMM_MAX_M]); N, K >= 1.
+ *    Dense: K % 8 == 0.  Affine: K % 64 == 0.
  *    x and W/Wq must be 16-byte aligned; scales and biases 4-byte aligned
  *    (read in 4- to 16-byte pieces); y and codes naturally aligned for their
  *    element type.  y must not overlap any input.
  *  - out_dtype AQG_OUT_F32 writes the fp32 sums; AQG_OUT_BF16 writes exactly
  *    the round-to-nearest-even bf16 of the values the same call would write
  *    with AQG_OUT_F32 (kernels are deterministic).
- *  - workspace: scratch of the calls that need one (the row argmax).
+ *  - workspace: scratch of the calls that need one (the row argmax, the
+ *    prompt GEMMs).
  *    aqg_workspace_bytes() gives the size a call needs; NULL / 0 is valid
  *    when that size is 0, otherwise a smaller workspace is
  *    AQG_ERR_INVALID_ARG.
@@ -83,6 +86,7 @@ typedef enum { AQG_OUT_BF16 = 0, AQG_OUT_F32 = 1 } aqg_out_dtype;
 #define AQG_KIND_SWIGLU 9
 #define AQG_KIND_SWIGLU_AFFINE 16  /* + b (2..8) = affine SwiGLU of width b */
 #define AQG_KIND_ARGMAX_DENSE 32   /* + b (2..8) = affine row argmax of width b */
+#define AQG_KIND_GEMM_AFFINE 48    /* + b (2..8) = affine prompt GEMM of width b (any M) */
 
 /* Returns AQG_ABI_VERSION. */
 int aqg_abi_version(void);
@@ -272,6 +276,48 @@ int aqg_gemv_affine_q7_argmax(const void* x, const uint32_t* Wq, const void* sca
 int aqg_gemv_affine_q8_argmax(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
                               float* max_val, int32_t* max_idx, int M, int N, int K,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Affine prompt GEMM of width b (one symbol per b = 2..8): the same product
+ * as aqg_gemv_affine_q{b},
+ *   y[m,n] = sum_k x[m,k] * (scale[n,k/64] * q[n,k] + bias[n,k/64]),
+ * for any number of activation rows M in [1, AQG_GEMM_MAX_M] (prompt chunks;
+ * for M <= 32 the GEMVs above are the faster call).  Same arrays, layouts,
+ * alignment and out_dtype rules as the GEMVs; K % 64 == 0.
+ *   workspace: device memory of at least
+ *   aqg_workspace_bytes(AQG_KIND_GEMM_AFFINE + b, M, N, K) bytes (about
+ *   2 M K bytes; 16-byte aligned, not overlapping any other argument),
+ *   required: the call writes x rearranged into matrix-core operands and
+ *   the per-group sums of x there before the product reads them.
+ * Accumulation is fp32 (per 64-code group: scale times the codes' dot
+ * product, plus the bias and code-offset terms); each (m, n) is computed
+ * the same way whatever M is.  The result is within the same bound of the
+ * exact product as the GEMVs', but not bit-equal to them.
+ * TensorFold PR #849 (format; the page also notes that its 8-bit modules
+ * have no prompt GEMM and run prompts on the decode tiles).
+ */
+#define AQG_GEMM_MAX_M 65536
+int aqg_gemm_affine_q2(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                       void* y, int M, int N, int K, int out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemm_affine_q3(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                       void* y, int M, int N, int K, int out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemm_affine_q4(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                       void* y, int M, int N, int K, int out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemm_affine_q5(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                       void* y, int M, int N, int K, int out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemm_affine_q6(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                       void* y, int M, int N, int K, int out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemm_affine_q7(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                       void* y, int M, int N, int K, int out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int aqg_gemm_affine_q8(const void* x, const uint32_t* Wq, const void* scales, const void* biases,
+                       void* y, int M, int N, int K, int out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Row argmax that allocates nothing, for callers that cannot allocate

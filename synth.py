@@ -59,6 +59,13 @@ MIXED_M = [1, 8, 16]
 SWIGLU_AFFINE_SHAPES = [("mlp_1536", 4096, 1536), ("mlp_1024", 3584, 1024)]
 SWIGLU_AFFINE_BITS = [2, 3, 4, 5, 6, 8]
 SWIGLU_AFFINE_M = [1, 4, 16, 32]
+# affine prompt GEMM (M > 32): the mixed-width and ~0.8B-decoder weight
+# shapes at prompt chunks of 128 rows (the prompt length of the pages'
+# decode benchmark) and 512 rows
+GEMM_BITS = [2, 3, 4, 5, 6, 7, 8]
+GEMM_SHAPES = [("wide_14336", 14336, 4096), ("mlp_up_3584", 3584, 1024), ("mlp_down_3584", 1024, 3584)]
+GEMM_M = [128, 512]
+PROMPT_M_MAX = 1024
 
 
 def rng(config_id: int, name: str) -> np.random.Generator:
@@ -96,6 +103,13 @@ def random_words(shape, config_id: int, name: str) -> np.ndarray:
 def activations(config_id: int, K: int, M: int = M_MAX) -> np.ndarray:
     """x[M, K] ~ N(0, 1) in bf16; drawn at M_MAX rows and sliced."""
     return normal_bf16((M_MAX, K), 1.0, config_id, "x/K%d" % K)[:M].copy()
+
+
+def prompt_activations(config_id: int, K: int, M: int) -> np.ndarray:
+    """x[M, K] ~ N(0, 1) in bf16 for a prompt chunk; drawn at PROMPT_M_MAX
+    rows and sliced, so a shorter chunk is a prefix of a longer one."""
+    assert M <= PROMPT_M_MAX
+    return normal_bf16((PROMPT_M_MAX, K), 1.0, config_id, "xprompt/K%d" % K)[:M].copy()
 
 
 def dense_weight(config_id: int, name: str, N: int, K: int) -> np.ndarray:

@@ -41,7 +41,7 @@ def test_header_declares_expected_entry_points():
                {"aqg_gemv_affine_q%d_argmax" % b for b in range(2, 9)} | \
                {"aqg_swiglu_affine_q%d" % b for b in range(2, 9)} | \
                {"aqg_gemv_bf16_multi"} | {"aqg_gemv_affine_q%d_multi" % b for b in range(2, 9)} | \
-               {"aqg_stream_read"}
+               {"aqg_stream_read"} | {"aqg_gemm_affine_q%d" % b for b in range(2, 9)}
     assert set(names) == expected
 
 
@@ -260,3 +260,77 @@ def test_multi_validation(lib):
                       1, 64, 0, None, 0, None)
     assert g(*args([S[0], 0, S[2]])) == aqg.AQG_ERR_INVALID_ARG           # a null scale array entry
     assert g(*args([S[0], S[1] + 2, S[2]])) == aqg.AQG_ERR_ALIGNMENT
+
+
+# ------------------------------------------------ affine prompt GEMM
+
+def gemm_ws_closed_form(bits, M, K):
+    """x operands (M rounded up to 64) x K bf16, then the pieces (3 per row
+    and group for 8 bits, else 6) over groups rounded up to 32, each part
+    rounded up to 256 bytes."""
+    Mp = -(-M // 64) * 64
+    Gp = -(-(K // 64) // 32) * 32
+    up = lambda v: -(-v // 256) * 256
+    return up(Mp * K * 2) + up((3 if bits == 8 else 6) * Mp * Gp * 2)
+
+
+@pytest.mark.parametrize("bits", range(2, 9))
+def test_gemm_workspace_bytes(bits):
+    kind = aqg.AQG_KIND_GEMM_AFFINE + bits
+    for M, K in [(1, 64), (33, 1024), (64, 1536), (65, 4096), (512, 4096), (1000, 3584)]:
+        assert aqg.workspace_bytes(kind, M, 100, K) == gemm_ws_closed_form(bits, M, K)
+    assert aqg.workspace_bytes(kind, 0, 100, 1024) == 0
+    assert aqg.workspace_bytes(kind, 33, 100, 96) == 0               # K not a multiple of 64
+    assert aqg.workspace_bytes(kind, aqg.GEMM_MAX_M + 1, 100, 64) == 0
+
+
+def gemm(lib, bits=4, x=A16, Wq=B16, s=D16, b=E16, y=C16, M=40, N=16, K=64, out=0, ws=0x100000, wsb=None):
+    if wsb is None:
+        wsb = gemm_ws_closed_form(bits, M, K) if M > 0 and K > 0 else 0
+    return getattr(lib, "aqg_gemm_affine_q%d" % bits)(x, Wq, s, b, y, M, N, K, out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), aqg.AQG_ERR_INVALID_ARG),
+    (dict(Wq=None), aqg.AQG_ERR_INVALID_ARG),
+    (dict(s=None), aqg.AQG_ERR_INVALID_ARG),
+    (dict(b=None), aqg.AQG_ERR_INVALID_ARG),
+    (dict(y=None), aqg.AQG_ERR_INVALID_ARG),
+    (dict(M=0), aqg.AQG_ERR_INVALID_ARG),
+    (dict(N=0), aqg.AQG_ERR_INVALID_ARG),
+    (dict(out=3), aqg.AQG_ERR_INVALID_ARG),
+    (dict(ws=None), aqg.AQG_ERR_INVALID_ARG),            # the workspace is required
+    (dict(wsb=1024), aqg.AQG_ERR_INVALID_ARG),           # and must hold the x operands and pieces
+    (dict(K=96), aqg.AQG_ERR_UNSUPPORTED),
+    (dict(M=aqg.GEMM_MAX_M + 1), aqg.AQG_ERR_UNSUPPORTED),
+    (dict(x=A16 + 8), aqg.AQG_ERR_ALIGNMENT),
+    (dict(Wq=B16 + 4), aqg.AQG_ERR_ALIGNMENT),
+    (dict(ws=0x100008), aqg.AQG_ERR_ALIGNMENT),
+    (dict(s=D16 + 2), aqg.AQG_ERR_ALIGNMENT),
+    (dict(y=C16 + 2, out=1), aqg.AQG_ERR_ALIGNMENT),
+    (dict(y=A16), aqg.AQG_ERR_INVALID_ARG),              # output overlaps x
+    (dict(ws=B16), aqg.AQG_ERR_INVALID_ARG),             # workspace overlaps Wq
+    (dict(ws=C16), aqg.AQG_ERR_INVALID_ARG),             # workspace overlaps y
+])
+def test_gemm_validation(lib, kwargs, status):
+    for bits in range(2, 9):
+        assert gemm(lib, bits=bits, **kwargs) == status
+
+
+def test_gemm_accepts_decode_and_prompt_sizes_up_to_the_device_check(lib):
+    """Valid arguments get past validation (to the device check: no GPU here,
+    or the call is made on one)."""
+    if HAS_GPU_NODE:
+        pytest.skip("a GPU node is present: the call would launch")
+    far = [(i + 1) << 30 for i in range(6)]   # arrays 1 GiB apart: no overlap
+    for M in (1, 32, 33, 4096):
+        assert gemm(lib, M=M, K=1024, x=far[0], Wq=far[1], s=far[2], b=far[3], y=far[4],
+                    ws=far[5]) == aqg.AQG_ERR_DEVICE
+
+
+def test_gemm_dispatch_query():
+    for bits in range(2, 9):
+        path, cols = aqg.dispatch_path(aqg.AQG_KIND_GEMM_AFFINE + bits, 512, 14336, 4096)
+        assert path == "affine_gemm" and cols == 64
+    with pytest.raises(aqg.AqgError):
+        aqg.dispatch_path(aqg.AQG_KIND_GEMM_AFFINE + 4, 40, 100, 96)
