@@ -27,23 +27,29 @@
 // and the six pieces per (row, group).
 //
 // Main kernel (affine_gemm_kernel): a workgroup of 8 wavefronts owns a tile
-// of 64 WN rows of W by 64 rows of x and walks K in stages of one group;
-// with WK > 1 the K range is split into WK chunks, one per wavefront slice.
-// Wavefront (wn, kc) owns rows 64 wn .. + 63 of the tile and chunk kc: a
-// 64 x 64 output tile = 4 x 4 MFMA tiles of 16 x 16.  Each stage is copied
-// straight into LDS by buffer loads with an LDS destination, spread evenly
-// over the wavefronts: the chunks' code bytes of the tile's rows (16 bytes
-// per lane for even widths, 4 for odd ones), the x operands (1 KB per
-// instruction) and the scales (one dword per row holding the group's bf16
-// scale).  NBUF stage buffers form a ring; copies run NBUF - 1 stages ahead
-// of the arithmetic, with one barrier per stage and explicit waits that
-// leave exactly the younger stages' copies in flight.  Per stage a
-// wavefront turns its 64 rows' scales to fp32 through a private LDS table,
-// reads its 8 x operands, and per 16-row block its lanes' code windows
-// (lane quarter c: codes 16c .. 16c + 15 of the group), builds the two A
-// operands, runs 8 MFMAs and 16 FMAs.  The chunk partials of a tile are
-// summed through LDS in chunk order (fixed: no result depends on M or on
-// the other rows), then stored as fp32 or RNE bf16.
+// of 64 WN rows of W by 64 rows of x and walks K one group per stage; with
+// WK > 1 the K range is split into WK chunks, one per slice of WN
+// wavefronts.  Wavefront (wn, kc) owns rows 64 wn .. + 63 of the tile in
+// chunk kc: a 64 x 64 output tile, 4 x 4 MFMA tiles of 16 x 16.
+//   * Codes are private to the wavefront that owns their rows, so they go
+//     from HBM straight into its registers: per 16-row block a lane reads
+//     the words holding its window (lane quarter c: codes 16c .. 16c + 15
+//     of the group).  The x operands are shared by the WN wavefronts of a
+//     chunk: each stage's 1 KB blocks are loaded by all threads and written
+//     to one of two LDS buffers.  A scale per lane (its row's) goes through
+//     a wavefront-private LDS table to the lanes holding that row's outputs.
+//   * Loads run D stages ahead of the arithmetic in a ring of register sets
+//     indexed with constants only (the loop is unrolled D + 1 times); D is
+//     as large as the registers allow beside the tile.  One barrier a stage.
+//   * Per stage and 16-row block: the two A operands from the code window,
+//     4 + 4 MFMAs into fresh 16 x 16 tiles, 16 FMAs of the scale into the
+//     running sums.  All loads are plain buffer loads the compiler sees, so
+//     its own waits cover them.  (Copies straight into LDS were measured
+//     slower here: their issue rate, not HBM, bounded the stage.)
+// The chunk partials of a tile are summed through LDS in chunk order
+// (fixed: no result depends on the other rows of x), then stored as fp32 or
+// RNE bf16.  Consecutive tiles (same rows of W, successive blocks of x) go to
+// one XCD, so a tile's codes are read from HBM once and then hit in its L2.
 //
 // Format: TensorFold PR #849, "qwen3_5 cuda: mixed-width MLX checkpoints, 2
 // to 8 bits in groups of 64" (MLX affine mode, groups of 64); the same page
@@ -177,63 +183,50 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(GemmArgs a)
 
 // ------------------------------------------------------------ main kernel
 
-template <int BITS, int WN, int WK, int NBUF>
+template <int BITS, int WN, int WK>
 struct GemmLayout {
     static constexpr int NW = WN * WK;                    // wavefronts
+    static constexpr int NT = 64 * NW;                    // threads
     static constexpr int MB = kGemmTileM / 16;            // 16-column blocks of a tile
     static constexpr int ROWS = 64 * WN;                  // rows of W per tile
     static constexpr int GB = 8 * BITS;                   // code bytes per row and group
-    static constexpr int CB = (GB % 16 == 0) ? 16 : 4;    // bytes per lane of a code copy
-    static constexpr int CODE = WK * ROWS * GB;           // LDS bytes of codes per stage
-    static constexpr int CODE_CPW = CODE / (64 * CB) / NW;   // code copies per wavefront per stage
+    static constexpr int NWW = (2 * BITS + 3) / 4;        // code words a lane reads per row and group
     static constexpr int XOP = WK * MB * 2 * 1024;        // x operand bytes per stage
-    static constexpr int XOP_CPW = XOP / 1024 / NW;       // 1 KB copies per wavefront per stage
-    static constexpr int SCL = WK * ROWS * 4;             // scale dwords per stage
-    static constexpr int STAGE = CODE + XOP + SCL;
-    static constexpr int CPS = CODE_CPW + XOP_CPW + 1;    // copies per wavefront per stage
+    static constexpr int XLD = XOP / 16 / NT;             // 16-byte x loads per thread per stage
     static constexpr int TAB = NW * 64 * 4;               // per-wavefront fp32 scale tables
-    static constexpr int RED = (WK - 1) * WN * 64 * 64 * 4;   // chunk partials (over the ring)
-    static constexpr int RING = NBUF * STAGE > RED ? NBUF * STAGE : RED;
+    static constexpr int RED = (WK - 1) * WN * 64 * 64 * 4;   // chunk partials (over the x buffers)
+    static constexpr int RING = 2 * XOP > RED ? 2 * XOP : RED;
     static constexpr size_t LDS = (size_t)RING + TAB;
     static_assert(NW == kGemmWaves, "eight wavefronts per workgroup");
-    static_assert(CODE % (64 * CB * NW) == 0, "code copies split evenly over the wavefronts");
-    static_assert(XOP % (1024 * NW) == 0, "x copies split evenly over the wavefronts");
-    static_assert(SCL == NW * 256, "one scale copy per wavefront");
-    static_assert(NBUF >= 2 && (NBUF - 2) * CPS <= 63, "vmcnt counts at most 63");
+    static_assert(XOP % (16 * NT) == 0, "x loads split evenly over the threads");
     static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
 
-// Code window of lane quarter c (codes 16c .. 16c + 15 of a group) from the
-// row's group bytes in LDS, as the A operands of the group's two k-steps.
+// The lane's code window (codes 16c .. 16c + 15 of a group) from the words
+// it read: NWW consecutive words of the row starting at word (16 b c) / 32
+// of the group, the window starting at bit sh = (16 b c) % 32 (0, or 16
+// for odd widths and odd c).  The A operands of the group's two k-steps.
 // m = field mask, mh = m << 16, cb = 0x43004300, opaque registers.
 template <int BITS>
-__device__ __forceinline__ void gemm_a_operands(const char* rowp, int c, uint32_t m, uint32_t mh, uint32_t cb,
-                                                u32x4_t& a0, u32x4_t& a1)
+__device__ __forceinline__ void gemm_a_from_words(const uint32_t (&w)[GemmLayout<BITS, 8, 1>::NWW], uint32_t sh,
+                                                  uint32_t m, uint32_t mh, uint32_t cb, u32x4_t& a0, u32x4_t& a1)
 {
     if constexpr (BITS == 2) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(rowp + 4 * c);
-        a0 = codes2_to_bf16(w, 0, m, cb);
-        a1 = codes2_to_bf16(w, 1, m, cb);
+        a0 = codes2_to_bf16(w[0], 0, m, cb);
+        a1 = codes2_to_bf16(w[0], 1, m, cb);
     } else if constexpr (BITS == 4) {
-        const uint2 w = *reinterpret_cast<const uint2*>(rowp + 8 * c);
-        a0 = codes4_to_bf16(w.x, m, cb);
-        a1 = codes4_to_bf16(w.y, m, cb);
+        a0 = codes4_to_bf16(w[0], m, cb);
+        a1 = codes4_to_bf16(w[1], m, cb);
     } else if constexpr (BITS == 8) {
-        const uint4 w = *reinterpret_cast<const uint4*>(rowp + 16 * c);
-        a0 = codes8_exact_bf16(w.x, w.y);
-        a1 = codes8_exact_bf16(w.z, w.w);
+        a0 = codes8_exact_bf16(w[0], w[1]);
+        a1 = codes8_exact_bf16(w[2], w[3]);
     } else {
-        using WD = AffineTileWidth<BITS>;
-        constexpr int NWN = WD::NWN;
-        const int bit0 = 16 * BITS * c;
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(rowp) + (bit0 >> 5);
-        const uint32_t sh = (uint32_t)(bit0 & 31);   // 0 or 16
-        uint32_t raw[NWN], wn[NWN];
+        constexpr int NWN = AffineTileWidth<BITS>::NWN;
+        static_assert(NWN <= GemmLayout<BITS, 8, 1>::NWW, "the window fits the words read");
+        uint32_t wn[NWN];
 #pragma unroll
-        for (int i = 0; i < NWN; ++i) raw[i] = src[i];
-#pragma unroll
-        for (int i = 0; i + 1 < NWN; ++i) wn[i] = __builtin_amdgcn_alignbit(raw[i + 1], raw[i], sh);
-        wn[NWN - 1] = raw[NWN - 1] >> sh;   // only its low 16 bits belong to the window when sh = 16
+        for (int i = 0; i + 1 < NWN; ++i) wn[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], sh);
+        wn[NWN - 1] = w[NWN - 1] >> sh;   // only its low 16 bits belong to the window when sh = 16
         a0 = codes_window_to_bf16<BITS, 0>(wn, m, mh, cb);
         a1 = codes_window_to_bf16<BITS, 1>(wn, m, mh, cb);
     }
@@ -260,12 +253,23 @@ __device__ __forceinline__ u32x4_t load8_groups(const uint16_t* arr, int64_t n, 
     return o;
 }
 
-template <int BITS, int WN, int WK, int NBUF>
+// One stage's loads of a thread: the code words of its 4 rows (one per
+// 16-row block), its x operand pieces and its row's scale.
+template <int BITS, int WK>
+struct GemmStage {
+    uint32_t cw[4][GemmLayout<BITS, 8, 1>::NWW];
+    u32x4_t xo[WK];
+    uint32_t sc;
+};
+
+template <int BITS, int WN, int WK, int D>
 __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a)
 {
-    using L = GemmLayout<BITS, WN, WK, NBUF>;
+    using L = GemmLayout<BITS, WN, WK>;
     constexpr int MB = L::MB;
+    constexpr int NWW = L::NWW;
     constexpr int NP = gemm_pieces(BITS);
+    constexpr int R = D + 1;   // stage register sets: the one in use and D in flight
     extern __shared__ __attribute__((aligned(16))) char gemm_lds[];
 
     const int lane = threadIdx.x & 63;
@@ -282,53 +286,46 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
     const int64_t n0 = (tile / TM) * L::ROWS;
     const int m0 = (int)(tile % TM) * kGemmTileM;
     const int GC = a.G / WK;            // groups (stages) per chunk
+    const int g0 = kc * GC;             // this wavefront's first group
     const int64_t row_bytes = (int64_t)a.K * BITS / 8;
     const int64_t rows_here = (int64_t)a.N - n0 < L::ROWS ? (int64_t)a.N - n0 : L::ROWS;
 
-    const u32x4v_t rw = buffer_words(reinterpret_cast<const char*>(a.wq) + n0 * row_bytes, rows_here * row_bytes);
+    // rows past N and x blocks past the workspace read as zeros
+    const __amdgpu_buffer_rsrc_t rw =
+        tile_rsrc(reinterpret_cast<const char*>(a.wq) + n0 * row_bytes, rows_here * row_bytes);
     const int64_t xp0 = (int64_t)(m0 / 16) * a.G * 2048;   // bytes
-    const u32x4v_t rx = buffer_words(reinterpret_cast<const char*>(a.xp) + xp0, (int64_t)MB * a.G * 2048);
-    const u32x4v_t rs = buffer_words(a.scales + n0 * a.G, (rows_here * a.G * 2 + 3) & ~(int64_t)3);
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(reinterpret_cast<const char*>(a.xp) + xp0, (int64_t)MB * a.G * 2048);
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(a.scales + n0 * a.G, rows_here * a.G * 2);
 
-    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)gemm_lds;
+    // code words: row 64 wn + 16 t + r of the tile, word (16 b c) / 32 of
+    // the group; x pieces: thread j loads piece j of each chunk's
+    // [mb][k-step][lane] block; scale: row 64 wn + lane
+    const int bit0 = 16 * BITS * c;
+    const uint32_t sh = (uint32_t)(bit0 & 31);
+    const uint32_t code_off = (uint32_t)((64 * wn + r) * row_bytes + (int64_t)g0 * L::GB + 4 * (bit0 >> 5));
+    const uint32_t code_tstride = (uint32_t)(16 * row_bytes);
+    const int j = threadIdx.x;
+    const int jmb = j / 128, jh = (j / 64) % 2, jl = j % 64;
+    const uint32_t x_off = (uint32_t)(((jmb * a.G + 0) * 2 + jh) * 1024 + jl * 16);
+    const uint32_t s_off = (uint32_t)((((int64_t)64 * wn + lane) * a.G + g0) * 2);
 
-    // this wavefront's copies of a stage (the same for every stage but for
-    // the group offset): code copy j covers LDS bytes [j 64 CB, (j+1) 64 CB)
-    // of the stage's [WK][ROWS][GB] codes
-    uint32_t code_voff[L::CODE_CPW];
+    auto load = [&](int i, GemmStage<BITS, WK>& st) __attribute__((always_inline)) {
+        const uint32_t ci = code_off + (uint32_t)(i * L::GB);
 #pragma unroll
-    for (int q = 0; q < L::CODE_CPW; ++q) {
-        const int f = (wave * L::CODE_CPW + q) * 64 * L::CB + lane * L::CB;
-        const int ck = f / (L::ROWS * L::GB);
-        const int rem = f % (L::ROWS * L::GB);
-        const int row = rem / L::GB, off = rem % L::GB;
-        code_voff[q] = (uint32_t)(row * row_bytes + (int64_t)ck * a.G / WK * L::GB + off);
-    }
-    // scales: wavefront (wn, kc) copies the dwords of its own rows and chunk
-    const int64_t my_row = n0 + 64 * wn + lane;   // row of this lane's scale copy
-    const int64_t srow = my_row - n0;
-
-    auto issue = [&](int i, int buf) __attribute__((always_inline)) {
-        const uint32_t base = lds0 + (uint32_t)buf * L::STAGE;
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int q = 0; q < L::CODE_CPW; ++q) {
-            const uint32_t dst = base + (uint32_t)((wave * L::CODE_CPW + q) * 64 * L::CB);
-            if constexpr (L::CB == 16) copy_1k_to_lds(rw, dst, code_voff[q], (uint32_t)(i * L::GB));
-            else copy_dword_to_lds(rw, dst, code_voff[q], (uint32_t)(i * L::GB));
-        }
+            for (int q = 0; q < NWW; ++q)
+                st.cw[t][q] = __builtin_amdgcn_raw_buffer_load_b32(rw, ci + t * code_tstride + 4 * q, 0, 0);
 #pragma unroll
-        for (int q = 0; q < L::XOP_CPW; ++q) {
-            const int j = wave * L::XOP_CPW + q;          // [chunk][mb][H]
-            const int ck = j / (MB * 2), mb = (j / 2) % MB, hh = j % 2;
-            const uint32_t dst = base + L::CODE + (uint32_t)j * 1024;
-            const uint32_t soff = (uint32_t)(((mb * a.G + ck * GC + i) * 2 + hh) * 1024);
-            copy_1k_to_lds(rx, dst, (uint32_t)lane * 16, soff);
-        }
-        {
-            const uint32_t dst = base + L::CODE + L::XOP + (uint32_t)wave * 256;
-            const uint32_t voff = (uint32_t)(((srow * a.G + kc * GC + i) * 2) & ~(int64_t)3);
-            copy_dword_to_lds(rs, dst, voff, 0u);
-        }
+        for (int q = 0; q < WK; ++q)
+            st.xo[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                rx, x_off + (uint32_t)((q * GC + i) * 2048), 0, 0));
+        st.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off + (uint32_t)(2 * i), 0, 0);
+    };
+    auto put_x = [&](int buf, const GemmStage<BITS, WK>& st) __attribute__((always_inline)) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(gemm_lds + buf * L::XOP);
+#pragma unroll
+        for (int q = 0; q < WK; ++q) dst[q * L::NT + j] = st.xo[q];
     };
 
     f32x4_t acc[4][MB];
@@ -345,50 +342,60 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
 
     float* tab = reinterpret_cast<float*>(gemm_lds + L::RING) + wave * 64;
 
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i)
-        if (i < GC) issue(i, i);
-
-    for (int i = 0; i < GC; ++i) {
-        if (i + NBUF - 2 < GC) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NBUF - 2) * L::CPS));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-        barrier_only();   // stage i is in LDS; every wavefront is done with stage i - 1
-        if (i + NBUF - 1 < GC) issue(i + NBUF - 1, (i + NBUF - 1) % NBUF);
-
-        const char* st = gemm_lds + (i % NBUF) * L::STAGE;
-        // scales of this wavefront's rows for group g, to fp32 (the dword
-        // holds the pair of bf16 that contains it)
-        {
-            const uint32_t sw = reinterpret_cast<const uint32_t*>(st + L::CODE + L::XOP)[wave * 64 + lane];
-            const bool odd = ((my_row * a.G + kc * GC + i) & 1) != 0;
-            tab[lane] = __uint_as_float(odd ? (sw & 0xFFFF0000u) : (sw << 16));
-        }
-        u32x4_t xb[MB][2];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                xb[mb][hh] = reinterpret_cast<const u32x4_t*>(st + L::CODE + ((kc * MB + mb) * 2 + hh) * 1024)[lane];
+    // group i: both k-steps of each 16 x 16 tile, then the group's scale
+    // into the running sums, one 16-row block at a time
+    auto compute = [&](int i, const GemmStage<BITS, WK>& st) __attribute__((always_inline)) {
+        tab[lane] = __uint_as_float(st.sc << 16);
         f32x4_t S[4];   // read through the same float pointer, after the write above
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int v = 0; v < 4; ++v) S[t][v] = tab[16 * t + 4 * c + v];
+        const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(gemm_lds + (i & 1) * L::XOP) + kc * 512;
+        u32x4_t xb[MB][2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) xb[mb][hh] = xs[(mb * 2 + hh) * 64 + lane];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const char* rowp = st + (kc * L::ROWS + 64 * wn + 16 * t + r) * L::GB;
             u32x4_t a0, a1;
-            gemm_a_operands<BITS>(rowp, c, cmask, cmaskh, cbias, a0, a1);
+            gemm_a_from_words<BITS>(st.cw[t], sh, cmask, cmaskh, cbias, a0, a1);
+            f32x4_t d[MB];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                f32x4_t d = mfma16x16x32(a0, xb[mb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
-                d = mfma16x16x32(a1, xb[mb][1], d);
+            for (int mb = 0; mb < MB; ++mb) d[mb] = mfma16x16x32(a0, xb[mb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[t][mb][v] = fmaf(S[t][v], d[v], acc[t][mb][v]);
-            }
+            for (int mb = 0; mb < MB; ++mb) d[mb] = mfma16x16x32(a1, xb[mb][1], d[mb]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[t][mb][v] = fmaf(S[t][v], d[mb][v], acc[t][mb][v]);
         }
+    };
+
+    // D stages in flight: the loads of group i + D go out before group i is
+    // computed; group i + 1's x pieces go to LDS after it.  The ring is
+    // indexed with constants only (unrolled R times), so it stays in
+    // registers.
+    GemmStage<BITS, WK> ring[R];
+    static_for<0, D>([&](auto Uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(Uc)::value;
+        if (u < GC) load(u, ring[u]);
+    });
+    put_x(0, ring[0]);
+    __syncthreads();
+    for (int base = 0; base < GC; base += R) {
+        static_for<0, R>([&](auto Uc) __attribute__((always_inline)) {
+            constexpr int u = decltype(Uc)::value;
+            const int i = base + u;
+            if (i < GC) {   // uniform over the workgroup
+                if (i + D < GC) load(i + D, ring[(u + D) % R]);
+                compute(i, ring[u]);
+                if (i + 1 < GC) put_x((i + 1) & 1, ring[(u + 1) % R]);
+                __syncthreads();
+            }
+        });
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
     // sum_g (b X - s D0): units (32-group block j, piece p), chunk kc taking
     // p = kc, kc + WK, ...
@@ -422,7 +429,7 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
 
     // chunk partials, summed in chunk order
     if constexpr (WK > 1) {
-        barrier_only();   // every wavefront is done with the stage ring
+        // every wavefront is done with the x buffers (the loop ends with a barrier)
         f32x4_t* red = reinterpret_cast<f32x4_t*>(gemm_lds);
         if (kc > 0) {
 #pragma unroll
@@ -482,30 +489,24 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
 // ------------------------------------------------------------ host side
 
 struct GemmCfg {
-    int wn, wk, nbuf;
+    int wn, wk;
 };
 
-// Stage buffers: as many as fit in 160 KB (at most 4), with the vmcnt wait
-// count (NBUF - 2) * copies per stage within its 6 bits.
-template <int BITS, int WN, int WK>
-constexpr int gemm_nbuf()
+// Stages in flight: as many as the registers allow beside the 64 x 64 tile
+// (a stage is 4 NWW code words, WK x pieces and a scale per lane).
+template <int BITS, int WK>
+constexpr int gemm_depth()
 {
-    constexpr int rows = 64 * WN, gb = 8 * BITS, cb = (gb % 16 == 0) ? 16 : 4;
-    constexpr int stage = WK * rows * gb + WK * (kGemmTileM / 16) * 2 * 1024 + WK * rows * 4;
-    constexpr int cps = WK * rows * gb / (64 * cb) / kGemmWaves + (kGemmTileM / 16) * 2 / WN + 1;
-    constexpr int tab = kGemmWaves * 256;
-    int n = (160 * 1024 - tab) / stage;
-    n = n > 4 ? 4 : n;
-    while (n > 2 && (n - 2) * cps > 63) --n;
-    return n;
+    constexpr int regs = 4 * GemmLayout<BITS, 8, 1>::NWW + 4 * WK + 1;
+    constexpr int d = 60 / regs;
+    return WK >= 4 ? 1 : d > 4 ? 4 : d;
 }
 
 template <int BITS, int WN, int WK>
 hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t s)
 {
-    constexpr int NBUF = gemm_nbuf<BITS, WN, WK>();
-    using L = GemmLayout<BITS, WN, WK, NBUF>;
-    auto fn = affine_gemm_kernel<BITS, WN, WK, NBUF>;
+    using L = GemmLayout<BITS, WN, WK>;
+    auto fn = affine_gemm_kernel<BITS, WN, WK, gemm_depth<BITS, WK>()>;
     hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(fn), L::LDS);
     if (e != hipSuccess) return e;
     const int64_t T = (((int64_t)a.N + L::ROWS - 1) / L::ROWS) * (a.Mp / kGemmTileM);
@@ -515,22 +516,23 @@ hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t s)
 }
 
 // Split of the 8 wavefronts: (WN, WK) = (8, 1), (4, 2) or (2, 4).  The widest
-// tile that still gives every CU a workgroup, else the one with the most
-// workgroups (WK must divide the groups per row).
+// tile that still gives three quarters of the CUs a workgroup (measured: at
+// 512 x 14336 x 4096, 224 workgroups of (8, 1) beat 448 of (4, 2) by 10 %),
+// else the one with the most workgroups (WK must divide the groups per row).
 inline GemmCfg choose_gemm(int M, int N, int K, int cus)
 {
     const int G = K / 64;
     const int64_t tm = ((int64_t)M + kGemmTileM - 1) / kGemmTileM;
     const int opts[3][2] = {{8, 1}, {4, 2}, {2, 4}};
-    GemmCfg best{8, 1, 0};
+    GemmCfg best{8, 1};
     int64_t best_t = -1;
     for (const auto& o : opts) {
         if (G % o[1] != 0) continue;
         const int64_t t = (((int64_t)N + 64 * o[0] - 1) / (64 * o[0])) * tm;
-        if (t >= cus) return GemmCfg{o[0], o[1], 0};
+        if (4 * t >= 3 * (int64_t)cus) return GemmCfg{o[0], o[1]};
         if (t > best_t) {
             best_t = t;
-            best = GemmCfg{o[0], o[1], 0};
+            best = GemmCfg{o[0], o[1]};
         }
     }
     return best;

@@ -50,6 +50,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for decode GEMV at M=1..32"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (no sparsity)
 ROTATION_BYTES = 1 << 30        # distinct copies per weight: at least this many bytes
 
 
@@ -134,6 +135,7 @@ class Call:
             wb *= 2
         out_b = 0 if kind == "argmax" else 2 * M * N
         self.bytes = wb + 2 * M * K + out_b
+        self.flops = 2 * M * N * K * (2 if kind in ("swiglu", "swiglu_affine") else 1)
         if kind == "argmax":
             self.val = torch.empty(M, dtype=torch.float32, device="cuda")
             self.idx = torch.empty(M, dtype=torch.int32, device="cuda")
@@ -141,6 +143,10 @@ class Call:
             self.ws = torch.empty(aqg.workspace_bytes(kindcode, M, N, K), dtype=torch.uint8, device="cuda")
         elif kind == "multi":
             self.out = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in parts]
+        elif kind == "gemm":
+            self.out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            self.ws = torch.empty(aqg.workspace_bytes(aqg.AQG_KIND_GEMM_AFFINE + bits, M, N, K),
+                                  dtype=torch.uint8, device="cuda")
         else:
             self.out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
@@ -162,6 +168,8 @@ class Call:
                                        workspace=self.ws)
             else:
                 aqg.gemv_bf16_argmax(self.x, w[0], out=(self.val, self.idx), workspace=self.ws)
+        elif k == "gemm":
+            aqg.gemm_affine(self.x, w[0], w[1], w[2], self.bits, out=self.out, workspace=self.ws)
         elif k == "multi":
             if self.bits:
                 mats = [tuple(w[3 * i:3 * i + 3]) for i in range(len(self.parts))]
@@ -268,6 +276,14 @@ def other_calls():
     for M in synth.AFFINE4_M:
         yield Call("multi_qkv", "attn_q_k_v", "multi", M, 3 * 1024, K, x, w, bits=4, parts=[1024] * 3)
     del w
+    # prompt chunks through the affine prompt GEMM (M > 32)
+    for name, N, K in synth.GEMM_SHAPES:
+        x = dev_bf16(synth.prompt_activations(synth.CFG_MIXED_WIDTH, K, max(synth.GEMM_M)))
+        for bits in (synth.GEMM_BITS if name == "wide_14336" else [4]):
+            w = Weights(affine_w(synth.CFG_MIXED_WIDTH, name, bits, N, K), affine_bytes(N, K, bits))
+            for M in synth.GEMM_M:
+                yield Call("prompt_gemm", name, "gemm", M, N, K, x, w, bits=bits)
+            del w
 
 
 def make_call(label):
@@ -284,7 +300,7 @@ def make_call(label):
     M = int(parts[2].split("=")[1])
     N, K = (int(v) for v in parts[3].split("x"))
     cfg = 9
-    x = dev_bf16(synth.normal_bf16((32, K), 1.0, cfg, "cc/x/%d" % K))
+    x = dev_bf16(synth.normal_bf16((max(32, M), K), 1.0, cfg, "cc/x/%d" % K))
 
     def affine_w(tag, n):
         aw = synth.affine_weight(cfg, tag, bits, n, K)
@@ -418,6 +434,10 @@ def measure(call, args, curve):
     us = time_call(call, args.calls)
     rec = dict(call.describe(), us=round(us, 3), GBps=round(call.bytes / us / 1e3, 1),
                frac=round(call.bytes / us / 1e3 / HBM_PEAK_GBPS, 4))
+    if call.kind == "gemm":
+        # a prompt GEMM is a dense contraction: also its matrix-core rate
+        rec["TFLOPs"] = round(call.flops / us / 1e6, 1)
+        rec["mfma_frac"] = round(call.flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)
     rec["hot_us"] = round(time_call_hot(call), 3)
     if curve:
         rec["curve_frac"] = round((curve["t0_us"] + call.bytes / (curve["bw_GBps"] * 1e3)) / us, 4)

@@ -290,9 +290,11 @@ int aqg_gemv_affine_q8_argmax(const void* x, const uint32_t* Wq, const void* sca
  *   required: the call writes x rearranged into matrix-core operands and
  *   the per-group sums of x there before the product reads them.
  * Accumulation is fp32 (per 64-code group: scale times the codes' dot
- * product, plus the bias and code-offset terms); each (m, n) is computed
- * the same way whatever M is.  The result is within the same bound of the
- * exact product as the GEMVs', but not bit-equal to them.
+ * product, plus the bias and code-offset terms).  Row m of y depends only on
+ * row m of x, W and the kernel's tiling, which is a function of ceil(M/64),
+ * N, K and the CU count: calls whose M round up to the same multiple of 64
+ * agree bit for bit on their common rows.  The result is within the same
+ * bound of the exact product as the GEMVs', but not bit-equal to them.
  * TensorFold PR #849 (format; the page also notes that its 8-bit modules
  * have no prompt GEMM and run prompts on the decode tiles).
  */
