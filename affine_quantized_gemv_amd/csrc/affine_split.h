@@ -1,7 +1,8 @@
-// Matrix-core kernel for affine GEMVs with 2-, 4- and 8-bit codes on small
+// Matrix-core kernel for affine GEMVs with 2- to 8-bit codes on small
 // matrices (few 16-row tiles) at M = 5..32 on gfx950: one workgroup per
-// 16-row tile and block of at most 16 columns, the row's 128-byte k-blocks
-// split over up to 16 wavefronts.
+// 16-row tile and block of at most 16 columns, the row's groups split over up
+// to 16 wavefronts (2, 4, 8 bits: in whole 128-byte k-blocks; 3, 5, 6, 7
+// bits: 2, 4 or 8 groups per wavefront).
 //
 // The matrices this serves are a few MB: latency-bound, so what matters is
 // how soon every CU has its loads in flight (as for the dense kernel in
@@ -13,6 +14,9 @@
 // of the codes (no LDS staging, no barrier before the arithmetic).  Per group
 // two MFMA k-steps on the codes placed as bf16 (128 + q; 8-bit codes as two
 // nibble chains, the high one weighted 16) give D = sum_k (C + q_k) x_k, and
+// (odd widths and 6 bits: each lane reads the words holding its 16-code
+// window of each group, lane quarter c taking codes 16c .. 16c + 15 in
+// natural k order, as affine_tile.h places them), and
 // the group adds scale * (D - D0) + bias * X with X = sum_k x_k, in fp32: the
 // factored form of sum_k x_k (scale * q_k + bias).  D0 is the same MFMA chain
 // on zero codes (C X as the matrix core computes it), formed once per group
@@ -26,6 +30,7 @@
 // layers at decode batch sizes.
 #pragma once
 #include "affine_mfma.h"
+#include "affine_tile.h"
 
 namespace aqg {
 namespace detail {
@@ -35,6 +40,15 @@ constexpr int kAffineSplitMaxWaves = 16;
 // codes, scales and biases: at most 8 wavefronts, so each may take 256
 // registers.
 template <int S> constexpr int affine_split_max_waves() { return S == 2 ? 8 : kAffineSplitMaxWaves; }
+
+// Widths read as per-lane code windows (no whole-line layout) and their
+// groups per unit of the KPW parameter (2, 4, 8 bits: a 128-byte k-block).
+template <int BITS> constexpr bool affine_split_natural() { return !(BITS == 2 || BITS == 4 || BITS == 8); }
+template <int BITS> constexpr int affine_split_gpk()
+{
+    if constexpr (affine_split_natural<BITS>()) return 1;
+    else return AffineMma<BITS>::GPK;
+}
 
 // NDW consecutive dwords at byte offset off of a buffer (16-, 8- and 4-byte
 // loads).
@@ -72,7 +86,8 @@ template <int BITS, int KPW, int CW = 0, int S = 1, bool SEG = false>
 __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split_kernel(ProjArgs a)
 {
     extern __shared__ float lds_red[];
-    constexpr int GPK = AffineMma<BITS>::GPK;     // groups per 128-byte k-block
+    constexpr bool NAT = affine_split_natural<BITS>();
+    constexpr int GPK = affine_split_gpk<BITS>();  // groups per unit of KPW
     constexpr int GPW = KPW * GPK;                // groups per wavefront
     constexpr int SDW = GPW / 2;                  // dwords of one row's scales (or biases) per wavefront
     static_assert(GPW % 2 == 0, "groups come in pairs");
@@ -112,22 +127,36 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
     const int r = lane & 15;
     const int64_t row_bytes = (int64_t)a.K * BITS / 8;
     const int gpr = a.K / 64;
-    const int kb0 = wave * KPW;                  // first k-block of this wavefront
+    const int kb0 = wave * KPW;                  // first k-block of this wavefront (odd widths: group)
     const int g0 = kb0 * GPK;                    // its first group
 
-    // codes: k-block p as two whole-line loads (rows 0..7 and 8..15)
-    const uint32_t voff = (uint32_t)((r & 7) * row_bytes + 16 * ((r < 8 ? 0 : 4) + c));
+    // codes (2, 4, 8 bits): k-block p as two whole-line loads (rows 0..7
+    // and 8..15); (other widths) each group's words holding lane quarter c's
+    // window of row r: NWN words from word (16 b c) / 32 of the group, the
+    // window starting at bit 0 or 16 of the first
+    constexpr int NWN = AffineTileWidth<BITS>::NWN;
+    const uint32_t voff = NAT ? (uint32_t)(r * row_bytes + 4 * ((16 * BITS * c) >> 5))
+                              : (uint32_t)((r & 7) * row_bytes + 16 * ((r < 8 ? 0 : 4) + c));
     const int half_off = (int)(8 * row_bytes);
-    u32x4_t wa[S][KPW][2];
+    u32x4_t wa[S][NAT ? 1 : KPW][2];
+    uint32_t wn[S][NAT ? GPW : 1][NWN];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const __amdgpu_buffer_rsrc_t rw =
             tile_rsrc(static_cast<const char*>(s == 0 ? w0_ : a.w1) + n0 * row_bytes, (N_ - n0) * row_bytes);
+        if constexpr (NAT) {
 #pragma unroll
-        for (int p = 0; p < KPW; ++p) {
-            const int koff = 128 * (kb0 + p);
-            wa[s][p][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff, kLoadNT));
-            wa[s][p][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff + half_off, kLoadNT));
+            for (int g = 0; g < GPW; ++g)
+#pragma unroll
+                for (int q = 0; q < NWN; ++q)
+                    wn[s][g][q] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff + 4 * q, (g0 + g) * 8 * BITS, kLoadNT);
+        } else {
+#pragma unroll
+            for (int p = 0; p < KPW; ++p) {
+                const int koff = 128 * (kb0 + p);
+                wa[s][p][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff, kLoadNT));
+                wa[s][p][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff + half_off, kLoadNT));
+            }
         }
     }
     // scales and biases of groups g0 .. g0 + GPW - 1 for rows 4c .. 4c + 3
@@ -159,8 +188,13 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
             float s0 = 0.f, s1 = 0.f;
-            xb[2 * g] = stage_x_operand<BITS>(xrow, 2 * g, c, s0);
-            xb[2 * g + 1] = stage_x_operand<BITS>(xrow, 2 * g + 1, c, s1);
+            if constexpr (NAT) {
+                xb[2 * g] = stage_x_natural(xrow, 2 * g, c, s0);
+                xb[2 * g + 1] = stage_x_natural(xrow, 2 * g + 1, c, s1);
+            } else {
+                xb[2 * g] = stage_x_operand<BITS>(xrow, 2 * g, c, s0);
+                xb[2 * g + 1] = stage_x_operand<BITS>(xrow, 2 * g + 1, c, s1);
+            }
             if (!have) {
                 xb[2 * g] = xb[2 * g + 1] = u32x4_t{0u, 0u, 0u, 0u};
                 s0 = s1 = 0.f;
@@ -177,9 +211,12 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
         }
     }
 
-    uint32_t cmask = AffineMma<BITS>::MASK, cbias = 0x43004300u;
+    uint32_t cmask = NAT ? AffineTileWidth<BITS>::MASK : AffineMma<NAT ? 4 : BITS>::MASK, cbias = 0x43004300u;
+    uint32_t cmaskh = AffineTileWidth<BITS>::MASK << 16;
     asm volatile("" : "+s"(cmask));      // no instruction: only hides the constants
+    asm volatile("" : "+s"(cmaskh));
     asm volatile("" : "+v"(cbias));
+    const uint32_t wsh = (uint32_t)((16 * BITS * c) & 31);   // odd widths: 0 or 16
     const bool hi8 = (lane & 8) != 0;
     f32x4_t acc[S];
 #pragma unroll
@@ -190,21 +227,32 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
     for (int s = 0; s < S; ++s) {
         // pc[0][t]: codes of k-step t of the block, pc[1][t]: k-step 4 + t
         uint32_t pc[2][4];
+        if constexpr (!NAT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t l0 = wa[s][p][0][i], l1 = wa[s][p][1][i];
-            const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l0, 0x128, 0xF, 0xF, false);
-            const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l1, 0x128, 0xF, 0xF, false);
-            pc[0][i] = hi8 ? r1 : l0;
-            pc[1][i] = hi8 ? l1 : r0;
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t l0 = wa[s][p][0][i], l1 = wa[s][p][1][i];
+                const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l0, 0x128, 0xF, 0xF, false);
+                const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)l1, 0x128, 0xF, 0xF, false);
+                pc[0][i] = hi8 ? r1 : l0;
+                pc[1][i] = hi8 ? l1 : r0;
+            }
+            transpose4x4_rows(pc[0]);
+            transpose4x4_rows(pc[1]);
         }
-        transpose4x4_rows(pc[0]);
-        transpose4x4_rows(pc[1]);
 #pragma unroll
         for (int gi = 0; gi < GPK; ++gi) {
             const int g = p * GPK + gi;          // group within the wavefront's range
             u32x4_t A0, A1, H0, H1;
-            if constexpr (BITS == 4) {
+            if constexpr (NAT) {
+                // the window normalised to start at bit 0 (only the low 16
+                // bits of the last word belong to it when it starts at 16)
+                uint32_t w[NWN];
+#pragma unroll
+                for (int q = 0; q + 1 < NWN; ++q) w[q] = __builtin_amdgcn_alignbit(wn[s][g][q + 1], wn[s][g][q], wsh);
+                w[NWN - 1] = wn[s][g][NWN - 1] >> wsh;
+                A0 = codes_window_to_bf16<BITS, 0>(w, cmask, cmaskh, cbias);
+                A1 = codes_window_to_bf16<BITS, 1>(w, cmask, cmaskh, cbias);
+            } else if constexpr (BITS == 4) {
                 A0 = codes4_to_bf16(pc[gi >> 1][2 * (gi & 1)], cmask, cbias);
                 A1 = codes4_to_bf16(pc[gi >> 1][2 * (gi & 1) + 1], cmask, cbias);
             } else if constexpr (BITS == 2) {
@@ -264,9 +312,20 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
 // k-blocks per wavefront: the smallest of 1, 2, 4 that splits the row's
 // 128-byte k-blocks over at most 16 wavefronts, with at most 8 groups per
 // wavefront (their x^T operands take 8 registers each; 0 if none fits).
+// Widths 3, 5, 6, 7: groups per wavefront, the smallest of 2, 4, 8 that
+// splits the row's groups evenly over at most max_waves wavefronts, with at
+// most 64 groups in the workgroup (more windows than that do not fit the
+// registers of 16 wavefronts; 0 if none).
 inline int affine_split_kpw(int bits, int K, int max_waves = kAffineSplitMaxWaves)
 {
-    if (!(bits == 2 || bits == 4 || bits == 8) || K % 64 != 0 || (K * bits) % 1024 != 0) return 0;
+    if (bits < 2 || bits > 8 || K % 64 != 0) return 0;
+    if (!(bits == 2 || bits == 4 || bits == 8)) {
+        const int G = K / 64;
+        for (int gpw : {2, 4, 8})
+            if (G % gpw == 0 && G / gpw <= max_waves && gpw * max_waves <= 64) return gpw;
+        return 0;
+    }
+    if ((K * bits) % 1024 != 0) return 0;
     const int kbl = K * bits / 1024;
     for (int kpw : {1, 2, 4})
         if (kbl % kpw == 0 && kbl / kpw <= max_waves) return kpw * (16 / bits) <= 8 ? kpw : 0;
@@ -277,10 +336,10 @@ template <int BITS, int KPW, int S, bool SEG>
 hipError_t launch_affine_split_seg(const ProjArgs& a, hipStream_t s)
 {
     if (a.M > 32) return hipErrorInvalidValue;
-    const int nks = (a.K * BITS / 1024) / KPW;
+    const int nks = affine_split_natural<BITS>() ? (a.K / 64) / KPW : (a.K * BITS / 1024) / KPW;
     const int64_t tiles = ((int64_t)a.N + 15) / 16;
     // partial tiles for the reduction (per stream), then each wavefront's code offsets
-    const size_t lds = (size_t)S * nks * 4 * 65 * 4 + (size_t)nks * KPW * AffineMma<BITS>::GPK * 16 * 4;
+    const size_t lds = (size_t)S * nks * 4 * 65 * 4 + (size_t)nks * KPW * affine_split_gpk<BITS>() * 16 * 4;
     // M = 17..32 runs once per 16-column block, and with at most half as many
     // row tiles as CUs M = 9..16 once per 8-column block (the two blocks of a
     // tile on one XCD).
@@ -316,16 +375,27 @@ template <int BITS, int S>
 hipError_t launch_affine_split_impl(const ProjArgs& a, const LaunchCfg& c, hipStream_t s)
 {
     (void)c;
-    constexpr int GPK = AffineMma<BITS>::GPK;
-    switch (affine_split_kpw(BITS, a.K, affine_split_max_waves<S>())) {
-        case 1: return launch_affine_split_one<BITS, 1, S>(a, s);
-        case 2:
-            if constexpr (2 * GPK <= 8) return launch_affine_split_one<BITS, 2, S>(a, s);
-            else return hipErrorInvalidValue;
-        case 4:
-            if constexpr (4 * GPK <= 8) return launch_affine_split_one<BITS, 4, S>(a, s);
-            else return hipErrorInvalidValue;
-        default: return hipErrorInvalidValue;
+    constexpr int GPK = affine_split_gpk<BITS>();
+    if constexpr (affine_split_natural<BITS>()) {
+        switch (affine_split_kpw(BITS, a.K, affine_split_max_waves<S>())) {
+            case 2: return launch_affine_split_one<BITS, 2, S>(a, s);
+            case 4: return launch_affine_split_one<BITS, 4, S>(a, s);
+            case 8:
+                if constexpr (S == 2) return launch_affine_split_one<BITS, 8, S>(a, s);
+                else return hipErrorInvalidValue;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (affine_split_kpw(BITS, a.K, affine_split_max_waves<S>())) {
+            case 1: return launch_affine_split_one<BITS, 1, S>(a, s);
+            case 2:
+                if constexpr (2 * GPK <= 8) return launch_affine_split_one<BITS, 2, S>(a, s);
+                else return hipErrorInvalidValue;
+            case 4:
+                if constexpr (4 * GPK <= 8) return launch_affine_split_one<BITS, 4, S>(a, s);
+                else return hipErrorInvalidValue;
+            default: return hipErrorInvalidValue;
+        }
     }
 }
 

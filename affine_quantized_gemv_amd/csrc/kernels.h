@@ -164,8 +164,9 @@ template <int BITS>
 hipError_t launch_affine_tile(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // Affine matrix-core launcher for small N, k split over one workgroup per
-// 16-row tile, BITS = 2, 4 or 8 (affine_split.hip; the fused SwiGLU over
-// affine gate and up matrices in affine_split_swiglu.hip).
+// 16-row tile, BITS = 2..8 (affine_split.hip, affine_split_odd.hip; the
+// fused SwiGLU over affine gate and up matrices in affine_split_swiglu.hip,
+// affine_split_odd_swiglu.hip).
 template <int BITS, bool SWIGLU>
 hipError_t launch_affine_split(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 

@@ -162,7 +162,15 @@ bool choose_affine_split(int bits, bool swiglu, int M, int N, int K, LaunchCfg& 
     c = LaunchCfg{};
     const int64_t tiles = ((int64_t)N + 15) / 16;
     const int maxw = swiglu ? detail::affine_split_max_waves<2>() : detail::affine_split_max_waves<1>();
-    if (M < 5 || M > 32 || tiles > ((M > 16 && !swiglu) ? 128 : 256) || detail::affine_split_kpw(bits, K, maxw) == 0)
+    // 3, 5, 6, 7 bits (per-lane code windows): from M = 1, and up to 256
+    // row tiles at any M: the dot-product kernels these replace spend most
+    // of their time unpacking (3584 x 1024 at M = 16: 14.2 -> 4.5 us, at
+    // M = 2: 5.7 -> 4.0 us; fused SwiGLU 2 x 4096 x 1536 at M = 32: 58 ->
+    // 12 us, at M = 2: 11.7 -> 7.3 us)
+    const bool nat = !(bits == 2 || bits == 4 || bits == 8);
+    const int min_m = nat ? 1 : 5;
+    const int64_t max_tiles = (M > 16 && !swiglu && !nat) ? 128 : 256;
+    if (M < min_m || M > 32 || tiles > max_tiles || detail::affine_split_kpw(bits, K, maxw) == 0)
         return false;
     c.path = PATH_AFFINE_SPLIT;
     c.MT = M <= 16 ? 16 : 32;
@@ -346,8 +354,8 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     if (swiglu && bits != 0) {
         // fused SwiGLU over affine gate and up matrices: both weight streams
         // through the same x operands, on the small-matrix matrix-core kernel
-        // from M = 5 (2, 4, 8 bits, at most 256 row tiles), else on the
-        // dot-product kernels
+        // (at most 256 row tiles; 2, 4, 8 bits from M = 5, the other widths
+        // from M = 2), else on the dot-product kernels
         if (choose_affine_split(bits, true, M, N, K, c)) return c;
         if (choose_piece(bits, true, M, N, K, c)) return c;
         if (choose_stream(bits, true, M, N, K, c)) return c;
@@ -382,6 +390,13 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     // issued at once (4-bit 1024 x 3584 at M = 16: 11.8 -> 7.3 us; 1024 x
     // 1024: 7.4 -> 4.0 us; 8-bit 4096 x 4096: 15.1 -> 14.2 us; 2- and 4-bit
     // 4096 x 4096 level with the tile kernel).
+    // (3, 5, 6, 7 bits: the tile kernel first where it serves, 0.5-1 us
+    // faster on 4096 x 4096 at M = 5..16)
+    // (and at M = 1 the streaming kernel where it serves: 3-bit 4096 x 4096
+    // 8.4 us against 9.3 us)
+    const bool nat = bits == 3 || bits == 5 || bits == 6 || bits == 7;
+    if (!swiglu && nat && M >= 5 && choose_affine_tile(bits, M, N, K, c)) return c;
+    if (!swiglu && nat && M == 1 && choose_stream(bits, false, M, N, K, c)) return c;
     if (!swiglu && choose_affine_split(bits, false, M, N, K, c)) return c;
     if (!swiglu && M >= 5 && choose_affine_tile(bits, M, N, K, c)) return c;
     if (!swiglu && M >= 3 && choose_affine_mfma(bits, M, N, K, c) &&
@@ -434,7 +449,11 @@ hipError_t launch_proj_table(int bits, bool swiglu, const ProjArgs& a, const Lau
     if (c.path == PATH_AFFINE_SPLIT) {
         switch (bits) {
             case 2: return swiglu ? launch_affine_split<2, true>(a, c, s) : launch_affine_split<2, false>(a, c, s);
+            case 3: return swiglu ? launch_affine_split<3, true>(a, c, s) : launch_affine_split<3, false>(a, c, s);
             case 4: return swiglu ? launch_affine_split<4, true>(a, c, s) : launch_affine_split<4, false>(a, c, s);
+            case 5: return swiglu ? launch_affine_split<5, true>(a, c, s) : launch_affine_split<5, false>(a, c, s);
+            case 6: return swiglu ? launch_affine_split<6, true>(a, c, s) : launch_affine_split<6, false>(a, c, s);
+            case 7: return swiglu ? launch_affine_split<7, true>(a, c, s) : launch_affine_split<7, false>(a, c, s);
             case 8: return swiglu ? launch_affine_split<8, true>(a, c, s) : launch_affine_split<8, false>(a, c, s);
             default: return hipErrorInvalidValue;
         }

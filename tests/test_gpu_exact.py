@@ -15,7 +15,8 @@ query must agree):
     bias is about -s 2^(b-1)) stay within the bound;
   * one-hot activations with s = 1, bias = 0 read single codes exactly, and
     with s = 2, bias = -1 give 2q - 1 exactly (the streaming kernel of 3-, 5-,
-    6- and 7-bit codes, which serves M <= 4 at K = 4096).
+    6- and 7-bit codes, which serves M <= 4 on matrices of more than 256 row
+    tiles at K = 4096, and M = 1 at 4096 rows and more).
 
 Format: TensorFold PR #849, "qwen3_5 cuda: mixed-width MLX checkpoints, 2 to
 8 bits in groups of 64" (MLX affine mode: value, scale and bias per group).
@@ -36,14 +37,16 @@ pytestmark = pytest.mark.gpu
 # (family, bits, M, N, K): one case per kernel family and width class
 CASES = [
     ("piece", 4, 1, 3000, 1024), ("piece", 2, 4, 3000, 1024), ("piece", 2, 8, 20000, 1024), ("piece", 8, 4, 3000, 1024),
-    ("stream", 3, 1, 2304, 4096), ("stream", 5, 4, 2304, 4096), ("stream", 6, 2, 2304, 4096),
+    ("stream", 3, 1, 2304, 4096), ("stream", 5, 4, 4400, 4096), ("stream", 6, 2, 4400, 4096),
     ("stream", 7, 1, 2304, 4096),
-    ("valu", 3, 9, 300, 1024), ("valu", 5, 32, 300, 1024),
+    ("valu", 3, 9, 300, 320), ("valu", 5, 32, 300, 320),
     ("affine_mfma", 4, 16, 40001, 1024), ("affine_mfma", 2, 12, 40001, 1024), ("affine_mfma", 8, 16, 40001, 3072),
     ("affine_mfma", 4, 4, 40001, 1024),
     ("affine_tile", 4, 16, 8000, 4096), ("affine_tile", 3, 8, 8000, 4096), ("affine_tile", 8, 16, 8000, 2048),
     ("affine_tile", 6, 32, 8000, 2048),
     ("affine_split", 4, 8, 1000, 1024), ("affine_split", 8, 16, 999, 4096), ("affine_split", 2, 32, 1000, 2048),
+    ("affine_split", 3, 4, 1000, 1024), ("affine_split", 5, 16, 999, 1536), ("affine_split", 6, 1, 512, 1024),
+    ("affine_split", 7, 32, 300, 3584),
 ]
 IDS = ["%s-q%d-M%d-%dx%d" % c for c in CASES]
 
@@ -141,11 +144,12 @@ def test_mlx_like_groups_within_bound(family, bits, M, N, K):
 @pytest.mark.parametrize("M", [1, 4])
 @pytest.mark.parametrize("bits", [3, 5, 6, 7])
 def test_stream_kernel_one_hot_exact(bits, M):
-    """The streaming kernel (3, 5, 6, 7 bits, N >= 2048 rows of K = 4096) reads
-    every code exactly: one-hot x with s = 1, bias = 0 gives q[n, col]; with
-    s = 2, bias = -1 it gives 2q - 1.  The columns cover every position of a
-    64-code group (including the codes that straddle two words)."""
-    N, K = 2304, 4096
+    """The streaming kernel (3, 5, 6, 7 bits, more than 256 row tiles of
+    K = 4096) reads every code exactly: one-hot x with s = 1, bias = 0 gives
+    q[n, col]; with s = 2, bias = -1 it gives 2q - 1.  The columns cover every
+    position of a 64-code group (including the codes that straddle two
+    words)."""
+    N, K = 4400, 4096
     _check_family("stream", bits, M, N, K)
     words = synth.random_words((N, K * bits // 32), 73, "ohs/%d" % bits)
     codes = oracle.unpack(words, bits, K).astype(np.float64)

@@ -456,10 +456,12 @@ def test_affine_one_hot_reads_codes_exactly(bits):
 @pytest.mark.parametrize("K", [1024, 3584])
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_affine_one_hot_every_group_position_m8(bits, K):
-    """M = 8 (streaming path) one-hot rows over all 64 positions of a group,
-    each in a different group of the row (K = 3584 at b = 4: the row's last
-    lane slot is ragged): y[m, n] = q[n, col_m] exactly.  Pins the in-GEMV
-    unpack of the streaming kernels for every code position."""
+    """M = 8 one-hot rows over all 64 positions of a group, each in a
+    different group of the row (K = 3584 at b = 4: the row's last lane slot
+    is ragged): y[m, n] = q[n, col_m] exactly.  Pins the in-GEMV unpack for
+    every code position on the path the shape takes at M = 8 (the piece
+    kernel for 2, 4 and 8 bits, the small-matrix matrix-core kernel for 3
+    bits; the failure message names it)."""
     N = 211
     words = synth.random_words((N, K * bits // 32), 78, "oh8/%d/%d" % (bits, K))
     codes = oracle.unpack(words, bits, K)
@@ -473,7 +475,8 @@ def test_affine_one_hot_every_group_position_m8(bits, K):
         x = np.zeros((8, K), np.uint16)
         x[np.arange(8), c] = 0x3F80
         y = run_guarded(gemv_affine_gpu(bf16_dev(x), wq, sd, bd, bits, 8), 8, N)
-        assert np.array_equal(y, codes[:, c].T.astype(np.float64)), "cols %s" % c
+        assert np.array_equal(y, codes[:, c].T.astype(np.float64)), \
+            "%s cols %s" % (aqg.dispatch_path(bits, 8, N, K)[0], c)
 
 
 @functools.lru_cache(maxsize=None)
@@ -618,7 +621,9 @@ def test_affine_matrix_core_2_and_8_bit(bits, N, K):
 @pytest.mark.parametrize("bits,N,K", [(4, 1000, 1024), (4, 3001, 2048), (4, 700, 3584), (4, 4090, 4096),
                                       (4, 300, 512), (4, 129, 256), (2, 1000, 4096), (2, 3000, 2048),
                                       (2, 999, 1536), (8, 2000, 1024), (8, 999, 4096), (8, 1000, 2048),
-                                      (4, 1000, 8192), (2, 500, 8192)])
+                                      (4, 1000, 8192), (2, 500, 8192),
+                                      (3, 1000, 1024), (5, 999, 1536), (6, 700, 3584), (7, 3000, 1024),
+                                      (3, 4090, 1536), (5, 300, 128)])
 def test_affine_split_path(bits, N, K):
     """Small matrices (at most 256 row tiles) on the matrix core with one
     workgroup per tile and K split over its wavefronts (8-bit K = 4096 and
@@ -627,11 +632,19 @@ def test_affine_split_path(bits, N, K):
     in two 16-column ones.  Ragged last tile; every M against the oracle
     (bf16 = RNE of fp32, no write outside the output) and bit for bit equal to
     the first rows of its bucket's widest call (16 or 32 rows), and the two
-    buckets to each other where both take this path."""
+    buckets to each other where both take this path.  3, 5, 6 and 7 bits
+    (per-lane code windows, 2 or 4 groups per wavefront) take it from M = 1
+    and up to 256 row tiles at every M."""
     x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
     ref, A = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
+    nat = bits in (3, 5, 6, 7)
     tops = {}
-    for M in (16, 5, 8, 9, 32, 17):
+    for M in ((16, 1, 2, 4, 5, 8, 9, 32, 17) if nat else (16, 5, 8, 9, 32, 17)):
+        path = aqg.dispatch_path(bits, M, N, K)[0]
+        if nat and M == 1 and path != "affine_split":
+            continue
+        if nat or M <= 16 or (N + 15) // 16 <= 128:
+            assert path == "affine_split", "M=%d" % M
         y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, M), M, N)
         assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q%d split %dx%dx%d" % (bits, M, N, K))
         b = 16 if M <= 16 else 32
@@ -639,17 +652,20 @@ def test_affine_split_path(bits, N, K):
             tops[b] = y
         else:
             assert np.array_equal(y, tops[b][:M]), "M=%d" % M
-    if (N + 15) // 16 <= 128:
+    if 32 in tops and aqg.dispatch_path(bits, 32, N, K)[0] == "affine_split":
         assert np.array_equal(tops[16], tops[32][:16])
 
 
-@pytest.mark.parametrize("bits,K", [(2, 4096), (4, 1024), (4, 3584), (8, 1024), (8, 4096)])
+@pytest.mark.parametrize("bits,K", [(2, 4096), (4, 1024), (4, 3584), (8, 1024), (8, 4096),
+                                    (3, 1024), (5, 1536), (6, 3584), (7, 1024), (7, 2048)])
 def test_affine_split_path_one_hot_exact(bits, K):
     """Split path (N = 1001: 63 row tiles), s = 1, bias = 0, one-hot x: y = q
     exactly with the ones at every position of a group, in every wavefront's
     k-blocks, for M = 16 (8-column workgroups) and 32 (16-column ones); then
     s = 2, bias = -1 on the same codes: y = 2 q - 1 exactly."""
     N = 1001
+    for MC in (16, 32):
+        assert aqg.dispatch_path(bits, MC, N, K)[0] == "affine_split"
     words = synth.random_words((N, K * bits // 32), 89, "soh/%d/%d" % (bits, K))
     codes = oracle.unpack(words, bits, K)
     G = K // 64
@@ -801,23 +817,28 @@ def test_affine_ragged_shapes(M, N, K, bits):
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_affine_rows_independent_of_m(bits):
-    """On 4096 x 4096, M <= 4 (streaming path, x in registers or LDS) matches
-    one-row calls bit for bit; M = 5..16 (tiles through LDS) match the 16-row
-    call and M = 17..32 the 32-row call bit for bit (the two buckets may take
-    different paths: 8-bit tiles of K = 4096 fit a CU's LDS only beside 16
-    columns)."""
+    """On 4096 x 4096, calls whose M the library serves with the same kernel
+    and column bucket (its dispatch query) agree bit for bit on their common
+    rows: the one-row call, and the widest M of each (path, columns) group.
+    The streaming and piece kernels (M <= 4 here for 2, 4, 8 bits and M = 1
+    for the others) compute each row on its own, so they also match one-row
+    calls."""
     name, N, K = synth.MIXED_SHAPES[0]
     x, aw, xd, wq, sd, bd = affine_case(synth.CFG_MIXED_WIDTH, name, bits, N, K)
-    y1 = torch.cat([aqg.gemv_affine(xd[m:m + 1], wq, sd, bd, bits, out_dtype=torch.float32)
-                    for m in range(4)]).cpu().numpy()
-    for M in (2, 3, 4):
-        yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
-        assert np.array_equal(yM, y1[:M]), "M=%d" % M
-    y16 = aqg.gemv_affine(xd[:16], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
-    for M in (5, 8, 9, 12):
-        yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
-        assert np.array_equal(yM, y16[:M]), "M=%d" % M
-    y32 = aqg.gemv_affine(xd[:32], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
-    for M in (17, 20):
-        yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
-        assert np.array_equal(yM, y32[:M]), "M=%d" % M
+    Ms = (1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 20, 32)
+    groups = {}
+    for M in Ms:
+        groups.setdefault(aqg.dispatch_path(bits, M, N, K), []).append(M)
+    y1 = aqg.gemv_affine(xd[:1], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
+    path1 = aqg.dispatch_path(bits, 1, N, K)[0]
+    for key, group in groups.items():
+        top = max(group)
+        ytop = aqg.gemv_affine(xd[:top], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
+        for M in group:
+            yM = aqg.gemv_affine(xd[:M], wq, sd, bd, bits, out_dtype=torch.float32).cpu().numpy()
+            assert np.array_equal(yM, ytop[:M]), "%s M=%d vs %d" % (key, M, top)
+        if key[0] in ("stream", "piece") and key[0] == path1:
+            rows = np.concatenate([aqg.gemv_affine(xd[m:m + 1], wq, sd, bd, bits, out_dtype=torch.float32)
+                                   .cpu().numpy() for m in range(top)])
+            assert np.array_equal(ytop, rows), "%s M=%d vs one-row calls" % (key, top)
+    assert len(groups) >= 2
