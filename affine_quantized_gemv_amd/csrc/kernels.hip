@@ -168,7 +168,7 @@ bool choose_affine_split(int bits, bool swiglu, int M, int N, int K, LaunchCfg& 
     // M = 2: 5.7 -> 4.0 us; fused SwiGLU 2 x 4096 x 1536 at M = 32: 58 ->
     // 12 us, at M = 2: 11.7 -> 7.3 us)
     const bool nat = !(bits == 2 || bits == 4 || bits == 8);
-    const int min_m = nat ? 1 : 5;
+    const int min_m = (nat || swiglu) ? 1 : 5;   // SwiGLU: the caller picks below M = 5
     const int64_t max_tiles = (M > 16 && !swiglu && !nat) ? 128 : 256;
     if (M < min_m || M > 32 || tiles > max_tiles || detail::affine_split_kpw(bits, K, maxw) == 0)
         return false;
@@ -354,10 +354,19 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     if (swiglu && bits != 0) {
         // fused SwiGLU over affine gate and up matrices: both weight streams
         // through the same x operands, on the small-matrix matrix-core kernel
-        // (at most 256 row tiles; 2, 4, 8 bits from M = 5, the other widths
-        // from M = 2), else on the dot-product kernels
-        if (choose_affine_split(bits, true, M, N, K, c)) return c;
-        if (choose_piece(bits, true, M, N, K, c)) return c;
+        // (at most 256 row tiles), else on the dot-product kernels
+        // 2, 4, 8 bits below M = 5: the matrix core where the piece kernel
+        // does not serve (2 x 4096 x 1536 on the streaming kernel at M = 1..4:
+        // 7.8-20.6 us, on the matrix core 6.4-6.7 us) and at M = 3, 4 for
+        // 4 and 8 bits (2 x 3584 x 1024 4-bit: 5.2 -> 5.0 us, 8-bit 7.5 ->
+        // 6.3 us); the piece kernel at M = 1, 2 (3.7 against 4.9 us) and for
+        // 2 bits (4.9 against 6.0 us at M = 4)
+        LaunchCfg cp;
+        const bool nat = !(bits == 2 || bits == 4 || bits == 8);
+        const bool piece = choose_piece(bits, true, M, N, K, cp);
+        if ((nat || M >= 5 || !piece || (M >= 3 && bits != 2)) && choose_affine_split(bits, true, M, N, K, c))
+            return c;
+        if (piece) return cp;
         if (choose_stream(bits, true, M, N, K, c)) return c;
         return choose_valu(bits, true, M, N, K);
     }
