@@ -216,7 +216,9 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
     int f_b = kb_lo;
     const int h = lane & 15;
     const uint32_t voff = (uint32_t)((h & 7) * row_bytes + 16 * ((h < 8 ? 0 : 4) + c));
-    const int half_off = (int)(8 * row_bytes);
+    // rows 8..15: the row offset goes in the vector offset, which is the
+    // part of the address the buffer range check covers
+    const uint32_t voff_hi = voff + (uint32_t)(8 * row_bytes);
     const uint32_t goff = BITS == 4 ? (uint32_t)(((lane >> 2) * gpr + (lane & 3)) * 2)
                         : BITS == 2 ? (uint32_t)(((lane >> 2) * gpr + 2 * (lane & 3)) * 2)
                                     : (uint32_t)((((lane >> 1) & 15) * gpr + (lane & 1)) * 2);
@@ -235,7 +237,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
             bw[d] = __builtin_amdgcn_raw_buffer_load_b16(rb, goff, 2 * GPK * f_b, kLoadNT);
         }
         wa[d][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, 128 * f_b, kLoadNT));
-        wa[d][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, 128 * f_b + half_off, kLoadNT));
+        wa[d][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff_hi, 128 * f_b, kLoadNT));
         const bool wrap = f_b + 1 == kb_hi;
         f_b = wrap ? kb_lo : f_b + 1;
         f_tile += wrap ? U : 0;

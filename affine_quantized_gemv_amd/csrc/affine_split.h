@@ -137,7 +137,9 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
     constexpr int NWN = AffineTileWidth<BITS>::NWN;
     const uint32_t voff = NAT ? (uint32_t)(r * row_bytes + 4 * ((16 * BITS * c) >> 5))
                               : (uint32_t)((r & 7) * row_bytes + 16 * ((r < 8 ? 0 : 4) + c));
-    const int half_off = (int)(8 * row_bytes);
+    // rows 8..15: the row offset goes in the vector offset, which is the
+    // part of the address the buffer range check covers
+    const uint32_t voff_hi = voff + (uint32_t)(8 * row_bytes);
     u32x4_t wa[S][NAT ? 1 : KPW][2];
     uint32_t wn[S][NAT ? GPW : 1][NWN];
 #pragma unroll
@@ -155,7 +157,7 @@ __global__ void __launch_bounds__(64 * affine_split_max_waves<S>()) affine_split
             for (int p = 0; p < KPW; ++p) {
                 const int koff = 128 * (kb0 + p);
                 wa[s][p][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff, kLoadNT));
-                wa[s][p][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, koff + half_off, kLoadNT));
+                wa[s][p][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, voff_hi, koff, kLoadNT));
             }
         }
     }

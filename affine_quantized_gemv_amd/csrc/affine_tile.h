@@ -161,7 +161,8 @@ __global__ void __launch_bounds__(64 * NWV) affine_tile_kernel(ProjArgs a)
 #pragma unroll
         for (int q = 0; q < L::CPW; ++q) {
             const int piece = wave * L::CPW + q;
-            copy_1k_to_lds(rw, dst + piece * 1040, (uint32_t)lane * 16, (uint32_t)piece * 1024);
+            // the piece's offset in the vector offset, which the range check covers
+            copy_1k_to_lds(rw, dst + piece * 1040, (uint32_t)(lane * 16 + piece * 1024), 0);
         }
         // only the first SBL lanes copy (a lane past a buffer's range still
         // writes zeros into LDS); lane 0 is always one of them, so each

@@ -78,7 +78,9 @@ __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(Pro
 
     // A: pair p covers k-steps s0 + 2p, s0 + 2p + 1 (64 k, 128 bytes per row)
     const uint32_t voff = (uint32_t)((h & 7) * row_bytes + 16 * ((h < 8 ? 0 : 4) + c));
-    const int half_off = (int)(8 * row_bytes);
+    // rows 8..15: the row offset goes in the vector offset, which is the
+    // part of the address the buffer range check covers
+    const uint32_t voff_hi = voff + (uint32_t)(8 * row_bytes);
     u32x4_t wa[NP][S][2];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -88,7 +90,7 @@ __global__ void __launch_bounds__(64 * kMfmaSplitMaxWaves) mfma_split_kernel(Pro
         for (int p = 0; p < NP; ++p) {
             const int koff = 64 * (s0 + 2 * p);  // bytes: 32 k per step, 2 bytes each
             wa[p][s][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, koff, kLoadNT));
-            wa[p][s][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, koff + half_off, kLoadNT));
+            wa[p][s][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff_hi, koff, kLoadNT));
         }
     }
     // B: lane (c, column r) of block b holds x[16b + r][32 s + 8c .. + 7]

@@ -78,7 +78,9 @@ __global__ void __launch_bounds__(kMfmaStreamThreads) mfma_stream_kernel(ProjArg
     int f_p = 0;                         // its k-step pair
     const int h = lane & 15;
     const uint32_t voff = (uint32_t)((h & 7) * row_bytes + 16 * ((h < 8 ? 0 : 4) + c));
-    const int half_off = (int)(8 * row_bytes);
+    // rows 8..15: the row offset goes in the vector offset, which is the
+    // part of the address the buffer range check covers
+    const uint32_t voff_hi = voff + (uint32_t)(8 * row_bytes);
     auto fetch = [&](auto Dd) __attribute__((always_inline)) {
         constexpr int d = decltype(Dd)::value;
         const int64_t n0 = f_tile * 16;
@@ -88,7 +90,7 @@ __global__ void __launch_bounds__(kMfmaStreamThreads) mfma_stream_kernel(ProjArg
             const __amdgpu_buffer_rsrc_t rs =
                 tile_rsrc(static_cast<const char*>(s == 0 ? a.w0 : a.w1) + n0 * row_bytes, bytes);
             wa[d][s][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 128 * f_p, kLoadNT));
-            wa[d][s][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 128 * f_p + half_off, kLoadNT));
+            wa[d][s][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff_hi, 128 * f_p, kLoadNT));
         }
         // advance (tile, pair) without branches: wave-uniform selects
         const bool wrap = f_p + 1 == KP;

@@ -147,7 +147,8 @@ __global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
         for (int q = 0; q < L::CPW; ++q) {
             const int piece = wave * L::CPW + q;
             const int row = piece / L::CPR, col = piece - row * L::CPR;
-            copy_1k_to_lds(rs, dst + row * L::RS + col * 1024, (uint32_t)lane * 16, (uint32_t)piece * 1024);
+            // the piece's offset in the vector offset, which the range check covers
+            copy_1k_to_lds(rs, dst + row * L::RS + col * 1024, (uint32_t)(lane * 16 + piece * 1024), 0);
         }
     };
 
