@@ -628,6 +628,7 @@ const char* aqg_path_name(int path)
         case aqg::PATH_MFMA_TILE: return "mfma_tile";
         case aqg::PATH_AFFINE_TILE: return "affine_tile";
         case aqg::PATH_AFFINE_SPLIT: return "affine_split";
+        case aqg::PATH_AFFINE_BURST: return "affine_burst";
         case aqg::PATH_AFFINE_GEMM: return "affine_gemm";
         default: return "unknown";
     }

@@ -109,7 +109,7 @@ __host__ __device__ inline SegView seg_view(const ProjArgs& a, int64_t n0)
 }
 
 enum Path { PATH_VALU = 0, PATH_MFMA = 1, PATH_STREAM = 2, PATH_PIECE = 3, PATH_MFMA_STREAM = 4, PATH_MFMA_SPLIT = 5, PATH_AFFINE_MFMA = 6,
-            PATH_MFMA_TILE = 7, PATH_AFFINE_TILE = 8, PATH_AFFINE_SPLIT = 9, PATH_AFFINE_GEMM = 10 };
+            PATH_MFMA_TILE = 7, PATH_AFFINE_TILE = 8, PATH_AFFINE_SPLIT = 9, PATH_AFFINE_GEMM = 10, PATH_AFFINE_BURST = 11 };
 
 // Launch geometry chosen for a call.
 struct LaunchCfg {
@@ -169,6 +169,12 @@ hipError_t launch_affine_tile(const ProjArgs& a, const LaunchCfg& c, hipStream_t
 // affine_split_odd_swiglu.hip).
 template <int BITS, bool SWIGLU>
 hipError_t launch_affine_split(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
+
+// Multi-tile affine matrix-core launcher at K = 4096 (1-4 row tiles per
+// workgroup, all loads in flight at once; M = 17..32 as two 16-column
+// launches), BITS = 2..8 (affine_burst.hip, affine_burst_odd.hip).
+template <int BITS>
+hipError_t launch_affine_burst(const ProjArgs& a, const LaunchCfg& c, hipStream_t s);
 
 // Affine matrix-core launcher, BITS = 2, 4 or 8 (affine_mfma*.hip).
 template <int BITS>

@@ -5,10 +5,12 @@
 // wide small-N ones from M = 3 on and for short ones with K <= 2048 from
 // M = 5 on; affine
 // matrix-core kernels for 2-, 4- and 8-bit codes (affine_mfma*.hip; on small
-// matrices from M = 5 on, affine_split.hip) and, where a K fits their LDS
-// ring, for every width from M = 5 on (affine_tile_b*.hip); plus the
-// code-unpack kernel.
+// matrices from M = 5 on, affine_split.hip), at K = 4096 the multi-tile
+// kernel where it measured fastest (affine_burst*.hip) and, where a K fits
+// their LDS ring, for every width from M = 5 on (affine_tile_b*.hip); plus
+// the code-unpack kernel.
 #include "affine_mfma.h"
+#include "affine_burst.h"
 #include "affine_split.h"
 #include "affine_tile.h"
 #include "mfma_split.h"
@@ -169,12 +171,70 @@ bool choose_affine_split(int bits, bool swiglu, int M, int N, int K, LaunchCfg& 
     // 12 us, at M = 2: 11.7 -> 7.3 us)
     const bool nat = !(bits == 2 || bits == 4 || bits == 8);
     const int min_m = (nat || swiglu) ? 1 : 5;   // SwiGLU: the caller picks below M = 5
-    const int64_t max_tiles = (M > 16 && !swiglu && !nat) ? 128 : 256;
+    // (M = 17..32 up to 256 tiles where no 32-column tile ring serves:
+    // 8-bit 4096 x 4096 at M = 32: 25.7 us against 290 on the VALU kernel)
+    const int64_t max_tiles =
+        (M > 16 && !swiglu && !nat && detail::affine_tile_supported(bits, N, K, 32)) ? 128 : 256;
     if (M < min_m || M > 32 || tiles > max_tiles || detail::affine_split_kpw(bits, K, maxw) == 0)
         return false;
     c.path = PATH_AFFINE_SPLIT;
     c.MT = M <= 16 ? 16 : 32;
     c.KT = K;
+    c.R = 1;
+    return true;
+}
+
+// Multi-tile affine geometry (affine_burst.h): K = 4096, at most 4 row tiles
+// per workgroup on one CU each (up to 1024 tiles on 256 CUs), where it was
+// measured fastest (us, against the kernel the shape ran on before; 4096 x
+// 4096 = 256 tiles, 14336 x 4096 = 896):
+//   2 bits from M = 3 (14336 x 4096 at M = 4: 11.5 against 16.2, M = 8:
+//     11.8 against 14.2, M = 16: 13.1 against 15.3), at M = 2 on up to 256
+//     tiles (4096 x 4096: 5.9 against 6.6);
+//   4 bits from M = 3 (4096 x 4096 at M = 4: 7.2 against 9.0, M = 16: 8.8
+//     against 9.5; 14336 x 4096 at M = 8: 14.5 against 15.0);
+//   5 bits at M <= 2 on up to 256 tiles (M = 1: 9.9 against 10.5);
+//   6, 7 bits at M = 3, 4 (14336 x 4096: 23.9 against 26.4, 25.8 against
+//     29.3) and on up to 256 tiles at M <= 4 (6 bits) or M <= 2 (7 bits:
+//     10.6 against 12.6 at M = 1);
+//   8 bits at M = 3, 4 (14336 x 4096 at M = 4: 24.1 against 27.2) and on
+//     more than 256 tiles from M = 5 (24.5 against 25.9 at M = 8), also at
+//     M = 17..32 as two 16-column launches (no tile ring holds 32 columns
+//     of 8-bit K = 4096 rows);
+//   never at 3 bits (the per-lane windows load slower than the tile and
+//     streaming kernels read them).
+// Depends on (bits, N, K) and M: every M it serves computes each output
+// the same way (16 columns per launch).
+bool affine_burst_measured(int bits, int M, int64_t tiles)
+{
+    const bool small = tiles <= 256;
+    switch (bits) {
+        case 2: return M >= 3 || (M == 2 && small);
+        case 4: return M >= 3;
+        case 5: return small && M <= 2;
+        case 6: return (M >= 3 && M <= 4) || (small && M <= 4);
+        case 7: return (M >= 3 && M <= 4) || (small && M <= 2);
+        case 8: return (M >= 3 && M <= 4) || (M >= 5 && !small);
+        default: return false;
+    }
+}
+
+bool choose_affine_burst(int bits, int M, int N, int K, LaunchCfg& c)
+{
+    c = LaunchCfg{};
+    const int64_t tiles = ((int64_t)N + 15) / 16;
+    int cus = 256;
+    if (detail::device_cus(cus) != hipSuccess) cus = 256;
+    if (!detail::affine_burst_supported(bits, N, K) || tiles > (int64_t)detail::kAffineBurstMaxTiles * cus) return false;
+    // (fewer than 192 tiles: not measured here, the one-tile-per-workgroup
+    // kernels keep them)
+    if (tiles < 192) return false;
+    if (M > 16 && !(bits == 8 && tiles > 256)) return false;
+    if (M <= 16 && !affine_burst_measured(bits, M, tiles)) return false;
+    c.path = PATH_AFFINE_BURST;
+    c.MT = 16;
+    c.KT = K;
+    c.nwaves = 8;
     c.R = 1;
     return true;
 }
@@ -404,6 +464,7 @@ LaunchCfg choose_config(int bits, bool swiglu, int M, int N, int K)
     // (and at M = 1 the streaming kernel where it serves: 3-bit 4096 x 4096
     // 8.4 us against 9.3 us)
     const bool nat = bits == 3 || bits == 5 || bits == 6 || bits == 7;
+    if (!swiglu && choose_affine_burst(bits, M, N, K, c)) return c;
     if (!swiglu && nat && M >= 5 && choose_affine_tile(bits, M, N, K, c)) return c;
     if (!swiglu && nat && M == 1 && choose_stream(bits, false, M, N, K, c)) return c;
     if (!swiglu && choose_affine_split(bits, false, M, N, K, c)) return c;
@@ -452,6 +513,19 @@ hipError_t launch_proj_table(int bits, bool swiglu, const ProjArgs& a, const Lau
             case 6: return launch_affine_tile<6>(a, c, s);
             case 7: return launch_affine_tile<7>(a, c, s);
             case 8: return launch_affine_tile<8>(a, c, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (c.path == PATH_AFFINE_BURST) {
+        if (swiglu) return hipErrorInvalidValue;
+        switch (bits) {
+            case 2: return launch_affine_burst<2>(a, c, s);
+            case 3: return launch_affine_burst<3>(a, c, s);
+            case 4: return launch_affine_burst<4>(a, c, s);
+            case 5: return launch_affine_burst<5>(a, c, s);
+            case 6: return launch_affine_burst<6>(a, c, s);
+            case 7: return launch_affine_burst<7>(a, c, s);
+            case 8: return launch_affine_burst<8>(a, c, s);
             default: return hipErrorInvalidValue;
         }
     }

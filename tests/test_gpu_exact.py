@@ -15,8 +15,9 @@ query must agree):
     bias is about -s 2^(b-1)) stay within the bound;
   * one-hot activations with s = 1, bias = 0 read single codes exactly, and
     with s = 2, bias = -1 give 2q - 1 exactly (the streaming kernel of 3-, 5-,
-    6- and 7-bit codes, which serves M <= 4 on matrices of more than 256 row
-    tiles at K = 4096, and M = 1 at 4096 rows and more).
+    6- and 7-bit codes, which serves M <= 4 (6 and 7 bits: M <= 2) on
+    matrices of more than 256 row tiles at K = 4096, and M = 1 at 4096 rows
+    and more; the multi-tile kernel in the burst tests of test_gpu_parity).
 
 Format: TensorFold PR #849, "qwen3_5 cuda: mixed-width MLX checkpoints, 2 to
 8 bits in groups of 64" (MLX affine mode: value, scale and bias per group).
@@ -42,8 +43,10 @@ CASES = [
     ("valu", 3, 9, 300, 320), ("valu", 5, 32, 300, 320),
     ("affine_mfma", 4, 16, 40001, 1024), ("affine_mfma", 2, 12, 40001, 1024), ("affine_mfma", 8, 16, 40001, 3072),
     ("affine_mfma", 4, 4, 40001, 1024),
-    ("affine_tile", 4, 16, 8000, 4096), ("affine_tile", 3, 8, 8000, 4096), ("affine_tile", 8, 16, 8000, 2048),
-    ("affine_tile", 6, 32, 8000, 2048),
+    ("affine_tile", 4, 16, 8000, 2048), ("affine_tile", 3, 8, 8000, 4096), ("affine_tile", 8, 16, 8000, 2048),
+    ("affine_tile", 6, 32, 8000, 2048), ("affine_tile", 2, 16, 20000, 4096),
+    ("affine_burst", 2, 8, 8001, 4096), ("affine_burst", 4, 3, 8000, 4096), ("affine_burst", 8, 32, 8000, 4096),
+    ("affine_burst", 7, 4, 4100, 4096), ("affine_burst", 6, 1, 4000, 4096), ("affine_burst", 5, 2, 3500, 4096),
     ("affine_split", 4, 8, 1000, 1024), ("affine_split", 8, 16, 999, 4096), ("affine_split", 2, 32, 1000, 2048),
     ("affine_split", 3, 4, 1000, 1024), ("affine_split", 5, 16, 999, 1536), ("affine_split", 6, 1, 512, 1024),
     ("affine_split", 7, 32, 300, 3584),
@@ -141,11 +144,11 @@ def test_mlx_like_groups_within_bound(family, bits, M, N, K):
     print(family, bits, metrics(y, ref, A))
 
 
-@pytest.mark.parametrize("M", [1, 4])
-@pytest.mark.parametrize("bits", [3, 5, 6, 7])
+@pytest.mark.parametrize("bits,M", [(3, 1), (3, 4), (5, 1), (5, 4), (6, 1), (6, 2), (7, 1), (7, 2)])
 def test_stream_kernel_one_hot_exact(bits, M):
     """The streaming kernel (3, 5, 6, 7 bits, more than 256 row tiles of
-    K = 4096) reads every code exactly: one-hot x with s = 1, bias = 0 gives
+    K = 4096; 6 and 7 bits at M = 3, 4 run on the multi-tile kernel) reads
+    every code exactly: one-hot x with s = 1, bias = 0 gives
     q[n, col]; with s = 2, bias = -1 it gives 2q - 1.  The columns cover every
     position of a 64-code group (including the codes that straddle two
     words)."""

@@ -618,7 +618,7 @@ def test_affine_matrix_core_2_and_8_bit(bits, N, K):
         assert np.array_equal(y16, y32[:16])
 
 
-@pytest.mark.parametrize("bits,N,K", [(4, 1000, 1024), (4, 3001, 2048), (4, 700, 3584), (4, 4090, 4096),
+@pytest.mark.parametrize("bits,N,K", [(4, 1000, 1024), (4, 3001, 2048), (4, 700, 3584), (4, 3000, 4096),
                                       (4, 300, 512), (4, 129, 256), (2, 1000, 4096), (2, 3000, 2048),
                                       (2, 999, 1536), (8, 2000, 1024), (8, 999, 4096), (8, 1000, 2048),
                                       (4, 1000, 8192), (2, 500, 8192),
@@ -696,29 +696,104 @@ def test_affine_tile_path(bits, N, K):
     x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
     ref, A = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
     Ms = (16, 5, 9) if (bits == 8 and K == 4096) else (32, 5, 9, 16, 17)
-    top = None
+    by_path = {}
     for M in Ms:
         y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, M), M, N)
-        assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q%d tile %dx%dx%d" % (bits, M, N, K))
-        if top is None:
-            top = y
-        else:
+        path = aqg.dispatch_path(bits, M, N, K)[0]
+        assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q%d %s %dx%dx%d" % (bits, path, M, N, K))
+        by_path.setdefault(path, {})[M] = y
+    assert "affine_tile" in by_path or (bits, K) in ((2, 4096), (4, 4096), (8, 4096))
+    # (2-, 4- and 8-bit K = 4096 run on the multi-tile kernel up to 16 columns)
+    for runs in by_path.values():
+        top = runs[max(runs)]
+        for M, y in runs.items():
             assert np.array_equal(y, top[:M]), "M=%d" % M
 
 
 @pytest.mark.parametrize("bits,N", [(4, 8000), (2, 8000), (5, 8000), (2, 20000), (4, 20000)])
 def test_affine_tile_path_several_tiles_per_workgroup(bits, N):
-    """Tile path with 1-2 (N = 8000: 500 row tiles) and 4-5 (N = 20000) tiles
-    per workgroup at K = 4096, M = 16.  The ring's first tiles are issued in
-    two parts (tile 0 before x is staged, the rest after), so the waits of
-    the first steps depend on how many tiles a workgroup has; each count is
-    checked against the oracle."""
+    """Several row tiles per workgroup at K = 4096, M = 16: N = 8000 (500
+    tiles: 1-2 per workgroup; 2 and 4 bits on the multi-tile kernel, 5 bits
+    on the tile ring) and N = 20000 (1250 tiles: 4-5 per workgroup on the tile
+    ring, more than the multi-tile kernel takes).  The tile ring's first
+    tiles are issued in two parts (tile 0 before x is staged, the rest
+    after), so the waits of the first steps depend on how many tiles a
+    workgroup has; each count is checked against the oracle."""
     K = 4096
     x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
     xs = x[:16]
     ref, A = oracle.gemv_affine(xs, aw.words, aw.scales, aw.biases, bits)
     y = run_guarded(gemv_affine_gpu(xd[:16], wq, sd, bd, bits, 16), 16, N)
     assert_within(y, ref, oracle.tolerance(A), "q%d tile 16x%dx%d" % (bits, N, K))
+
+
+def burst_ms(bits, N):
+    """The M <= 16 the multi-tile kernel serves for this width and N."""
+    return [M for M in (16, 1, 2, 3, 4, 5, 8, 9) if aqg.dispatch_path(bits, M, N, 4096)[0] == "affine_burst"]
+
+
+@pytest.mark.parametrize("bits,N", [(b, N) for b in (2, 4, 5, 6, 7, 8) for N in (3990, 14350)
+                                    if (b, N) != (5, 14350)])
+def test_affine_burst_path(bits, N):
+    """Multi-tile kernel at K = 4096 (all of a workgroup's 1-4 row tiles in
+    flight, codes straight into the MFMA lanes, bias and code-offset terms as
+    an MFMA pair on exact bf16 pieces): N = 3990 (250 tiles, one per
+    workgroup) and 14350 (897 tiles, 3-4 per workgroup), both with a ragged
+    last tile.  Every M it serves against the oracle (bf16 = RNE of fp32, no
+    write outside the output) and bit for bit equal to the first rows of
+    its widest call; 8 bits at M = 17 and 32 (two 16-column launches) as
+    well, the first 16 rows equal to the M = 16 call."""
+    K = 4096
+    Ms = burst_ms(bits, N)
+    assert Ms, "no M of q%d %dx%d on the multi-tile kernel" % (bits, N, K)
+    x, aw, xd, wq, sd, bd = affine_mma_case(bits, N, K)
+    ref, A = oracle.gemv_affine(x, aw.words, aw.scales, aw.biases, bits)
+    runs = {}
+    for M in Ms:
+        y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, M), M, N)
+        assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q%d burst %dx%dx%d" % (bits, M, N, K))
+        runs[M] = y
+    top = runs[max(runs)]
+    for M, y in runs.items():
+        assert np.array_equal(y, top[:M]), "M=%d" % M
+    if bits == 8 and N > 4096:
+        for M in (32, 17):
+            assert aqg.dispatch_path(bits, M, N, K)[0] == "affine_burst"
+            y = run_guarded(gemv_affine_gpu(xd, wq, sd, bd, bits, M), M, N)
+            assert_within(y, ref[:M], oracle.tolerance(A[:M]), "q%d burst %dx%dx%d" % (bits, M, N, K))
+            if 16 in runs:
+                assert np.array_equal(y[:16], runs[16]), "M=%d" % M
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5, 6, 7, 8])
+def test_affine_burst_one_hot_exact(bits):
+    """Multi-tile kernel (N = 3990, K = 4096), s = 1, bias = 0, one-hot x: y
+    = q exactly with the ones at every position of a group and in every
+    wavefront's groups, at the widest M it serves; then s = 2, bias = -1 on
+    the same codes: y = 2 q - 1 exactly (the bias and offset MFMA pair
+    reproduces bias * X and cancels the code offset exactly here).  8 bits
+    also at M = 32 on N = 14350 (two 16-column launches)."""
+    K = 4096
+    G = K // 64
+    cols = np.array([((r * 5 + 3) % G) * 64 + r for r in range(64)])
+    for N in ((3990, 14350) if bits == 8 else (3990,)):
+        MC = 32 if N > 3990 else max(burst_ms(bits, N))
+        assert aqg.dispatch_path(bits, MC, N, K)[0] == "affine_burst"
+        words = synth.random_words((N, K * bits // 32), 91, "roh/%d/%d" % (bits, N))
+        codes = oracle.unpack(words, bits, K)
+        wq = u32_dev(words)
+        for sv, bv in ((0x3F80, 0x0000), (0x4000, 0xBF80)):
+            sd = bf16_dev(np.full((N, G), sv, np.uint16))
+            bd = bf16_dev(np.full((N, G), bv, np.uint16))
+            want_s = oracle.bf16_to_f64(np.array([sv], np.uint16))[0]
+            want_b = oracle.bf16_to_f64(np.array([bv], np.uint16))[0]
+            for c0 in range(0, 64, MC):
+                c = cols[c0:c0 + MC]
+                x = np.zeros((len(c), K), np.uint16)
+                x[np.arange(len(c)), c] = 0x3F80
+                y = run_guarded(gemv_affine_gpu(bf16_dev(x), wq, sd, bd, bits, len(c)), len(c), N)
+                want = (want_s * codes[:, c] + want_b).T.astype(np.float64)
+                assert np.array_equal(y, want), "q%d N=%d M=%d cols %s" % (bits, N, len(c), c)
 
 
 @pytest.mark.parametrize("bits,K", [(2, 4096), (4, 2048), (8, 1024), (8, 4096), (3, 4096), (5, 4096), (6, 2048),
