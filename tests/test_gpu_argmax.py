@@ -153,7 +153,8 @@ def test_affine4_planted_max_and_ties(M):
 @pytest.mark.parametrize("bits,M,N,K", [(0, 8, 1536, 1536), (0, 20, 4096, 1536), (3, 4, 50000, 1024),
                                         (5, 16, 20000, 4096), (2, 12, 3000, 1024), (8, 32, 999, 4096),
                                         (0, 3, 40007, 1024), (4, 17, 40001, 1024), (2, 1, 33333, 2048),
-                                        (8, 5, 700, 512)])
+                                        (8, 5, 700, 512), (2, 8, 14350, 4096), (8, 24, 14350, 4096),
+                                        (4, 3, 3990, 4096)])
 def test_argmax_other_shapes(bits, M, N, K):
     x = synth.normal_bf16((M, K), 1.0, 60, "am/x/%d" % K)
     xd = bf16_dev(x)
