@@ -160,7 +160,7 @@ int run_gemm(int bits, const void* x, const uint32_t* Wq, const void* scales, co
     if (M <= 0 || N <= 0 || K <= 0) return AQG_ERR_INVALID_ARG;
     if (out_dtype != AQG_OUT_BF16 && out_dtype != AQG_OUT_F32) return AQG_ERR_INVALID_ARG;
     if (M > AQG_GEMM_MAX_M || K % 64 != 0) return AQG_ERR_UNSUPPORTED;
-    const size_t need = aqg::gemm_workspace_bytes(bits, M, K);
+    const size_t need = aqg::gemm_workspace_base(bits, M, K);
     if (!ws || wsb < need) return AQG_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(Wq, 16) || !aligned(ws, 16)) return AQG_ERR_ALIGNMENT;
     if (!aligned(scales, 4) || !aligned(biases, 4)) return AQG_ERR_ALIGNMENT;
@@ -176,6 +176,20 @@ int run_gemm(int bits, const void* x, const uint32_t* Wq, const void* scales, co
     if (overlap(ws, need, y, ybytes)) return AQG_ERR_INVALID_ARG;
     int st = check_device();
     if (st != AQG_OK) return st;
+    // tiling and K split for this device; the split only where the workspace
+    // also holds its partial products (and they overlap no argument)
+    int cus = 256;
+    if (aqg::detail::device_cus(cus) != hipSuccess) cus = 256;
+    const aqg::GemmCfg g = aqg::choose_gemm(M, N, K, cus);
+    int ks = aqg::gemm_ksplit(M, N, K, g, cus);
+    const size_t pb = aqg::gemm_part_bytes(M, N, ks);
+    if (ks > 1 && wsb < need + pb) ks = 1;
+    if (ks > 1) {
+        const void* part = static_cast<char*>(ws) + need;
+        for (int i = 0; i < 4; ++i)
+            if (overlap(part, pb, in[i], inb[i])) return AQG_ERR_INVALID_ARG;
+        if (overlap(part, pb, y, ybytes)) return AQG_ERR_INVALID_ARG;
+    }
 
     aqg::GemmArgs a{};
     a.x = static_cast<const uint16_t*>(x);
@@ -192,6 +206,9 @@ int run_gemm(int bits, const void* x, const uint32_t* Wq, const void* scales, co
     a.Gp = (a.G + 31) / 32 * 32;
     a.Mp = (M + aqg::kGemmTileM - 1) / aqg::kGemmTileM * aqg::kGemmTileM;
     a.out_f32 = out_dtype == AQG_OUT_F32;
+    a.wn = g.wn;
+    a.ks = ks;
+    a.part = ks > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + need) : nullptr;
     return finish(launch_gemm_bits(bits, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -459,7 +476,7 @@ size_t aqg_workspace_bytes(int kind, int M, int N, int K)
 {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     if (kind >= AQG_KIND_GEMM_AFFINE + 2 && kind <= AQG_KIND_GEMM_AFFINE + 8)
-        return M > AQG_GEMM_MAX_M || K % 64 != 0 ? 0 : aqg::gemm_workspace_bytes(kind - AQG_KIND_GEMM_AFFINE, M, K);
+        return M > AQG_GEMM_MAX_M || K % 64 != 0 ? 0 : aqg::gemm_workspace_bytes(kind - AQG_KIND_GEMM_AFFINE, M, N, K);
     if (M > 32) return 0;
     if (kind == AQG_KIND_ARGMAX_DENSE || (kind >= AQG_KIND_ARGMAX_DENSE + 2 && kind <= AQG_KIND_ARGMAX_DENSE + 8))
         return argmax_plan(kind - AQG_KIND_ARGMAX_DENSE, M, N, K).bytes;

@@ -285,8 +285,11 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
     const int64_t tile = (gridDim.x % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
     const int64_t n0 = (tile / TM) * L::ROWS;
     const int m0 = (int)(tile % TM) * kGemmTileM;
-    const int GC = a.G / WK;            // groups (stages) per chunk
-    const int g0 = kc * GC;             // this wavefront's first group
+    // blockIdx.y: this workgroup's share of the groups when the tile is split
+    // over a.ks workgroups (their partial products are summed afterwards)
+    const int GC = a.G / (WK * a.ks);   // groups (stages) per chunk
+    const int zb = (int)blockIdx.y * WK * GC;   // first group of this workgroup
+    const int g0 = zb + kc * GC;        // this wavefront's first group
     const int64_t row_bytes = (int64_t)a.K * BITS / 8;
     const int64_t rows_here = (int64_t)a.N - n0 < L::ROWS ? (int64_t)a.N - n0 : L::ROWS;
 
@@ -306,7 +309,7 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
     const uint32_t code_tstride = (uint32_t)(16 * row_bytes);
     const int j = threadIdx.x;
     const int jmb = j / 128, jh = (j / 64) % 2, jl = j % 64;
-    const uint32_t x_off = (uint32_t)(((jmb * a.G + 0) * 2 + jh) * 1024 + jl * 16);
+    const uint32_t x_off = (uint32_t)(((jmb * a.G + zb) * 2 + jh) * 1024 + jl * 16);
     const uint32_t s_off = (uint32_t)((((int64_t)64 * wn + lane) * a.G + g0) * 2);
 
     auto load = [&](int i, GemmStage<BITS, WK>& st) __attribute__((always_inline)) {
@@ -398,8 +401,8 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
     }
 
     // sum_g (b X - s D0): units (32-group block j, piece p), chunk kc taking
-    // p = kc, kc + WK, ...
-    {
+    // p = kc, kc + WK, ...; all groups, in the first share of a split tile
+    if (blockIdx.y == 0) {
         const bool even = (a.G & 1) == 0;
         const int NJ = a.Gp / 32;
         for (int j = 0; j < NJ; ++j) {
@@ -450,7 +453,30 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
     }
 
     // store: lane (c, r) holds rows n .. n + 3 of column m of each 16 x 16 tile
+    // (a split tile: this share's fp32 partial products)
     const bool vec = (a.N & 3) == 0;
+    if (a.ks > 1) {
+        float* part = a.part + (size_t)blockIdx.y * a.M * a.N;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t n = n0 + 64 * wn + 16 * t + 4 * c;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = m0 + 16 * mb + r;
+                if (m >= a.M || n >= a.N) continue;
+                float* y = part + (int64_t)m * a.N + n;
+                const f32x4_t v = acc[t][mb];
+                if (vec) {
+                    *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < a.N) y[e] = v[e];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int64_t n = n0 + 64 * wn + 16 * t + 4 * c;
@@ -488,9 +514,21 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
 
 // ------------------------------------------------------------ host side
 
-struct GemmCfg {
-    int wn, wk;
-};
+// Sum of the ks partial products of every output, in share order 0, 1, ...,
+// ks - 1, then the output rounding.
+// (a template, like every kernel of this header, so each width's unit
+// instantiates its own copy)
+template <int BITS>
+__global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmArgs a)
+{
+    const int64_t MN = (int64_t)a.M * a.N;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= MN) return;
+    float v = a.part[i];
+    for (int z = 1; z < a.ks; ++z) v += a.part[(int64_t)z * MN + i];
+    if (a.out_f32) static_cast<float*>(a.y)[i] = v;
+    else static_cast<uint16_t*>(a.y)[i] = f32_to_bf16_rne(v);
+}
 
 // Stages in flight: as many as the registers allow beside the 64 x 64 tile
 // (a stage is 4 NWW code words, WK x pieces and a scale per lane).
@@ -510,32 +548,13 @@ hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t s)
     hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(fn), L::LDS);
     if (e != hipSuccess) return e;
     const int64_t T = (((int64_t)a.N + L::ROWS - 1) / L::ROWS) * (a.Mp / kGemmTileM);
-    if (T > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3((unsigned)T), dim3(64 * kGemmWaves), L::LDS, s, a);
+    if (T > 0x7FFFFFFF || a.ks < 1 || a.G % (WK * a.ks) != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3((unsigned)T, (unsigned)a.ks), dim3(64 * kGemmWaves), L::LDS, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.ks == 1) return e;
+    const int64_t MN = (int64_t)a.M * a.N;
+    hipLaunchKernelGGL(gemm_reduce_kernel<BITS>, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
-}
-
-// Split of the 8 wavefronts: (WN, WK) = (8, 1), (4, 2) or (2, 4).  The widest
-// tile that still gives three quarters of the CUs a workgroup (measured: at
-// 512 x 14336 x 4096, 224 workgroups of (8, 1) beat 448 of (4, 2) by 10 %),
-// else the one with the most workgroups (WK must divide the groups per row).
-inline GemmCfg choose_gemm(int M, int N, int K, int cus)
-{
-    const int G = K / 64;
-    const int64_t tm = ((int64_t)M + kGemmTileM - 1) / kGemmTileM;
-    const int opts[3][2] = {{8, 1}, {4, 2}, {2, 4}};
-    GemmCfg best{8, 1};
-    int64_t best_t = -1;
-    for (const auto& o : opts) {
-        if (G % o[1] != 0) continue;
-        const int64_t t = (((int64_t)N + 64 * o[0] - 1) / (64 * o[0])) * tm;
-        if (4 * t >= 3 * (int64_t)cus) return GemmCfg{o[0], o[1]};
-        if (t > best_t) {
-            best_t = t;
-            best = GemmCfg{o[0], o[1]};
-        }
-    }
-    return best;
 }
 
 template <int BITS>
@@ -545,9 +564,7 @@ hipError_t launch_affine_gemm_impl(const GemmArgs& a, hipStream_t s)
     hipLaunchKernelGGL(gemm_prep_kernel<BITS>, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int cus = 256;
-    if (device_cus(cus) != hipSuccess) cus = 256;
-    const GemmCfg g = choose_gemm(a.M, a.N, a.K, cus);
+    const GemmCfg g{a.wn, 8 / a.wn};
     if (g.wn == 8) return launch_gemm_cfg<BITS, 8, 1>(a, s);
     if (g.wn == 4) return launch_gemm_cfg<BITS, 4, 2>(a, s);
     return launch_gemm_cfg<BITS, 2, 4>(a, s);

@@ -206,6 +206,9 @@ struct GemmArgs {
     int Gp;                   // G rounded up to 32
     int Mp;                   // M rounded up to 64
     int out_f32;
+    int wn;                   // 64-row blocks of W per tile: 8, 4 or 2 (8 / wn chunks of K)
+    int ks;                   // groups split over ks workgroups per tile (1: no split)
+    float* part;              // ks > 1: fp32 partial products [ks][M][N]
 };
 
 constexpr int kGemmTileM = 64;      // rows of x per tile
@@ -215,7 +218,7 @@ __host__ __device__ constexpr int gemm_pieces(int bits) { return bits == 8 ? 3 :
 
 // Workspace of a prompt GEMM: the x operands (Mp K bf16), then, from the
 // next 256-byte boundary, the pieces.
-inline size_t gemm_workspace_bytes(int bits, int M, int K)
+inline size_t gemm_workspace_base(int bits, int M, int K)
 {
     const size_t Mp = ((size_t)M + kGemmTileM - 1) / kGemmTileM * kGemmTileM;
     const size_t G = (size_t)K / 64, Gp = (G + 31) / 32 * 32;
@@ -226,6 +229,70 @@ inline size_t gemm_pieces_offset(int M, int K)
 {
     const size_t Mp = ((size_t)M + kGemmTileM - 1) / kGemmTileM * kGemmTileM;
     return (Mp * K * 2 + 255) / 256 * 256;
+}
+
+// Split of the 8 wavefronts of a prompt-GEMM workgroup: 64 WN rows of W per
+// tile, K in WK chunks.
+struct GemmCfg {
+    int wn, wk;
+};
+
+// (WN, WK) = (8, 1), (4, 2) or (2, 4).  The widest tile that still gives three
+// quarters of the CUs a workgroup (measured: at 512 x 14336 x 4096, 224
+// workgroups of (8, 1) beat 448 of (4, 2) by 10 %), else the one with the most
+// workgroups (WK must divide the groups per row).
+inline GemmCfg choose_gemm(int M, int N, int K, int cus)
+{
+    const int G = K / 64;
+    const int64_t tm = ((int64_t)M + kGemmTileM - 1) / kGemmTileM;
+    const int opts[3][2] = {{8, 1}, {4, 2}, {2, 4}};
+    GemmCfg best{8, 1};
+    int64_t best_t = -1;
+    for (const auto& o : opts) {
+        if (G % o[1] != 0) continue;
+        const int64_t t = (((int64_t)N + 64 * o[0] - 1) / (64 * o[0])) * tm;
+        if (4 * t >= 3 * (int64_t)cus) return GemmCfg{o[0], o[1]};
+        if (t > best_t) {
+            best_t = t;
+            best = GemmCfg{o[0], o[1]};
+        }
+    }
+    return best;
+}
+
+// Workgroups per tile that split its groups when the tiles alone leave more
+// than a quarter of the CUs idle (1024-row matrices): the smallest ks = 2..8
+// that fills three quarters of the CUs with at least 2 groups per wavefront
+// chunk (ks WK must divide the groups), else the largest such ks; 1 when
+// none fits.  Each tile's ks partial products are summed by a second kernel
+// in a fixed order.
+inline int gemm_ksplit(int M, int N, int K, GemmCfg g, int cus)
+{
+    const int G = K / 64;
+    const int64_t T = (((int64_t)N + 64 * g.wn - 1) / (64 * g.wn)) * (((int64_t)M + kGemmTileM - 1) / kGemmTileM);
+    if (4 * T >= 3 * (int64_t)cus) return 1;
+    int best = 1;
+    for (int ks = 2; ks <= 8; ++ks) {
+        if (G % (g.wk * ks) != 0 || G / (g.wk * ks) < 2) continue;
+        best = ks;
+        if (4 * T * ks >= 3 * (int64_t)cus) break;
+    }
+    return best;
+}
+
+// Bytes of the partial products when the tiles are split ks ways.
+inline size_t gemm_part_bytes(int M, int N, int ks)
+{
+    return ks > 1 ? ((size_t)ks * M * N * 4 + 255) / 256 * 256 : 0;
+}
+
+// Workspace that lets a prompt GEMM use its K split on a full 256-CU gfx950:
+// the base (x operands, pieces) plus the partial products.  A workspace of at
+// least the base is accepted; the split is used only where the partials fit.
+inline size_t gemm_workspace_bytes(int bits, int M, int N, int K)
+{
+    const GemmCfg g = choose_gemm(M, N, K, 256);
+    return gemm_workspace_base(bits, M, K) + gemm_part_bytes(M, N, gemm_ksplit(M, N, K, g, 256));
 }
 
 // Affine prompt GEMM, BITS = 2..8 (affine_gemm_b*.hip): the pre-pass over x,

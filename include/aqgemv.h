@@ -51,7 +51,8 @@
  *    prompt GEMMs).
  *    aqg_workspace_bytes() gives the size a call needs; NULL / 0 is valid
  *    when that size is 0, otherwise a smaller workspace is
- *    AQG_ERR_INVALID_ARG.
+ *    AQG_ERR_INVALID_ARG (the prompt GEMMs also accept less, down to what
+ *    their operands need: see there).
  *  - Accumulation is fp32; the result of each (m, n) does not depend on M
  *    within one code path (rows are independent).
  *  - Thread safety: stateless apart from a per-device architecture check that
@@ -284,17 +285,22 @@ int aqg_gemv_affine_q8_argmax(const void* x, const uint32_t* Wq, const void* sca
  * for any number of activation rows M in [1, AQG_GEMM_MAX_M] (prompt chunks;
  * for M <= 32 the GEMVs above are the faster call).  Same arrays, layouts,
  * alignment and out_dtype rules as the GEMVs; K % 64 == 0.
- *   workspace: device memory of at least
- *   aqg_workspace_bytes(AQG_KIND_GEMM_AFFINE + b, M, N, K) bytes (about
- *   2 M K bytes; 16-byte aligned, not overlapping any other argument),
- *   required: the call writes x rearranged into matrix-core operands and
- *   the per-group sums of x there before the product reads them.
+ *   workspace: device memory, 16-byte aligned, not overlapping any other
+ *   argument: the call writes x rearranged into matrix-core operands and the
+ *   per-group sums of x there (about 2 M K bytes, always required), and,
+ *   when the row tiles alone would leave a quarter of the CUs idle (N of a
+ *   few thousand rows), splits each tile's groups over 2..8 workgroups whose
+ *   fp32 partial products (ks M N 4 bytes) it sums in a fixed order.
+ *   aqg_workspace_bytes(AQG_KIND_GEMM_AFFINE + b, M, N, K) is the size with
+ *   the split on a full 256-CU gfx950; a smaller workspace that still holds
+ *   the operands is accepted and runs without the split.
  * Accumulation is fp32 (per 64-code group: scale times the codes' dot
  * product, plus the bias and code-offset terms).  Row m of y depends only on
  * row m of x, W and the kernel's tiling, which is a function of ceil(M/64),
- * N, K and the CU count: calls whose M round up to the same multiple of 64
- * agree bit for bit on their common rows.  The result is within the same
- * bound of the exact product as the GEMVs', but not bit-equal to them.
+ * N, K, the CU count and whether the workspace holds the split's partial
+ * products: such calls agree bit for bit on their common rows.  The result
+ * is within the same bound of the exact product as the GEMVs', but not
+ * bit-equal to them.
  * TensorFold PR #849 (format; the page also notes that its 8-bit modules
  * have no prompt GEMM and run prompts on the decode tiles).
  */

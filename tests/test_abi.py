@@ -274,11 +274,57 @@ def gemm_ws_closed_form(bits, M, K):
     return up(Mp * K * 2) + up((3 if bits == 8 else 6) * Mp * Gp * 2)
 
 
+def gemm_split_closed_form(M, N, K, cus=256):
+    """Workgroups per tile splitting its groups, as the header states it: the
+    wavefront split (WN, WK) in (8, 1), (4, 2), (2, 4), the widest giving
+    three quarters of the CUs a tile, else the one with the most tiles; then,
+    if the tiles leave more than a quarter of the CUs idle, the smallest ks in
+    2..8 that fills three quarters with at least 2 groups per wavefront chunk
+    (ks WK dividing the groups), else the largest such ks."""
+    G = K // 64
+    tm = -(-M // 64)
+    best, best_t = (8, 1), -1
+    for wn, wk in ((8, 1), (4, 2), (2, 4)):
+        if G % wk:
+            continue
+        t = -(-N // (64 * wn)) * tm
+        if 4 * t >= 3 * cus:
+            best, best_t = (wn, wk), t
+            break
+        if t > best_t:
+            best, best_t = (wn, wk), t
+    wn, wk = best
+    T = -(-N // (64 * wn)) * tm
+    if 4 * T >= 3 * cus:
+        return 1
+    ks = 1
+    for k in range(2, 9):
+        if G % (wk * k) or G // (wk * k) < 2:
+            continue
+        ks = k
+        if 4 * T * k >= 3 * cus:
+            break
+    return ks
+
+
+def gemm_ws_full(bits, M, N, K):
+    ks = gemm_split_closed_form(M, N, K)
+    part = -(-ks * M * N * 4 // 256) * 256 if ks > 1 else 0
+    return gemm_ws_closed_form(bits, M, K) + part
+
+
 @pytest.mark.parametrize("bits", range(2, 9))
 def test_gemm_workspace_bytes(bits):
+    """The size query: the operands (always required) plus, where the tiles
+    are split, the partial products; 14336-row matrices are never split, the
+    1024- and 3584-row ones of the prompt shapes are."""
     kind = aqg.AQG_KIND_GEMM_AFFINE + bits
     for M, K in [(1, 64), (33, 1024), (64, 1536), (65, 4096), (512, 4096), (1000, 3584)]:
-        assert aqg.workspace_bytes(kind, M, 100, K) == gemm_ws_closed_form(bits, M, K)
+        for N in (100, 1024, 3584, 14336):
+            assert aqg.workspace_bytes(kind, M, N, K) == gemm_ws_full(bits, M, N, K), (M, N, K)
+    assert gemm_split_closed_form(128, 14336, 4096) == 1
+    assert gemm_split_closed_form(128, 1024, 3584) == 7
+    assert gemm_split_closed_form(128, 3584, 1024) == 2
     assert aqg.workspace_bytes(kind, 0, 100, 1024) == 0
     assert aqg.workspace_bytes(kind, 33, 100, 96) == 0               # K not a multiple of 64
     assert aqg.workspace_bytes(kind, aqg.GEMM_MAX_M + 1, 100, 64) == 0
