@@ -14,7 +14,10 @@ which takes any M) within |y - y_ref| <= 2e-3 sum|w||x| + 1e-6:
     write lands outside y (canary words on both sides);
   * a row's result does not depend on the other rows of x (bit for bit,
     between M values that share a tiling), and one workspace serves calls of
-    different M in a row.
+    different M in a row;
+  * small matrices whose tiles split their groups over several workgroups
+    (partials in the workspace) and the same call with a workspace too small
+    for the partials (run unsplit) are both within the bound.
 Inputs: synth's mixed-width weight recipe (codes uniform in [0, 2^b - 1],
 scales U(0.001, 0.02), biases U(-0.1, 0.1)) and x ~ N(0, 1), bf16.
 """
@@ -125,3 +128,33 @@ def test_gemm_workspace_reused_across_sizes():
         aqg.gemm_affine(xd[:M], wd[0], wd[1], wd[2], bits, out=shared, workspace=ws)
         aqg.gemm_affine(xd[:M], wd[0], wd[1], wd[2], bits, out=fresh)
         assert torch.equal(shared, fresh), M
+
+
+def test_gemm_split_and_unsplit_both_within_the_bound():
+    """1024 x 3584 at M = 128: with the workspace the size query gives, each
+    tile's groups are split over several workgroups (fp32 partial products,
+    summed in a fixed order); with a workspace of only the operands' size the
+    call is accepted and runs unsplit.  Every output of both within the bound
+    of the oracle, and each repeatable bit for bit."""
+    import test_abi
+    bits, N, K, M = 4, 1024, 3584, 128
+    w, wd = weight("split/%dx%d" % (N, K), bits, N, K)
+    x = synth.prompt_activations(CFG, K, M)
+    xd = bf16_dev(x)
+    full = aqg.workspace_bytes(aqg.AQG_KIND_GEMM_AFFINE + bits, M, N, K)
+    base = test_abi.gemm_ws_closed_form(bits, M, K)
+    assert test_abi.gemm_split_closed_form(M, N, K) > 1 and full > base
+    ref, A = oracle.gemv_affine(x, w.words, w.scales, w.biases, bits)
+    fn = aqg.load().aqg_gemm_affine_q4
+    for name, nbytes in (("split", full), ("unsplit", base)):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        runs = []
+        for _ in range(2):
+            out = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            st = fn(aqg._p(xd), aqg._p(wd[0]), aqg._p(wd[1]), aqg._p(wd[2]), aqg._p(out), M, N, K,
+                    aqg.AQG_OUT_F32, aqg._p(ws), nbytes, None)
+            torch.cuda.synchronize()
+            assert st == 0, (name, st)
+            runs.append(out.cpu().numpy().astype(np.float64))
+        assert np.array_equal(runs[0], runs[1]), name
+        assert_within(runs[0], ref, oracle.tolerance(A), "gemm q4 %s %dx%dx%d" % (name, M, N, K))
