@@ -302,28 +302,49 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
 
     // code words: row 64 wn + 16 t + r of the tile, word (16 b c) / 32 of
     // the group; x pieces: thread j loads piece j of each chunk's
-    // [mb][k-step][lane] block; scale: row 64 wn + lane
+    // [mb][k-step][lane] block; scale: row 64 wn + lane.  The lane's part
+    // (row, position in the group) is the vector offset, which the range
+    // check covers (rows past N read zeros).  For 2-, 4- and 8-bit codes the
+    // group's offset (and the stage's offsets of x and the scales), the same
+    // for the whole wavefront, is the scalar offset, so a stage costs no
+    // address arithmetic; for the other widths (groups of 24 to 56 bytes)
+    // that measured much slower (5 bits, 14336 x 4096 at 512 rows: 231 us
+    // against 138 us), so there it stays in the vector offset.
+    constexpr bool SOFF = BITS == 2 || BITS == 4 || BITS == 8;
     const int bit0 = 16 * BITS * c;
     const uint32_t sh = (uint32_t)(bit0 & 31);
-    const uint32_t code_off = (uint32_t)((64 * wn + r) * row_bytes + (int64_t)g0 * L::GB + 4 * (bit0 >> 5));
+    const uint32_t code_off = (uint32_t)((64 * wn + r) * row_bytes + (SOFF ? 0 : (int64_t)g0 * L::GB) + 4 * (bit0 >> 5));
     const uint32_t code_tstride = (uint32_t)(16 * row_bytes);
     const int j = threadIdx.x;
     const int jmb = j / 128, jh = (j / 64) % 2, jl = j % 64;
     const uint32_t x_off = (uint32_t)(((jmb * a.G + zb) * 2 + jh) * 1024 + jl * 16);
-    const uint32_t s_off = (uint32_t)((((int64_t)64 * wn + lane) * a.G + g0) * 2);
+    const uint32_t s_off = (uint32_t)(((int64_t)64 * wn + lane) * a.G * 2);
 
     auto load = [&](int i, GemmStage<BITS, WK>& st) __attribute__((always_inline)) {
-        const uint32_t ci = code_off + (uint32_t)(i * L::GB);
+        const uint32_t cs = SOFF ? (uint32_t)((g0 + i) * L::GB) : 0u;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t vo = code_off + (SOFF ? 0u : (uint32_t)(i * L::GB)) + t * code_tstride;
+            if constexpr (BITS == 4) {          // 8 bytes at 8 c: one aligned 8-byte load
+                const u32x2v_t v = __builtin_bit_cast(u32x2v_t, __builtin_amdgcn_raw_buffer_load_b64(rw, vo, cs, 0));
+                st.cw[t][0] = v[0];
+                st.cw[t][1] = v[1];
+            } else if constexpr (BITS == 8) {   // 16 bytes at 16 c
+                const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, vo, cs, 0));
 #pragma unroll
-            for (int q = 0; q < NWW; ++q)
-                st.cw[t][q] = __builtin_amdgcn_raw_buffer_load_b32(rw, ci + t * code_tstride + 4 * q, 0, 0);
+                for (int q = 0; q < 4; ++q) st.cw[t][q] = v[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < NWW; ++q)
+                    st.cw[t][q] = __builtin_amdgcn_raw_buffer_load_b32(rw, vo + 4 * q, cs, 0);
+            }
+        }
 #pragma unroll
         for (int q = 0; q < WK; ++q)
             st.xo[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                rx, x_off + (uint32_t)((q * GC + i) * 2048), 0, 0));
-        st.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off + (uint32_t)(2 * i), 0, 0);
+                rx, x_off + (SOFF ? 0u : (uint32_t)((q * GC + i) * 2048)), SOFF ? (uint32_t)((q * GC + i) * 2048) : 0u, 0));
+        st.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off + (SOFF ? 0u : (uint32_t)(2 * (g0 + i))),
+                                                     SOFF ? (uint32_t)(2 * (g0 + i)) : 0u, 0);
     };
     auto put_x = [&](int buf, const GemmStage<BITS, WK>& st) __attribute__((always_inline)) {
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(gemm_lds + buf * L::XOP);
@@ -379,11 +400,20 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
     // D stages in flight: the loads of group i + D go out before group i is
     // computed; group i + 1's x pieces go to LDS after it.  The ring is
     // indexed with constants only (unrolled R times), so it stays in
-    // registers.
+    // registers.  Every load is unconditional (a stage past the chunk's
+    // last group reloads that group, a cache hit): a load under a branch
+    // makes the compiler wait for every load in flight where the paths
+    // join, which would drain the ring at each stage.  Only the arithmetic
+    // of the stages past the end is skipped, and the LDS writes after it
+    // go to the buffer nobody reads any more.
+    // (issued stage by stage, in the loop's order: the wait for a stage's
+    // data counts the loads issued after it, and where the first pass joins
+    // the loop the compiler takes the smaller count of the two paths)
     GemmStage<BITS, WK> ring[R];
     static_for<0, D>([&](auto Uc) __attribute__((always_inline)) {
         constexpr int u = decltype(Uc)::value;
-        if (u < GC) load(u, ring[u]);
+        load(u < GC ? u : GC - 1, ring[u]);
+        __builtin_amdgcn_sched_barrier(0);
     });
     put_x(0, ring[0]);
     __syncthreads();
@@ -391,12 +421,10 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
         static_for<0, R>([&](auto Uc) __attribute__((always_inline)) {
             constexpr int u = decltype(Uc)::value;
             const int i = base + u;
-            if (i < GC) {   // uniform over the workgroup
-                if (i + D < GC) load(i + D, ring[(u + D) % R]);
-                compute(i, ring[u]);
-                if (i + 1 < GC) put_x((i + 1) & 1, ring[(u + 1) % R]);
-                __syncthreads();
-            }
+            load(i + D < GC ? i + D : GC - 1, ring[(u + D) % R]);
+            if (i < GC) compute(i, ring[u]);   // uniform over the workgroup
+            put_x((i + 1) & 1, ring[(u + 1) % R]);
+            __syncthreads();
         });
     }
 
