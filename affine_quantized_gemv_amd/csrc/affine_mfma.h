@@ -151,10 +151,15 @@ __host__ __device__ inline size_t affine_mfma_wave_bytes(int gps)
     return 256 + (size_t)16 * gps * 2;
 }
 
-template <int BITS, int MT, int D, int GPS>
+// XR: the x^T operands and code offsets of the whole row held in registers
+// (4-bit codes, K = 1024, 16 columns, no K split: then the ring's slot d
+// always holds k-block d of a tile, so they are indexed with constants).
+template <int BITS, int MT, int D, int GPS, bool XR>
 __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArgs a)
 {
     extern __shared__ u32x4_t lds_a4[];
+    constexpr int XRS = XR ? 32 : 1;   // k-steps held in registers
+    static_assert(!XR || (BITS == 4 && MT == 16 && D == 4), "register x: 4-bit codes, K = 1024, 16 columns");
     constexpr int NB = MT / 16;
     constexpr int NW = kAffineMfmaThreads / 64;
     constexpr int PER_TILE = 16 * MT;
@@ -243,6 +248,10 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
         f_tile += wrap ? U : 0;
     };
 
+    // XR: the row's x^T operands (k-steps 0..31) and code offsets (groups
+    // 0..15) of the lane's column, from LDS once the prologue has staged them
+    u32x4_t xr[XRS];
+    float zr[XR ? 16 : 1];
     f32x4_t acc[NB], accb[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = accb[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -332,9 +341,11 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
             }
             const int S0 = 2 * (GPK * c_b + gi);
             const float* d0g = xs + (size_t)(GPK * c_b + gi) * MT + r;   // code offsets of the group's columns
+            const int GX = XR ? GPK * d + gi : 0;                          // the group (XR: c_b == d)
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const u32x4_t B0 = xb[(S0 * NB + b) * 64 + lane], B1 = xb[((S0 + 1) * NB + b) * 64 + lane];
+                const u32x4_t B0 = XR ? xr[2 * GX] : xb[(S0 * NB + b) * 64 + lane];
+                const u32x4_t B1 = XR ? xr[2 * GX + 1] : xb[((S0 + 1) * NB + b) * 64 + lane];
                 f32x4_t dg = mfma16x16x32(A0, B0, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 dg = mfma16x16x32(A1, B1, dg);
                 if constexpr (BITS == 8) {
@@ -343,7 +354,7 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
 #pragma unroll
                     for (int i = 0; i < 4; ++i) dg[i] = fmaf(16.0f, dh[i], dg[i]);
                 }
-                const float z = d0g[16 * b];
+                const float z = XR ? zr[GX] : d0g[16 * b];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(sc[i], dg[i] - z, acc[b][i]);
             }
@@ -515,6 +526,12 @@ __global__ void __launch_bounds__(kAffineMfmaThreads) affine_mfma_kernel(ProjArg
     // pending staging load out of the loop's waits.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    if constexpr (XR) {
+#pragma unroll
+        for (int S = 0; S < XRS; ++S) xr[S] = xb[S * 64 + lane];
+#pragma unroll
+        for (int g = 0; g < 16; ++g) zr[g] = xs[g * MT + r];
+    }
     // without a K split nothing below waits for the other wavefronts
     if (nkc == 1 && my_tiles == 0) {
         if (a.amx && lane < kArgmaxRows) amx_store(a.amx, a.amx_slots, u, lane, amx_neutral_value(), kAmxNoIndex);
@@ -607,10 +624,11 @@ inline void affine_mfma_geometry(int64_t T, int nkc, int cus, int bpc, int& bloc
     tmax = (T + (int64_t)blocks * ts - 1) / ((int64_t)blocks * ts);
 }
 
-template <int BITS, int MT, int GPS>
+template <int BITS, int MT, int GPS, bool XR = false>
 hipError_t launch_affine_mfma_one(const ProjArgs& a, int nkc, hipStream_t s)
 {
-    const void* fn = reinterpret_cast<const void*>(&affine_mfma_kernel<BITS, MT, kAffineMfmaDepth, GPS>);
+    if (XR && (a.K != 1024 || nkc != 1)) return hipErrorInvalidValue;
+    const void* fn = reinterpret_cast<const void*>(&affine_mfma_kernel<BITS, MT, kAffineMfmaDepth, GPS, XR>);
     {
         hipError_t e = raise_lds_limit(fn, kMfmaStreamLdsMax);
         if (e != hipSuccess) return e;
@@ -641,7 +659,7 @@ hipError_t launch_affine_mfma_one(const ProjArgs& a, int nkc, hipStream_t s)
     int lk = 0;
     while ((1 << lk) < nkc) ++lk;
     a2.ksplit_log2 = lk;
-    hipLaunchKernelGGL((affine_mfma_kernel<BITS, MT, kAffineMfmaDepth, GPS>), dim3(blocks), dim3(kAffineMfmaThreads), lds, s, a2);
+    hipLaunchKernelGGL((affine_mfma_kernel<BITS, MT, kAffineMfmaDepth, GPS, XR>), dim3(blocks), dim3(kAffineMfmaThreads), lds, s, a2);
     return hipGetLastError();
 }
 
@@ -654,7 +672,10 @@ hipError_t launch_affine_mfma_impl(const ProjArgs& a, const LaunchCfg& c, hipStr
     const bool w = c.MT == 16;
     switch (affine_mfma_gps(a.K, BITS, nkc)) {
         case 8: return w ? launch_affine_mfma_one<BITS, 16, 8>(a, nkc, s) : launch_affine_mfma_one<BITS, 32, 8>(a, nkc, s);
-        case 16: return w ? launch_affine_mfma_one<BITS, 16, 16>(a, nkc, s) : launch_affine_mfma_one<BITS, 32, 16>(a, nkc, s);
+        case 16:
+            if constexpr (BITS == 4)
+                if (w && a.K == 1024 && nkc == 1) return launch_affine_mfma_one<BITS, 16, 16, true>(a, nkc, s);
+            return w ? launch_affine_mfma_one<BITS, 16, 16>(a, nkc, s) : launch_affine_mfma_one<BITS, 32, 16>(a, nkc, s);
         case 32: return w ? launch_affine_mfma_one<BITS, 16, 32>(a, nkc, s) : launch_affine_mfma_one<BITS, 32, 32>(a, nkc, s);
         case 64: return w ? launch_affine_mfma_one<BITS, 16, 64>(a, nkc, s) : launch_affine_mfma_one<BITS, 32, 64>(a, nkc, s);
         default: return hipErrorInvalidValue;
