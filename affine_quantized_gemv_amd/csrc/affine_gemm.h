@@ -193,7 +193,7 @@ struct GemmLayout {
     static constexpr int NWW = (2 * BITS + 3) / 4;        // code words a lane reads per row and group
     static constexpr int XOP = WK * MB * 2 * 1024;        // x operand bytes per stage
     static constexpr int XLD = XOP / 16 / NT;             // 16-byte x loads per thread per stage
-    static constexpr int TAB = NW * 64 * 4;               // per-wavefront fp32 scale tables
+    static constexpr int TAB = NW * 2 * 8 * 64 * 4;       // per-wavefront fp32 scale tables [2][8][64]
     static constexpr int RED = (WK - 1) * WN * 64 * 64 * 4;   // chunk partials (over the x buffers)
     static constexpr int RING = 2 * XOP > RED ? 2 * XOP : RED;
     static constexpr size_t LDS = (size_t)RING + TAB;
@@ -318,7 +318,9 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
     const int j = threadIdx.x;
     const int jmb = j / 128, jh = (j / 64) % 2, jl = j % 64;
     const uint32_t x_off = (uint32_t)(((jmb * a.G + zb) * 2 + jh) * 1024 + jl * 16);
-    const uint32_t s_off = (uint32_t)(((int64_t)64 * wn + lane) * a.G * 2);
+    // scales: 8-group windows, one 8-row block a stage (see load)
+    const uint32_t s_off = (uint32_t)((((int64_t)64 * wn + (lane >> 3)) * a.G + (lane & 7)) * 2);
+    const uint32_t s_rb = (uint32_t)(8 * a.G * 2);   // bytes per 8 rows
 
     auto load = [&](int i, GemmStage<BITS, WK>& st) __attribute__((always_inline)) {
         const uint32_t cs = SOFF ? (uint32_t)((g0 + i) * L::GB) : 0u;
@@ -343,8 +345,20 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
         for (int q = 0; q < WK; ++q)
             st.xo[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                 rx, x_off + (SOFF ? 0u : (uint32_t)((q * GC + i) * 2048)), SOFF ? (uint32_t)((q * GC + i) * 2048) : 0u, 0));
-        st.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off + (SOFF ? 0u : (uint32_t)(2 * (g0 + i))),
-                                                     SOFF ? (uint32_t)(2 * (g0 + i)) : 0u, 0);
+        // the scales of the next 8-group window, 8 rows a stage: lane l takes
+        // row 8 (i % 8) + l / 8 of the wavefront's rows and group l % 8 of
+        // window i / 8 + 1, so one load covers 8 rows of 16 bytes (not 64
+        // rows); the row stays in the vector offset (range-checked)
+        const uint32_t sg = (uint32_t)(2 * (g0 + 8 * (i / 8 + 1)));
+        st.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off + (uint32_t)(i % 8) * s_rb + (SOFF ? 0u : sg),
+                                                     SOFF ? sg : 0u, 0);
+    };
+    // window 0 before the first stage
+    auto load_window0 = [&](uint32_t (&w0)[8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            w0[b] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off + (uint32_t)b * s_rb + (SOFF ? 0u : (uint32_t)(2 * g0)),
+                                                         SOFF ? (uint32_t)(2 * g0) : 0u, 0);
     };
     auto put_x = [&](int buf, const GemmStage<BITS, WK>& st) __attribute__((always_inline)) {
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(gemm_lds + buf * L::XOP);
@@ -364,17 +378,22 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
     asm volatile("" : "+s"(cmaskh));
     asm volatile("" : "+v"(cbias));
 
-    float* tab = reinterpret_cast<float*>(gemm_lds + L::RING) + wave * 64;
+    // the wavefront's scales [window parity][group of the window][row]
+    float* tab = reinterpret_cast<float*>(gemm_lds + L::RING) + wave * (2 * 8 * 64);
 
     // group i: both k-steps of each 16 x 16 tile, then the group's scale
     // into the running sums, one 16-row block at a time
     auto compute = [&](int i, const GemmStage<BITS, WK>& st) __attribute__((always_inline)) {
-        tab[lane] = __uint_as_float(st.sc << 16);
-        f32x4_t S[4];   // read through the same float pointer, after the write above
+        // this stage's block of the next window, then the scales of group i
+        // (written 8 or more stages ago, by this wavefront: LDS operations of
+        // one wavefront take effect in program order)
+        tab[((i / 8 + 1) & 1) * 512 + (lane & 7) * 64 + 8 * (i % 8) + (lane >> 3)] = __uint_as_float(st.sc << 16);
+        const float* tg = tab + ((i / 8) & 1) * 512 + (i % 8) * 64;
+        f32x4_t S[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) S[t][v] = tab[16 * t + 4 * c + v];
+            for (int v = 0; v < 4; ++v) S[t][v] = tg[16 * t + 4 * c + v];
         const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(gemm_lds + (i & 1) * L::XOP) + kc * 512;
         u32x4_t xb[MB][2];
 #pragma unroll
@@ -409,12 +428,17 @@ __global__ void __launch_bounds__(64 * kGemmWaves) affine_gemm_kernel(GemmArgs a
     // (issued stage by stage, in the loop's order: the wait for a stage's
     // data counts the loads issued after it, and where the first pass joins
     // the loop the compiler takes the smaller count of the two paths)
+    uint32_t w0[8];
+    load_window0(w0);
+    __builtin_amdgcn_sched_barrier(0);
     GemmStage<BITS, WK> ring[R];
     static_for<0, D>([&](auto Uc) __attribute__((always_inline)) {
         constexpr int u = decltype(Uc)::value;
         load(u < GC ? u : GC - 1, ring[u]);
         __builtin_amdgcn_sched_barrier(0);
     });
+#pragma unroll
+    for (int b = 0; b < 8; ++b) tab[(lane & 7) * 64 + 8 * b + (lane >> 3)] = __uint_as_float(w0[b] << 16);
     put_x(0, ring[0]);
     __syncthreads();
     for (int base = 0; base < GC; base += R) {
