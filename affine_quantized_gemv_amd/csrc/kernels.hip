@@ -326,7 +326,7 @@ bool choose_stream(int bits, bool swiglu, int M, int N, int K, LaunchCfg& c)
     if (T < 2048) return false;
     c.xreg = (bits != 0 && U <= 64 && (c.MT == 1 || (c.MT == 2 && bits != 8 && !swiglu))) ? 1 : 0;
     const size_t per_unit = bits ? (bits == 8 ? 16 * 16 : 16 * 8) + 8 : 16;
-    c.lds = c.xreg ? 0 : (size_t)c.MT * U * per_unit;
+    c.lds = (size_t)c.MT * U * per_unit;   // staged x (also the source of register-resident x)
     // output staging, bounded with the fewest wavefronts the launch can get
     // (one 4-wave workgroup per CU)
     const int64_t row_bytes = bits ? (int64_t)K * bits / 8 : (int64_t)K * 2;

@@ -21,7 +21,7 @@
 #pragma once
 #include <atomic>
 
-#include "proj_kernel.h"
+#include "piece_kernel.h"
 
 namespace aqg {
 namespace detail {
@@ -34,6 +34,27 @@ constexpr size_t kStreamLdsMax = 160 * 1024;
 template <int BITS, int MT> struct StreamDepth {
     static constexpr int D = BITS == 0 ? (MT <= 2 ? 8 : 4) : ((BITS <= 4 && MT <= 4) ? 4 : 2);
 };
+
+// One unit of weights (Geo<BITS>::NW words at byte offset voff + soff of a
+// buffer) in 16-byte loads plus an 8-byte tail; non-temporal: weights are
+// read once.
+template <int BITS>
+__device__ __forceinline__ void load_unit_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int NW = Geo<BITS>::NW;
+    static_assert(NW % 2 == 0, "units are whole 8-byte pieces");
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, kLoadNT));
+        w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+    if constexpr (NW % 4 != 0) {
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff + 16 * (NW / 4), soff, kLoadNT));
+        w[NW - 2] = v.x; w[NW - 1] = v.y;
+    }
+}
 
 template <int BITS, int MT, bool SWIGLU, bool XREG, int D = StreamDepth<BITS, MT>::D>
 __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
@@ -49,7 +70,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
     const int LPR = 1 << L;
     const int G = 64 >> L;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar tile math
     const int slot = lane >> L;
     const int li = lane & (LPR - 1);
     const int U = a.K / UK;                                   // units per row
@@ -71,23 +92,96 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
     const int64_t row_words = (BITS == 0) ? (int64_t)a.K / 2 : (int64_t)a.K * BITS / 32;
     const int gpr = a.K / 64;
 
+    // ---- stream: items are (tile, unit slot j) in order; ring of D items.
+    // In the steady-state loop every load is unconditional (indices clamped to
+    // a valid unit; an idle lane re-reads a neighbour's address, which
+    // coalesces) and nothing writes global memory, so the vector-memory wait
+    // counts stay exact: consuming ring slot d waits for slot d's loads only,
+    // never for the D-1 younger ones.  Finished outputs go to a lane-private
+    // slice of LDS and are written out after the loop by the same lane.
+    uint32_t wb[D][S][1][NW];
+    // scales and biases stay raw bf16 in the ring and are widened when their
+    // slot is consumed: widened at fetch time, the conversion is an early
+    // use of the youngest loads, and the compiler then waits for every load
+    // in flight (vmcnt(0)) once per ring turn
+    uint16_t sr[D][S], br[D][S];
+    int64_t f_tile = wg * CT;   // next item to fetch: tile, its index within
+    int f_c = 0;                // the super-tile, and the unit slot
+    int f_j = 0;
+    // next tile of this wavefront: the next one in the super-tile, else the
+    // first of the super-tile W further on (counters, no 64-bit division)
+    auto next_tile = [&](int64_t t) __attribute__((always_inline)) {
+        ++t;
+        if (++f_c == CT) { f_c = 0; t += (W - 1) * CT; }
+        return t;
+    };
+    // Loads go through a buffer descriptor per row tile (base and byte range
+    // of the tile's rows, scalar) with loop-invariant lane offsets, so a fetch
+    // costs scalar work only.  Rows past N fall outside the range and read as
+    // zero; a lane slot past the row's last unit reads into the next row or
+    // outside the range, and its contribution is zeroed by `live` below.
+    const int64_t row_bytes = row_words * 4;
+    const uint32_t wvo = (uint32_t)((int64_t)slot * row_bytes + (int64_t)li * NW * 4);
+    [[maybe_unused]] const uint32_t svo = (uint32_t)((slot * gpr + li) * 2);
+    auto fetch = [&](int d) __attribute__((always_inline)) {
+        const int64_t n0 = f_tile * G;
+        const int64_t rows = a.N - n0;
+        const uint32_t uo = (uint32_t)(f_j * LPR);            // this slot's first unit
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const char* base = static_cast<const char*>(s == 0 ? a.w0 : a.w1);
+            load_unit_buf<BITS>(tile_rsrc(base + n0 * row_bytes, rows * row_bytes), wvo, uo * NW * 4, wb[d][s][0]);
+        }
+        if constexpr (BITS != 0) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc((s == 0 ? a.scales : a.scales1) + n0 * gpr, rows * gpr * 2);
+                const __amdgpu_buffer_rsrc_t rb = tile_rsrc((s == 0 ? a.biases : a.biases1) + n0 * gpr, rows * gpr * 2);
+                sr[d][s] = __builtin_amdgcn_raw_buffer_load_b16(rs, svo, uo * 2, kLoadNT);
+                br[d][s] = __builtin_amdgcn_raw_buffer_load_b16(rb, svo, uo * 2, kLoadNT);
+            }
+        }
+        if (++f_j == upl) { f_j = 0; f_tile = next_tile(f_tile); }
+    };
+    // prologue: D items, unconditionally (past the end they are clamped,
+    // harmless re-reads that are never consumed)
+    auto prologue_fetch = [&]() __attribute__((always_inline)) {
+        static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(decltype(Dd)::value); });
+    };
+
     // ---- x: LDS (whole K) or registers (one group per lane)
     uint4* xp = lds_s4;
     float2* xc = reinterpret_cast<float2*>(lds_s4 + MT * NCH * U);
     uint32_t xq[XREG ? MT : 1][XREG ? PairPlan<(BITS ? BITS : 2)>::NP : 1];
     float xX[MT], xT[MT];
     if constexpr (XREG) {
+        // Lane li's operands are those of group li (the same in every
+        // wavefront), so the workgroup computes each group's once into LDS
+        // (MT*U <= 128 tasks, one per thread) and every lane copies its own:
+        // the operand arithmetic (~500 VALU instructions per group) is paid
+        // once per workgroup instead of once per wavefront.  The x loads go
+        // out first, then the first weight loads, then that arithmetic, so
+        // it waits for x alone and overlaps the weights' latency.
+        using St = Stager<BITS, MT>;
+        const St st{a, 0, U, xp, xc};
+        const int ntask = st.ntasks();
+        const bool mine = (int)threadIdx.x < ntask;
+        typename St::Regs xr = st.load(mine ? (int)threadIdx.x : ntask - 1);
+        prologue_fetch();
+        if (mine) st.store(threadIdx.x, xr);
+        __syncthreads();
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            uint32_t xw[32];
-            const bool have = m < a.M && li < U;
-            const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + 64 * li);
+            const bool have = li < U;
+            const int g = have ? li : 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                uint4 v = have ? src[i] : make_uint4(0, 0, 0, 0);
-                xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+            for (int c = 0; c < NCH; ++c) {
+                const uint4 v = have ? xp[(m * NCH + c) * U + g] : make_uint4(0, 0, 0, 0);
+                xq[m][4 * c] = v.x; xq[m][4 * c + 1] = v.y; xq[m][4 * c + 2] = v.z; xq[m][4 * c + 3] = v.w;
             }
-            group_x_operands<BITS>(xw, xq[m], xX[m], xT[m]);
+            const float2 v = have ? xc[m * U + g] : make_float2(0.0f, 0.0f);
+            xX[m] = v.x;
+            xT[m] = v.y;
         }
     } else {
         using St = Stager<BITS, MT>;
@@ -111,56 +205,15 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
     }
     if (my_tiles == 0) return;
 
-    // ---- stream: items are (tile, unit slot j) in order; ring of D items.
-    // In the steady-state loop every load is unconditional (indices clamped to
-    // a valid unit; an idle lane re-reads a neighbour's address, which
-    // coalesces) and nothing writes global memory, so the vector-memory wait
-    // counts stay exact: consuming ring slot d waits for slot d's loads only,
-    // never for the D-1 younger ones.  Finished outputs go to a lane-private
-    // slice of LDS and are written out after the loop by the same lane.
-    uint32_t wb[D][S][1][NW];
-    float sb[D][S][1], bb[D][S][1];
-    int64_t f_tile = wg * CT;   // next item to fetch: tile, its index within
-    int f_c = 0;                // the super-tile, and the unit slot
-    int f_j = 0;
-    // next tile of this wavefront: the next one in the super-tile, else the
-    // first of the super-tile W further on (counters, no 64-bit division)
-    auto next_tile = [&](int64_t t) __attribute__((always_inline)) {
-        ++t;
-        if (++f_c == CT) { f_c = 0; t += (W - 1) * CT; }
-        return t;
-    };
-    auto fetch = [&](int d) __attribute__((always_inline)) {
-        int u = li + f_j * LPR;
-        if (u >= U) u = U - 1;
-        int64_t n = f_tile * G + slot;
-        if (n >= a.N) n = a.N - 1;                            // clamp: load, never store
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const uint32_t* base = reinterpret_cast<const uint32_t*>(s == 0 ? a.w0 : a.w1);
-            load_unit<BITS>(base + n * row_words + (int64_t)u * NW, wb[d][s][0]);
-        }
-        if constexpr (BITS != 0) {
-#pragma unroll
-            for (int s = 0; s < S; ++s) {
-                sb[d][s][0] = bf16_to_f32((s == 0 ? a.scales : a.scales1)[n * gpr + u]);
-                bb[d][s][0] = bf16_to_f32((s == 0 ? a.biases : a.biases1)[n * gpr + u]);
-            }
-        }
-        if (++f_j == upl) { f_j = 0; f_tile = next_tile(f_tile); }
-    };
-
     // lane-private output staging: VPL values per tile (outputs m = li + v*LPR)
     constexpr int VPL_MAX = MT;
     const int VPL = (MT + LPR - 1) >> L;
-    float* obuf = reinterpret_cast<float*>(XREG ? lds_s4 : (lds_s4 + MT * NCH * U + ((BITS != 0) ? (MT * U + 1) / 2 : 0)))
+    float* obuf = reinterpret_cast<float*>(lds_s4 + MT * NCH * U + ((BITS != 0) ? (MT * U + 1) / 2 : 0))
                   + (size_t)wave * a.tmax * 64 * VPL;
     (void)VPL_MAX;
 
     const int64_t nitems = my_tiles * upl;
-    // prologue: D items, unconditionally (past the end they are clamped,
-    // harmless re-reads that are never consumed)
-    static_for<0, D>([&](auto Dd) __attribute__((always_inline)) { fetch(decltype(Dd)::value); });
+    if constexpr (!XREG) prologue_fetch();
 
     float acc[S][1][MT];
 #pragma unroll
@@ -180,6 +233,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
                 const int u0 = li + c_j * LPR;
                 const bool live = u0 < U;
                 const int u = live ? u0 : U - 1;
+                [[maybe_unused]] float sb[S][1], bb[S][1];
                 if constexpr (BITS == 0) {
 #pragma unroll
                     for (int s = 0; s < S; ++s)
@@ -188,8 +242,8 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
                 } else {
 #pragma unroll
                     for (int s = 0; s < S; ++s) {
-                        sb[d][s][0] = live ? sb[d][s][0] : 0.0f;
-                        bb[d][s][0] = live ? bb[d][s][0] : 0.0f;
+                        sb[s][0] = live ? bf16_to_f32(sr[d][s]) : 0.0f;
+                        bb[s][0] = live ? bf16_to_f32(br[d][s]) : 0.0f;
                     }
                 }
                 {
@@ -231,10 +285,10 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
                         for (int m = 0; m < MT; ++m)
 #pragma unroll
                             for (int s = 0; s < S; ++s)
-                                acc[s][0][m] = fmaf(sb[d][s][0], (dd[s][m] + de[s][m]) - xT[m],
-                                                    fmaf(bb[d][s][0], xX[m], acc[s][0][m]));
+                                acc[s][0][m] = fmaf(sb[s][0], (dd[s][m] + de[s][m]) - xT[m],
+                                                    fmaf(bb[s][0], xX[m], acc[s][0][m]));
                     } else {
-                        unit_mac<BITS, MT, S, 1>(wb[d], sb[d], bb[d], xp, xc, U, u, acc);
+                        unit_mac<BITS, MT, S, 1>(wb[d], sb, bb, xp, xc, U, u, acc);
                     }
                 }
                 if (++c_j == upl) {
@@ -263,6 +317,9 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
         static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
             consume(Dd);
             fetch(decltype(Dd)::value);
+            // keep each slot's loads right after its arithmetic, so a slot
+            // waits for its own loads only
+            __builtin_amdgcn_sched_barrier(0);
         });
     }
     for (; base < nitems; base += D) {                  // drain
@@ -291,15 +348,15 @@ __global__ void __launch_bounds__(kStreamThreads) stream_kernel(ProjArgs a)
     }
 }
 
-// LDS bytes of one workgroup: the staged x (none when x is in registers) plus
-// the lane-private output staging for `tmax` tiles per wavefront.
+// LDS bytes of one workgroup: the staged x (with x in registers, the operands
+// the lanes copy from) plus the lane-private output staging for `tmax` tiles
+// per wavefront.
 template <int BITS, int MT, bool XREG>
 size_t stream_lds_bytes(const LaunchCfg& c, int K, int64_t tmax)
 {
     const int L = c.lpr_log2;
     const int vpl = (MT + (1 << L) - 1) >> L;
     const size_t out = (size_t)c.nwaves * tmax * 64 * vpl * 4;
-    if (XREG) return out;
     const int U = BITS == 0 ? K / 8 : K / 64;
     const size_t x16 = (size_t)MT * Geo<BITS>::NCH * U + (BITS != 0 ? ((size_t)MT * U + 1) / 2 : 0);
     return x16 * 16 + out;
