@@ -112,10 +112,17 @@ __device__ __forceinline__ void piece_x(const uint16_t* __restrict__ xrow, bool 
     piece_operands<BITS>(xw, xq, X, T);
 }
 
-// Buffer descriptor over `bytes` bytes from p (clamped to the 32-bit range).
+// Buffer descriptor over `bytes` bytes from p (clamped to [0, 0x7FFFFFF0]).
+// The clamp compares the two 32-bit halves: a signed 64-bit compare has no
+// scalar form, so it would run on the vector unit in every stream loop.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int64_t bytes)
 {
-    const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
+    // (an empty asm keeps the halves apart: recombined, they would become
+    // that 64-bit compare again; the descriptor is wave-uniform, so is hi)
+    int hi = __builtin_amdgcn_readfirstlane((int)(bytes >> 32));
+    asm volatile("" : "+s"(hi));
+    const uint32_t lo = (uint32_t)bytes;
+    const int n = hi < 0 ? 0 : ((hi > 0 || lo >= 0x7FFFFFF0u) ? 0x7FFFFFF0 : (int)lo);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kBufferFlags);
 }
 
@@ -510,8 +517,11 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
         if (a.amx && lane < MT) amx_store(a.amx, a.amx_slots, wg, lane, amx_neutral_value(), kAmxNoIndex);
         return;
     }
-    int64_t bt = 0;
-    for (; bt + 2 * RD <= my_tiles; bt += RD) {          // steady state
+    // 32-bit loop counts (a wavefront's tiles fit easily): a signed 64-bit
+    // compare would run on the vector unit once per step
+    const int nt = (int)my_tiles;
+    int bt = 0;
+    for (; bt + 2 * RD <= nt; bt += RD) {                // steady state
         static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
             // raised priority from a slot's arithmetic through its next loads:
             // a wavefront whose data has arrived finishes with it and refills
@@ -527,12 +537,12 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
             __builtin_amdgcn_sched_barrier(0);
         });
     }
-    for (; bt < my_tiles; bt += RD) {                   // drain
+    for (; bt < nt; bt += RD) {                         // drain
         static_for<0, D>([&](auto Dd) __attribute__((always_inline)) {
             constexpr int r = decltype(Dd)::value / J;
-            if (bt + r < my_tiles) {
+            if (bt + r < nt) {
                 consume(Dd);
-                if (bt + r + RD < my_tiles) fetch(Dd);
+                if (bt + r + RD < nt) fetch(Dd);
             }
         });
     }
