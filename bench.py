@@ -324,11 +324,27 @@ def make_call(label):
 
 # ------------------------------------------------------------------ timing
 
+def warm_clocks(g, s, e0, e1, ms=25.0):
+    """Replay graph g for about `ms` of device time, untimed: the GPU's clocks
+    settle after the host-side setup between calls (idle gaps in which they
+    drop), so the timed replays that follow see the steady state a decode loop
+    runs in rather than the first milliseconds after an idle period."""
+    g.replay()
+    e0.record(s)
+    g.replay()
+    e1.record(s)
+    e1.synchronize()
+    per = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(min(500, int(ms / per))):
+        g.replay()
+
+
 def time_call(call, n, reps=5):
     """Average device time (us) per call.  At least n calls, and at least one
     call per weight copy (>= 1 GiB of distinct weights), are captured into a HIP
-    graph; the graph is replayed `reps` times between HIP events on the launch
-    stream, so host launch overhead is excluded and no weight is cache-hot."""
+    graph; after ~25 ms of untimed replays (clocks settled) the graph is
+    replayed `reps` times between HIP events on the launch stream, so host
+    launch overhead is excluded and no weight is cache-hot."""
     import torch
     n = max(n, call.w.R)
     call()
@@ -337,9 +353,9 @@ def time_call(call, n, reps=5):
     with torch.cuda.graph(g):
         for _ in range(n):
             call()
-    g.replay()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warm_clocks(g, s, e0, e1)
     torch.cuda.synchronize()
     MARKERS.push(label_of(call))
     e0.record(s)
@@ -363,9 +379,9 @@ def time_call_hot(call, n=40, reps=3):
         with torch.cuda.graph(g):
             for _ in range(n):
                 call()
-        g.replay()
         s = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        warm_clocks(g, s, e0, e1)
         torch.cuda.synchronize()
         e0.record(s)
         for _ in range(reps):
@@ -630,8 +646,9 @@ def summarize_counters(d, labels):
                      "run; FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by bytes per counter unit of a "
                      "256 MiB device copy (__amd_rocclr_copyBuffer); other counters per dispatch, mean",
            "calibration": {k: round(v, 5) for k, v in scale.items()}, "calls": {}}
-    table = ["| call | kernel | HBM B / algorithmic | VALU inst / KiB | MFMA inst / KiB | waves / CU | "
-             "busy % waiting | LDS bank conflicts / KiB |", "|---|---|---|---|---|---|---|---|"]
+    table = ["| call | kernel | HBM B / algorithmic | VALU inst / KiB | SALU inst / KiB | MFMA inst / KiB | "
+             "VALU issue / CU busy cycle | waves / CU | busy % waiting | LDS bank conflicts / KiB |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
     for label in labels:
         name = slug(label)
         # a call may run several kernels (the row argmax: the GEMV, then the
@@ -640,6 +657,7 @@ def summarize_counters(d, labels):
         per = {}
         for ctr in ("FETCH_SIZE", "WRITE_SIZE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_WAVES", "SQ_WAVE_CYCLES",
                     "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE",
+                    "SQ_INSTS_SALU", "SQ_BUSY_CU_CYCLES",
                     "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES"):
             by_kernel = {}
             for r in rows(ctr, name):
@@ -675,10 +693,17 @@ def summarize_counters(d, labels):
             if "SQ_WAVE_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals else None
         wait = 100 * vals["SQ_WAIT_INST_ANY"] / vals["SQ_WAVE_CYCLES"] \
             if "SQ_WAIT_INST_ANY" in vals and vals.get("SQ_WAVE_CYCLES") else None
-        table.append("| %s | `%s` | %s | %s | %s | %s | %s | %s |" % (
+        # VALU instructions over the CUs' busy cycles (SQ_BUSY_CU_CYCLES, summed
+        # over CUs): 1.0 is every SIMD issuing a wave64 VALU instruction every
+        # 4 cycles, the vector unit's full rate
+        vissue = vals["SQ_INSTS_VALU"] / vals["SQ_BUSY_CU_CYCLES"] \
+            if "SQ_INSTS_VALU" in vals and vals.get("SQ_BUSY_CU_CYCLES") else None
+        table.append("| %s | `%s` | %s | %s | %s | %s | %s | %s | %s | %s |" % (
             label, kern, f(rec.get("traffic_over_algorithmic"), "%.4f"),
             f(vals["SQ_INSTS_VALU"] / kib if "SQ_INSTS_VALU" in vals else None),
+            f(vals["SQ_INSTS_SALU"] / kib if "SQ_INSTS_SALU" in vals else None),
             f(vals["SQ_INSTS_MFMA"] / kib if "SQ_INSTS_MFMA" in vals else None, "%.2f"),
+            f(vissue, "%.2f"),
             f(waves_cu), f(wait), f(vals["SQ_LDS_BANK_CONFLICT"] / kib if "SQ_LDS_BANK_CONFLICT" in vals else None)))
     with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as fh:
         json.dump(doc, fh, indent=1)
