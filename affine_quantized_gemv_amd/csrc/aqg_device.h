@@ -78,10 +78,13 @@ __device__ __forceinline__ uint32_t bf16_scale_pow2(uint32_t h)
     }
 }
 
+// (bound_ctrl set: a source lane that is out of its row or inactive reads 0.
+// The patterns used here never leave the row, and with it set the compiler
+// folds the move into the add that consumes it, one instruction per step.)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over aligned segments of 2^L lanes (L <= 4), result in every lane of the

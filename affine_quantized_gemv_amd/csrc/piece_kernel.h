@@ -120,10 +120,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int64
     // (an empty asm keeps the halves apart: recombined, they would become
     // that 64-bit compare again; the descriptor is wave-uniform, so is hi)
     int hi = __builtin_amdgcn_readfirstlane((int)(bytes >> 32));
-    asm volatile("" : "+s"(hi));
+    asm("" : "+s"(hi));
     const uint32_t lo = (uint32_t)bytes;
     const int n = hi < 0 ? 0 : ((hi > 0 || lo >= 0x7FFFFFF0u) ? 0x7FFFFFF0 : (int)lo);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kBufferFlags);
+}
+
+// Buffer descriptor over n >= 0 bytes from p (n already within range).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int n)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kBufferFlags);
+}
+
+// min(max(rows, 0), g) for a wave-uniform row count, with 32-bit scalar
+// compares on the two halves (see tile_rsrc).
+__device__ __forceinline__ int rows_in_tile(int64_t rows, int g)
+{
+    int hi = __builtin_amdgcn_readfirstlane((int)(rows >> 32));
+    asm("" : "+s"(hi));
+    const uint32_t lo = (uint32_t)rows;
+    return hi < 0 ? 0 : ((hi > 0 || lo >= (uint32_t)g) ? g : (int)lo);
 }
 
 // s_waitcnt immediate for lgkmcnt(0) alone (vmcnt and expcnt at their
@@ -318,13 +334,17 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
             nrows = seg_rows(a, sg);
             n0 -= seg_start(a, sg);
         }
-        const int64_t rows = nrows - n0;
+        // The descriptors cover this tile's rows that exist (0..G): every
+        // load of a tile lies within its G rows (weights at woff, the G*K/64
+        // <= 64 scales and biases at lane*2), so the range needs one clamp
+        // per tile, not one per descriptor.
+        const int rt = rows_in_tile(nrows - n0, G);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            rw[s] = tile_rsrc(static_cast<const char*>(s == 0 ? w0 : a.w1) + n0 * row_bytes, rows * row_bytes);
+            rw[s] = make_rsrc(static_cast<const char*>(s == 0 ? w0 : a.w1) + n0 * row_bytes, rt * (int)row_bytes);
             if constexpr (BITS != 0) {
-                rs[s] = tile_rsrc((s == 0 ? sc0 : a.scales1) + n0 * gpr, rows * gpr * 2);
-                rb[s] = tile_rsrc((s == 0 ? bi0 : a.biases1) + n0 * gpr, rows * gpr * 2);
+                rs[s] = make_rsrc((s == 0 ? sc0 : a.scales1) + n0 * gpr, rt * gpr * 2);
+                rb[s] = make_rsrc((s == 0 ? bi0 : a.biases1) + n0 * gpr, rt * gpr * 2);
             }
         }
     };
@@ -436,13 +456,16 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
             });
             if constexpr (j == 0) {
                 // the row's first piece takes every piece's scale and bias
+                // (widened to fp32 once, in the lane that loaded them)
 #pragma unroll
-                for (int s = 0; s < S; ++s)
+                for (int s = 0; s < S; ++s) {
+                    const int sf = (int)(sw[s][d / J] << 16), bf = (int)(bw[s][d / J] << 16);
 #pragma unroll
                     for (int jj = 0; jj < J; ++jj) {
-                        rsc[s][jj] = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(gsrc[jj], (int)sw[s][d / J]) << 16);
-                        rbi[s][jj] = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(gsrc[jj], (int)bw[s][d / J]) << 16);
+                        rsc[s][jj] = __int_as_float(__builtin_amdgcn_ds_bpermute(gsrc[jj], sf));
+                        rbi[s][jj] = __int_as_float(__builtin_amdgcn_ds_bpermute(gsrc[jj], bf));
                     }
+                }
             }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
