@@ -53,8 +53,11 @@ constexpr size_t kPieceLdsMax = 160 * 1024;
 // (affine: with the unpack's registers, more measured slower than LDS)
 template <int BITS> constexpr int piece_xreg_budget() { return BITS == 0 ? 128 : 64; }
 // Resident wavefronts per CU: more were measured no faster (dense: 8 with
-// ~3 KB in flight each; affine, with more arithmetic per byte: 24).
-template <int BITS, int MT> constexpr int piece_max_waves_per_cu() { return BITS == 0 ? 8 : MT == 1 ? 28 : 24; }
+// ~3 KB in flight each; affine, with more arithmetic per byte: 24, and 20 at
+// M = 1, where each wavefront's set-up is a larger share of its work: 4-bit
+// 14336 x 4096 7.9 us at 16 or 20 against 8.7 us at 24 or 28, the 4-bit LM
+// head 15.3 against 15.6 us).
+template <int BITS, int MT> constexpr int piece_max_waves_per_cu() { return BITS == 0 ? 8 : MT == 1 ? 20 : 24; }
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kLoadNT = 2;                // non-temporal: weights are read once
 
