@@ -40,6 +40,10 @@ CASES = [
     ("piece", 4, 1, 3000, 1024), ("piece", 2, 4, 3000, 1024), ("piece", 2, 8, 20000, 1024), ("piece", 8, 4, 3000, 1024),
     ("stream", 3, 1, 2304, 4096), ("stream", 5, 4, 4400, 4096), ("stream", 6, 2, 4400, 4096),
     ("stream", 7, 1, 2304, 4096),
+    # rows whose group count is not a power of two: lane slots past the row's
+    # last group (8 of 64 at K = 3584, 15 of 32 at K = 1088 with two rows a
+    # tile, 1 of 64 at K = 4032) read past the row and must add nothing
+    ("stream", 3, 1, 4500, 3584), ("stream", 5, 2, 4500, 1088), ("stream", 7, 4, 4500, 4032),
     ("valu", 3, 9, 300, 320), ("valu", 5, 32, 300, 320),
     ("affine_mfma", 4, 16, 40001, 1024), ("affine_mfma", 2, 12, 40001, 1024), ("affine_mfma", 8, 16, 40001, 3072),
     ("affine_mfma", 4, 4, 40001, 1024),
