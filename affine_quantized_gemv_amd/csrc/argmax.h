@@ -29,6 +29,27 @@ __device__ __forceinline__ void amx_xor(float& bv, int& bi, int mask)
     amx_take(bv, bi, ov, oi);
 }
 
+// Combine with the lane a DPP pattern pairs it with (all lanes active; the
+// patterns used stay within a 16-lane row).
+template <int CTRL>
+__device__ __forceinline__ void amx_dpp(float& bv, int& bi)
+{
+    const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), CTRL, 0xF, 0xF, true));
+    const int oi = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xF, 0xF, true);
+    amx_take(bv, bi, ov, oi);
+}
+
+// Every lane of each 16-lane row ends with the row's best: pairs, quads, the
+// two quads of a half-row, the two halves (the segment-sum tree of the
+// GEMVs, with the total order's combine in place of the add).
+__device__ __forceinline__ void amx_row(float& bv, int& bi)
+{
+    amx_dpp<0xB1>(bv, bi);    // quad_perm [1,0,3,2]
+    amx_dpp<0x4E>(bv, bi);    // quad_perm [2,3,0,1]
+    amx_dpp<0x141>(bv, bi);   // row_half_mirror
+    amx_dpp<0x140>(bv, bi);   // row_mirror
+}
+
 // Partials are laid out row-major, [m][slots]: the final reduction of a row
 // reads one contiguous run.
 __device__ __forceinline__ void amx_store(void* amx, int64_t slots, int64_t producer, int m, float v, int i)

@@ -12,25 +12,34 @@ namespace {
 // same answer in any grouping; they are written for latency: every thread
 // issues kArgmaxUnroll independent loads before combining them (a loop of
 // one dependent load per step took 4.5 us over 2048 partials and 10 us over
-// 7168).
+// 7168), and the combines run on DPP lane moves where they stay in a row.
 constexpr int kArgmaxThreads = 1024;
 constexpr int kArgmaxUnroll = 8;
 
 // Block-wide combine of one (value, index) per thread; thread 0 returns it.
+// Within a wavefront: the row tree, then lane swaps across 16 and 32; across
+// the wavefronts: wavefront 0 takes their results one per lane and runs the
+// row tree again (a serial loop over them took ~1 us of dependent LDS reads).
 __device__ __forceinline__ void amx_block(float& bv, int& bi)
 {
-    __shared__ float sv[kArgmaxThreads / 64];
-    __shared__ int si[kArgmaxThreads / 64];
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) amx_xor(bv, bi, s);
+    constexpr int NWV = kArgmaxThreads / 64;
+    static_assert(NWV <= 16, "one wavefront result per lane of a row");
+    __shared__ float sv[NWV];
+    __shared__ int si[NWV];
+    amx_row(bv, bi);
+    amx_xor(bv, bi, 16);
+    amx_xor(bv, bi, 32);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) {
         sv[wave] = bv;
         si[wave] = bi;
     }
     __syncthreads();
-    if (threadIdx.x == 0)
-        for (int w = 1; w < kArgmaxThreads / 64; ++w) amx_take(bv, bi, sv[w], si[w]);
+    if (wave == 0) {
+        bv = lane < NWV ? sv[lane] : amx_neutral_value();
+        bi = lane < NWV ? si[lane] : kAmxNoIndex;
+        amx_row(bv, bi);
+    }
 }
 
 // One workgroup per row m: the best of the P producers' partials.

@@ -590,8 +590,15 @@ __global__ void __launch_bounds__(kPieceThreads) piece_kernel(ProjArgs a)
             const int64_t n = tile * G + r / MT;
             if (m < a.M && n < a.N) amx_take(bv, bi, obuf[v], (int)n);
         }
+        if constexpr (MT == 1) {
+            // one row: the DPP row tree, then the lane swaps across 16 and 32
+            amx_row(bv, bi);
+            amx_xor(bv, bi, 16);
+            amx_xor(bv, bi, 32);
+        } else {
 #pragma unroll
-        for (int sh = MT; sh < 64; sh <<= 1) amx_xor(bv, bi, sh);
+            for (int sh = MT; sh < 64; sh <<= 1) amx_xor(bv, bi, sh);
+        }
         if (lane < MT) amx_store(a.amx, a.amx_slots, wg, lane, bv, bi);
         return;
     }
