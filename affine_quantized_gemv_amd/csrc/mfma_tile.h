@@ -265,9 +265,9 @@ __global__ void __launch_bounds__(64 * NW) mfma_tile_kernel(ProjArgs a)
         });
     }
     if (a.amx) {
-        // the 16 threads of row om are one 16-lane row of a wavefront
-#pragma unroll
-        for (int sh = 1; sh < 16; sh <<= 1) amx_xor(amx_v, amx_i, sh);
+        // the 16 threads of row om are one 16-lane row of a wavefront: the
+        // DPP row tree combines them
+        amx_row(amx_v, amx_i);
         if (on == 0 && om < kArgmaxRows) amx_store(a.amx, a.amx_slots, blockIdx.x, om, amx_v, amx_i);
     }
 }
